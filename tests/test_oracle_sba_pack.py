@@ -1,0 +1,221 @@
+"""Pins for the oracle's SBA search and bit-plane packing (CPU only).
+
+SBA follows page 1 ("SliM-LLM" blog digest), core design, component one
+(KL objective, |G_{N-1}| = |G_{N+1}|, double-pointer search over [0, k/2],
+16 iterations for LLaMA-7B) and page 2, "Approach" (average group salience,
+balanced counts).  Packing follows page 1's FAQ on storage (no bitmap, zero
+extra storage).  Checks: the pages' invariants, scipy's rel_entr, the
+closed-form binary KL, a pure-Python brute force of the whole search on tiny
+inputs, and a naive bit loop for the packer.
+"""
+import itertools
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+from scipy.special import rel_entr
+
+import oracle
+import synth
+
+GOLD = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "pages_constants.json")))
+
+
+def test_balance_invariant_and_scan_length():
+    k = GOLD["llama7b_width"]["value"] // GOLD["group_size"]["value"]
+    assert k == 32
+    rng = np.random.default_rng(0)
+    order = oracle.rank_groups(rng.random(k))
+    R = k // 2 + 1
+    assert R - 1 == GOLD["llama7b_sba_iterations"]["value"]
+    for N in (2, 3):
+        for r in range(R):
+            b = oracle.allocation(order, r, N)
+            assert (b == N + 1).sum() == r and (b == N - 1).sum() == r
+            assert int(b.sum()) == k * N
+            assert set(b.tolist()) <= {N - 1, N, N + 1}
+    # an interior step mixes all three widths; at r = k/2 (even k) every group moved
+    b = oracle.allocation(order, 8, 2)
+    assert sorted(set(b.tolist())) == GOLD["bit_set_at_2bit"]["value"]
+    assert sorted(set(oracle.allocation(order, 16, 2).tolist())) == [1, 3]
+
+
+def test_odd_k_keeps_middle_group():
+    order = oracle.rank_groups(np.array([5.0, 1.0, 3.0, 4.0, 2.0]))
+    assert order.tolist() == [0, 3, 2, 4, 1]
+    b = oracle.allocation(order, 2, 2)
+    assert b.tolist() == [3, 1, 2, 3, 1]
+
+
+def test_rank_ties_lower_index_first():
+    assert oracle.rank_groups([1.0, 2.0, 2.0, 1.0]).tolist() == [1, 2, 0, 3]
+
+
+def test_kl_matches_rel_entr_and_is_nonnegative():
+    rng = np.random.default_rng(1)
+    X = rng.standard_normal((50, 16)).astype(np.float32)
+    W = rng.standard_normal((9, 16)).astype(np.float32)
+    Wh = (W + 0.3 * rng.standard_normal(W.shape)).astype(np.float32)
+    kl_t = oracle.kl_divergence(X, W, Wh, per_token=True)
+    y, yh = X.astype(np.float64) @ W.T.astype(np.float64), X.astype(np.float64) @ Wh.T.astype(np.float64)
+    p = np.exp(y - y.max(1, keepdims=True)); p /= p.sum(1, keepdims=True)
+    q = np.exp(yh - yh.max(1, keepdims=True)); q /= q.sum(1, keepdims=True)
+    np.testing.assert_allclose(kl_t, rel_entr(p, q).sum(1), rtol=1e-10, atol=1e-14)
+    assert np.all(kl_t >= -1e-15)
+    assert oracle.kl_divergence(X, W, W) == pytest.approx(0.0, abs=1e-15)
+
+
+def test_kl_binary_closed_form():
+    rng = np.random.default_rng(2)
+    X = rng.standard_normal((20, 5)).astype(np.float32)
+    W = rng.standard_normal((2, 5)).astype(np.float32)
+    Wh = rng.standard_normal((2, 5)).astype(np.float32)
+    kl_t = oracle.kl_divergence(X, W, Wh, per_token=True)
+    for t in range(20):
+        y = X[t].astype(np.float64) @ W.T.astype(np.float64)
+        yh = X[t].astype(np.float64) @ Wh.T.astype(np.float64)
+        p = 1 / (1 + math.exp(-(y[0] - y[1])))
+        q = 1 / (1 + math.exp(-(yh[0] - yh[1])))
+        ref = p * math.log(p / q) + (1 - p) * math.log((1 - p) / (1 - q))
+        assert kl_t[t] == pytest.approx(ref, rel=1e-9, abs=1e-15)
+
+
+def _brute_sba(X, W, S, N, g):
+    """Whole search in pure Python: scalar quantizer, loop products, loop softmax."""
+    T, m = X.shape
+    n = W.shape[0]
+    k = m // g
+    order = sorted(range(k), key=lambda j: (-S[j], j))
+    kls = []
+    for r in range(k // 2 + 1):
+        bits = [N] * k
+        for j in order[:r]:
+            bits[j] = N + 1
+        for j in order[k - r:] if r else []:
+            bits[j] = N - 1
+        Wh = [[0.0] * m for _ in range(n)]
+        for i in range(n):
+            for j in range(k):
+                seg = [np.float32(W[i, j * g + c]) for c in range(g)]
+                lo, hi = min(seg), max(seg)
+                maxq = np.float32(2 ** bits[j] - 1)
+                s0 = np.float32(np.float32(hi - lo) / maxq)
+                if s0 == 0:
+                    s0 = np.float32(1)
+                z0 = np.float32(-lo / s0)
+                rr = np.float32(1) / s0
+                for c in range(g):
+                    t = np.float32(np.float32(seg[c] * rr) + z0)
+                    q = np.float32(min(max(float(np.rint(t)), 0.0), float(maxq)))
+                    Wh[i][j * g + c] = float(np.float32(np.float32(q - z0) * s0))
+        tot = 0.0
+        for t in range(T):
+            y = [sum(float(X[t, c]) * float(W[i, c]) for c in range(m)) for i in range(n)]
+            yh = [sum(float(X[t, c]) * Wh[i][c] for c in range(m)) for i in range(n)]
+            my, myh = max(y), max(yh)
+            ly = my + math.log(sum(math.exp(v - my) for v in y))
+            lyh = myh + math.log(sum(math.exp(v - myh) for v in yh))
+            tot += sum(math.exp(y[i] - ly) * ((y[i] - ly) - (yh[i] - lyh)) for i in range(n))
+        kls.append(tot / T)
+    rs = min(range(len(kls)), key=lambda r: (kls[r], r))
+    return kls, rs
+
+
+def test_sba_search_bruteforce_tiny():
+    rng = np.random.default_rng(3)
+    T, n, m, g = 6, 3, 128, 32
+    X = rng.standard_normal((T, m)).astype(np.float32)
+    X[:, 70:74] *= 12
+    W = (rng.standard_normal((n, m)) * 0.05).astype(np.float32)
+    _, S, _ = oracle.salience(oracle.hessian(X), W, g)
+    bits, kl, rs = oracle.sba_search(X, W, S, 2, g, "f32")
+    kb, rb = _brute_sba(X, W, S, 2, g)
+    np.testing.assert_allclose(kl, kb, rtol=1e-9, atol=1e-15)
+    assert rs == rb
+    assert bits.tolist() == oracle.allocation(oracle.rank_groups(S), rb, 2).tolist()
+
+
+def test_sba_two_valued_segments_give_zero_kl_and_r0():
+    # Each bf16 segment holds two distinct values: min-max reproduces both at
+    # every bit-width, so every step has KL = 0 and the tie rule picks r = 0.
+    rng = np.random.default_rng(4)
+    n, m, g = 5, 128, 32
+    lo = rng.standard_normal((n, m // g, 1)) * 0.02
+    hi = lo + np.abs(rng.standard_normal((n, m // g, 1))) * 0.02 + 0.001
+    pick = rng.random((n, m // g, g)) < 0.5
+    w = np.where(pick, lo, hi).reshape(n, m).astype(np.float32)
+    W = synth.to_bf16_bits(w)
+    X = synth.to_bf16_bits(rng.standard_normal((40, m)).astype(np.float32))
+    S = rng.random(m // g)
+    bits, kl, rs = oracle.sba_search(X, W, S, 2, g, "bf16")
+    assert np.all(np.abs(kl) < 1e-12) and rs == 0
+    assert np.all(bits == 2)
+
+
+def test_sba_scan_agrees_with_exhaustive_balanced_evaluations():
+    # Every step of the scan is one of the balanced allocations; evaluating the
+    # same allocation independently gives the same KL.
+    wl = synth.WORKLOADS["tiny-512"]
+    X, W = synth.make_x(wl, 512, 0, 512), synth.make_w(wl, 0)
+    _, S, _ = oracle.salience(oracle.hessian(X), W, 128)
+    bits, kl, rs = oracle.sba_search(X, W, S, 2, 128, "f32")
+    order = oracle.rank_groups(S)
+    evals = {}
+    for combo in itertools.product((1, 2, 3), repeat=4):
+        c = np.array(combo)
+        if (c == 1).sum() != (c == 3).sum():
+            continue
+        wh = oracle.trial_weights(W, c, 128, "f32")
+        evals[combo] = oracle.kl_divergence(X, W, wh)
+    assert len(evals) == 19
+    for r in range(3):
+        b = tuple(oracle.allocation(order, r, 2).tolist())
+        assert kl[r] == pytest.approx(evals[b], rel=1e-10)
+    assert min(evals.values()) <= kl[rs] + 1e-15
+
+
+# ---------------------------------------------------------------- packing
+def _naive_pack(codes, bits, g):
+    n, m = codes.shape
+    out = []
+    for j in range(m // g):
+        for p in range(int(bits[j])):
+            for i in range(n):
+                for w in range(g // 32):
+                    word = 0
+                    for c in range(32):
+                        if (int(codes[i, j * g + 32 * w + c]) >> p) & 1:
+                            word |= 1 << c
+                    out.append(word)
+    return np.array(out, dtype=np.uint32)
+
+
+@pytest.mark.parametrize("g", [32, 64, 128])
+def test_pack_naive_roundtrip_and_size(g):
+    rng = np.random.default_rng(g)
+    n, m, N = 5, 4 * g, 2
+    order = oracle.rank_groups(rng.random(m // g))
+    bits = oracle.allocation(order, 1, N)
+    codes = np.zeros((n, m), dtype=np.uint8)
+    for j in range(m // g):
+        codes[:, j * g:(j + 1) * g] = rng.integers(0, 2 ** int(bits[j]), size=(n, g))
+    words = oracle.pack_bitplanes(codes, bits, g)
+    assert words.size == oracle.packed_words(n, m, N) == n * m * N // 32
+    np.testing.assert_array_equal(words, _naive_pack(codes, bits, g))
+    np.testing.assert_array_equal(oracle.unpack_bitplanes(words, bits, n, m, g), codes)
+
+
+def test_pack_all_max_and_single_bit():
+    n, m, g = 3, 128, 32
+    bits = np.array([3, 1, 2, 2], dtype=np.int8)
+    codes = np.zeros((n, m), dtype=np.uint8)
+    for j in range(4):
+        codes[:, j * g:(j + 1) * g] = 2 ** int(bits[j]) - 1
+    assert np.all(oracle.pack_bitplanes(codes, bits, g) == 0xFFFFFFFF)
+    codes[:] = 0
+    codes[2, 64 + 5] = 2                              # group 2, plane 1, row 2, bit 5
+    words = oracle.pack_bitplanes(codes, bits, g)
+    off = n * 1 * (3 + 1) + (1 * n + 2) * 1
+    assert np.count_nonzero(words) == 1 and words[off] == (1 << 5)
