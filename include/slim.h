@@ -1,0 +1,198 @@
+/*
+ * slim.h -- C ABI of the SliM-LLM per-layer quantizer path on gfx950 (MI355X).
+ *
+ * The path quantizes one linear layer W[n, m] (n outputs, m inputs) from
+ * calibration activations X[T, m], as described in "SliM-LLM: Salience-Driven
+ * Mixed-Precision Quantization for Large Language Models" (blog digest on
+ * rkmt.cn, section "core design": component one SBA and component two SQC;
+ * the scime.ai summary, section "Approach"):
+ *
+ *   slim_hessian        H = 2 X^T X                         (component one, Hessian from calibration)
+ *   slim_salience       d = diag((H + a I)^-1), delta = w^2 / d^2, group means   (component one)
+ *   slim_sba_search     balanced bit allocation scored by output KL           (component one)
+ *   slim_sqc_calibrate  3-sigma mask + tau-grid search of scale and zero       (component two)
+ *   slim_pack           group-structured bit-planes, no bitmap                (FAQ: storage)
+ *
+ * Conventions shared by every call:
+ *  - Pointers are DEVICE pointers unless the parameter says "host".  Arrays
+ *    are dense and row-major; X, W, H, hinv_diag, codes, packed and the
+ *    workspace must be 16-byte aligned (SLIM_E_ALIGN otherwise).
+ *  - The caller owns all memory.  The library allocates nothing and keeps no
+ *    per-call state; scratch memory comes from a caller-provided workspace of
+ *    at least the size the matching *_workspace() query returns.
+ *  - Every call enqueues its kernels on `stream` (a hipStream_t passed as
+ *    void*, NULL = the default stream) and returns without synchronising.
+ *  - Return value: SLIM_OK, or a negative SLIM_E_* code.  Arguments are
+ *    checked before anything is enqueued; on an error nothing is enqueued.
+ *    After SLIM_E_HIP, slim_last_hip_error() gives the hipError_t (per thread).
+ *  - Numeric failures found on the device are reported through a device
+ *    int32 `info` word (LAPACK convention): 0 = fine, j > 0 = the leading minor
+ *    of order j is not positive definite, -1 = non-finite input.
+ *  - Group size g is one of 32, 64, 128 and must divide m.  Average bit-width
+ *    N satisfies 2 <= N <= 7 (bit set {N-1, N, N+1}, codes fit in a byte).
+ *  - Storage dtypes: SLIM_BF16 (bfloat16 bit patterns) or SLIM_F32.
+ *  - Calls on distinct buffers may run concurrently; calls sharing a
+ *    workspace must be ordered on one stream.
+ */
+#ifndef SLIM_H
+#define SLIM_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SLIM_VERSION 1
+
+enum slim_status {
+  SLIM_OK = 0,
+  SLIM_E_NULL = -1,      /* a required pointer is NULL                       */
+  SLIM_E_SHAPE = -2,     /* a size is out of range or sizes are inconsistent */
+  SLIM_E_DTYPE = -3,     /* unsupported storage dtype                        */
+  SLIM_E_PARAM = -4,     /* a hyper-parameter is out of range                */
+  SLIM_E_WORKSPACE = -5, /* workspace missing or smaller than required       */
+  SLIM_E_HIP = -6,       /* a HIP runtime call or launch failed              */
+  SLIM_E_ALIGN = -7      /* a vector-loaded pointer is not 16-byte aligned   */
+};
+
+/* Size limits: input width m <= SLIM_MAX_WIDTH; groups per row
+ * k = m / g <= SLIM_MAX_GROUPS for the SBA search. */
+#define SLIM_MAX_WIDTH 65536
+#define SLIM_MAX_GROUPS 2048
+
+typedef enum slim_dtype { SLIM_F32 = 0, SLIM_BF16 = 1 } slim_dtype;
+
+/* Library version (SLIM_VERSION). */
+int slim_version(void);
+
+/* Static, human-readable text for a status code (host). */
+const char *slim_status_string(int status);
+
+/* hipError_t of the last failed HIP call on this thread (0 if none). */
+int slim_last_hip_error(void);
+
+/* ------------------------------------------------------------------------
+ * Hessian proxy (component one: "the Hessian is approximated from the
+ * calibration activations, no back-propagation").
+ *
+ *   H[m, m] (+)= 2 * X^T X,   X[t, m] token-major in dtype xdt.
+ *
+ * H is float32, full and exactly symmetric on return.  accumulate = 0
+ * overwrites H; accumulate = 1 adds to it (H must then be symmetric on entry,
+ * e.g. from a previous call on an earlier token chunk).  t = 0 writes zeros
+ * (or leaves H unchanged when accumulating).  The token sum runs in float32
+ * on MFMA (bfloat16 or float32 operands as stored) and is reduced over
+ * token splits in a fixed order, so results are bitwise reproducible.
+ * Requires t >= 0, m >= 1.
+ * ---------------------------------------------------------------------- */
+size_t slim_hessian_workspace(int64_t t, int64_t m);
+int slim_hessian(const void *X, int xdt, int64_t t, int64_t m, float *H, int accumulate,
+                 void *ws, size_t ws_bytes, void *stream);
+
+/* ------------------------------------------------------------------------
+ * Salience (component one: element salience is the SparseGPT elimination
+ * error w_ij^2 / [H^-1]_jj^2; scime.ai "Approach": groups are ranked by their
+ * average salience).
+ *
+ *   H_d = H + damp_frac * mean(diag H) * I           (float64)
+ *   hinv_diag[j] = [H_d^-1]_jj                       (float64 Cholesky, stored float32)
+ *   delta_ij = fl32(fl32(w_ij * w_ij) / fl32(d_j * d_j)),  d = hinv_diag
+ *   group_sal[q] = mean of delta over rows 0..n-1, columns q*g .. q*g+g-1
+ *                  (float64 sum in a fixed order, stored float64: it decides
+ *                  the ranking, so no rounding is added before the search)
+ *
+ * H: float32 [m, m], symmetric (only the lower triangle is read).
+ * W: [n, m] in dtype wdt.  elem_sal: optional float32 [n, m] (NULL = skip).
+ * info: device int32, see conventions; outputs are unspecified if info != 0.
+ * Requires n >= 1, m >= 1, m % group == 0, damp_frac >= 0.
+ * ---------------------------------------------------------------------- */
+size_t slim_salience_workspace(int64_t n, int64_t m, int group);
+int slim_salience(const float *H, int64_t m, double damp_frac, const void *W, int wdt, int64_t n,
+                  int group, float *hinv_diag, double *group_sal, float *elem_sal, int32_t *info,
+                  void *ws, size_t ws_bytes, void *stream);
+
+/* ------------------------------------------------------------------------
+ * SBA search (component one: bit-widths minimise the KL divergence of the
+ * layer output under |G_{N-1}| = |G_{N+1}|, searched by two pointers over
+ * [0, k/2]).
+ *
+ * Groups are ranked by descending group_sal (ties: lower index first).  For
+ * every step r = 0 .. floor(k/2) the first r ranked groups get N+1 bits, the
+ * last r get N-1 and the rest N.  Each step's trial weights are the min-max
+ * quantizer at tau = 1 per row segment, stored back in dtype wdt, and the
+ * step is scored by
+ *     kl[r] = mean_t KL( softmax_j(x_t W^T) || softmax_j(x_t W_r^T) )
+ * (softmax over the n outputs, natural log).  r_star = first argmin of kl;
+ * bits[q] is the allocation at r_star.
+ *
+ * X: [t, m] (dtype xdt), W: [n, m] (dtype wdt == xdt); group_sal float64 [k];
+ * bits int8 [k]; kl float64 [floor(k/2)+1]; r_star int32 [1].
+ * Requires t >= 1, n >= 1, m % group == 0.
+ * ---------------------------------------------------------------------- */
+size_t slim_sba_workspace(int64_t t, int64_t n, int64_t m, int group, int dtype);
+int slim_sba_search(const void *X, int xdt, int64_t t, const void *W, int wdt, int64_t n, int64_t m,
+                    int group, const double *group_sal, int avg_bits, int8_t *bits, double *kl,
+                    int32_t *r_star, void *ws, size_t ws_bytes, void *stream);
+
+/* ------------------------------------------------------------------------
+ * SQC calibration (component two: salient weights outside mu +- 3 sigma and
+ * the rest share one quantizer; tau scales its scale and zero over n_tau + 1
+ * linear candidates in [1 - lambda, 1 + lambda]; the candidate with the
+ * smallest salience-weighted l2 error wins; no parameter is added).
+ *
+ * Per row segment (row i, group q, b = bits[q], maxq = 2^b - 1):
+ *   lo/hi = min/max; s0 = (hi-lo)/maxq (1 if 0); z0 = -lo/s0       (float32)
+ *   mask  = w < mu - 3 sigma  or  w > mu + 3 sigma  (population sigma, float64)
+ *   for tau_i = 1 + lambda (2i - n_tau)/n_tau:  s = tau s0, z = tau z0,
+ *       q = clamp(rint(w * (1/s) + z), 0, maxq), e = w - (q - z) s   (float32, no FMA)
+ *       E_i = mean_{mask}(delta e^2) + mean_{~mask}(delta e^2)     (float64)
+ *   tau* = first argmin E;  scale = tau* s0, zero = tau* z0, codes at tau*.
+ *
+ * W: [n, m] (dtype wdt); bits int8 [k]; hinv_diag float32 [m] (delta as in
+ * slim_salience); scale, zero float32 [n, k]; codes uint8 [n, m];
+ * mask uint32 [n, m/32] (bit c of word w of row i <-> column 32w + c);
+ * tau_idx uint8 [n, k] or NULL.  Requires 1 <= n_tau <= 255, lambda in
+ * [0, 1), bits[q] in [1, 8].  n = 0 is a no-op.
+ * ---------------------------------------------------------------------- */
+int slim_sqc_calibrate(const void *W, int wdt, int64_t n, int64_t m, int group, const int8_t *bits,
+                       const float *hinv_diag, double lambda, int n_tau, float *scale, float *zero,
+                       uint8_t *codes, uint32_t *mask, uint8_t *tau_idx, void *stream);
+
+/* The tau candidates slim_sqc_calibrate uses, written to host memory
+ * out_host[0 .. n_tau] (float64 evaluation rounded once to float32). */
+int slim_tau_table(double lambda, int n_tau, float *out_host);
+
+/* ------------------------------------------------------------------------
+ * Packing (FAQ on storage: group-wise bit-widths need no bitmap or codebook
+ * and no extra storage; dequantization keeps the uniform-quantizer form).
+ *
+ * Bit-planes, group-major.  Group q starts at word off(q) = n (g/32) *
+ * sum_{q' < q} bits[q'];  word (q, plane p, row i, w) is at off(q) +
+ * (p n + i)(g/32) + w; its bit c is bit p of codes[i, q g + 32 w + c].
+ * packed: uint32 [n m avg_bits / 32] (slim_pack_words).  Bits above bits[q]
+ * in a code are ignored.  If bits[q] leaves [1, 8] or the widths do not sum to
+ * k * avg_bits, *info (device int32, may be NULL) is set to 1 and no word
+ * outside `packed` is written.  n = 0 is a no-op.
+ * ---------------------------------------------------------------------- */
+int64_t slim_pack_words(int64_t n, int64_t m, int avg_bits);
+int slim_pack(const uint8_t *codes, int64_t n, int64_t m, int group, const int8_t *bits,
+              int avg_bits, uint32_t *packed, int32_t *info, void *stream);
+
+/* ------------------------------------------------------------------------
+ * Kernel timing (instrumentation, not part of the method).  When enabled,
+ * the library records a pair of HIP events on the launch stream around every
+ * launch of the named kernels: "hessian_gram", "chol_update", "sba_klgemm",
+ * "sqc_calibrate", "pack_planes".  slim_timing_read synchronises those events
+ * and returns the summed milliseconds and the launch count since the last
+ * reset.  Returns SLIM_E_PARAM for an unknown name.
+ * ---------------------------------------------------------------------- */
+int slim_timing_enable(int on);
+int slim_timing_reset(void);
+int slim_timing_read(const char *kernel, double *total_ms, int64_t *launches);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* SLIM_H */

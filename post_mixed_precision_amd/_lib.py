@@ -1,0 +1,225 @@
+"""ctypes binding of libslim.so (argument marshalling only).
+
+Every computation runs in the HIP kernels behind include/slim.h; this module
+only allocates outputs and workspaces with torch on the device, passes raw
+pointers and the current HIP stream, and turns status codes into exceptions.
+There is no fallback: if the library is missing this module raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libslim.so")
+
+SLIM_F32, SLIM_BF16 = 0, 1
+STATUS = {0: "SLIM_OK", -1: "SLIM_E_NULL", -2: "SLIM_E_SHAPE", -3: "SLIM_E_DTYPE",
+          -4: "SLIM_E_PARAM", -5: "SLIM_E_WORKSPACE", -6: "SLIM_E_HIP", -7: "SLIM_E_ALIGN"}
+
+_c_i64, _c_int, _c_dbl, _c_vp, _c_sz = ctypes.c_int64, ctypes.c_int, ctypes.c_double, ctypes.c_void_p, ctypes.c_size_t
+
+_SIGS = {
+    "slim_version": (_c_int, []),
+    "slim_status_string": (ctypes.c_char_p, [_c_int]),
+    "slim_last_hip_error": (_c_int, []),
+    "slim_hessian_workspace": (_c_sz, [_c_i64, _c_i64]),
+    "slim_hessian": (_c_int, [_c_vp, _c_int, _c_i64, _c_i64, _c_vp, _c_int, _c_vp, _c_sz, _c_vp]),
+    "slim_salience_workspace": (_c_sz, [_c_i64, _c_i64, _c_int]),
+    "slim_salience": (_c_int, [_c_vp, _c_i64, _c_dbl, _c_vp, _c_int, _c_i64, _c_int, _c_vp, _c_vp, _c_vp,
+                               _c_vp, _c_vp, _c_sz, _c_vp]),
+    "slim_sba_workspace": (_c_sz, [_c_i64, _c_i64, _c_i64, _c_int, _c_int]),
+    "slim_sba_search": (_c_int, [_c_vp, _c_int, _c_i64, _c_vp, _c_int, _c_i64, _c_i64, _c_int, _c_vp, _c_int,
+                                 _c_vp, _c_vp, _c_vp, _c_vp, _c_sz, _c_vp]),
+    "slim_sqc_calibrate": (_c_int, [_c_vp, _c_int, _c_i64, _c_i64, _c_int, _c_vp, _c_vp, _c_dbl, _c_int, _c_vp,
+                                    _c_vp, _c_vp, _c_vp, _c_vp, _c_vp]),
+    "slim_tau_table": (_c_int, [_c_dbl, _c_int, _c_vp]),
+    "slim_pack_words": (_c_i64, [_c_i64, _c_i64, _c_int]),
+    "slim_pack": (_c_int, [_c_vp, _c_i64, _c_i64, _c_int, _c_vp, _c_int, _c_vp, _c_vp, _c_vp]),
+    "slim_timing_enable": (_c_int, [_c_int]),
+    "slim_timing_reset": (_c_int, []),
+    "slim_timing_read": (_c_int, [ctypes.c_char_p, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(_c_i64)]),
+}
+
+_lib = None
+
+
+class SlimError(RuntimeError):
+    pass
+
+
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load libslim.so (import torch first so both share one HIP runtime)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise ImportError(f"libslim.so not built at {path}; run post_mixed_precision_amd.build.build()")
+    try:
+        import torch  # noqa: F401  (loads torch's HIP runtime first: same soname, one runtime)
+    except Exception:  # pragma: no cover
+        pass
+    lib = ctypes.CDLL(path)
+    for name, (res, args) in _SIGS.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    _lib = lib
+    return lib
+
+
+def check(status: int, what: str):
+    if status != 0:
+        lib = load_library()
+        msg = lib.slim_status_string(status).decode()
+        extra = f" (hipError {lib.slim_last_hip_error()})" if status == -6 else ""
+        raise SlimError(f"{what}: {STATUS.get(status, status)}: {msg}{extra}")
+
+
+# --------------------------------------------------------------------------
+# torch-facing wrappers
+# --------------------------------------------------------------------------
+def _torch():
+    import torch
+    return torch
+
+
+def _dtype_code(t) -> int:
+    torch = _torch()
+    if t.dtype == torch.bfloat16:
+        return SLIM_BF16
+    if t.dtype == torch.float32:
+        return SLIM_F32
+    raise SlimError(f"unsupported dtype {t.dtype}; use bfloat16 or float32")
+
+
+def _dev(t):
+    torch = _torch()
+    if not (isinstance(t, torch.Tensor) and t.is_cuda):
+        raise SlimError("tensors must live in GPU memory")
+    if not t.is_contiguous():
+        raise SlimError("tensors must be contiguous")
+    return t
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device):
+    return ctypes.c_void_p(_torch().cuda.current_stream(device).cuda_stream)
+
+
+def _ws(nbytes: int, device):
+    return _torch().empty(max(int(nbytes), 256), dtype=_torch().uint8, device=device)
+
+
+def hessian(X, H=None, accumulate: bool = False):
+    """H (+)= 2 X^T X, X [T, m] bf16/f32 on the GPU -> H float32 [m, m]."""
+    torch = _torch()
+    lib = load_library()
+    X = _dev(X)
+    T, m = X.shape
+    if H is None:
+        H = torch.empty((m, m), dtype=torch.float32, device=X.device)
+    ws = _ws(lib.slim_hessian_workspace(T, m), X.device)
+    check(lib.slim_hessian(_ptr(X), _dtype_code(X), T, m, _ptr(H), int(accumulate), _ptr(ws), ws.numel(),
+                           _stream(X.device)), "slim_hessian")
+    return H
+
+
+def salience(H, W, group: int, damp_frac: float = 0.01, elem: bool = False):
+    """-> (hinv_diag f32 [m], group_sal f64 [k], info i32 [1], elem_sal f32 [n, m] or None)."""
+    torch = _torch()
+    lib = load_library()
+    H, W = _dev(H), _dev(W)
+    n, m = W.shape
+    k = m // group
+    hinv = torch.empty(m, dtype=torch.float32, device=W.device)
+    gsal = torch.empty(k, dtype=torch.float64, device=W.device)
+    info = torch.zeros(1, dtype=torch.int32, device=W.device)
+    esal = torch.empty((n, m), dtype=torch.float32, device=W.device) if elem else None
+    ws = _ws(lib.slim_salience_workspace(n, m, group), W.device)
+    check(lib.slim_salience(_ptr(H), m, float(damp_frac), _ptr(W), _dtype_code(W), n, group, _ptr(hinv), _ptr(gsal),
+                            _ptr(esal), _ptr(info), _ptr(ws), ws.numel(), _stream(W.device)), "slim_salience")
+    return hinv, gsal, info, esal
+
+
+def sba_search(X, W, group_sal, group: int, avg_bits: int):
+    """-> (bits int8 [k], kl f64 [k//2+1], r_star int32 [1])."""
+    torch = _torch()
+    lib = load_library()
+    X, W, group_sal = _dev(X), _dev(W), _dev(group_sal)
+    T, m = X.shape
+    n = W.shape[0]
+    k = m // group
+    bits = torch.empty(k, dtype=torch.int8, device=W.device)
+    kl = torch.empty(k // 2 + 1, dtype=torch.float64, device=W.device)
+    rs = torch.empty(1, dtype=torch.int32, device=W.device)
+    ws = _ws(lib.slim_sba_workspace(T, n, m, group, _dtype_code(W)), W.device)
+    check(lib.slim_sba_search(_ptr(X), _dtype_code(X), T, _ptr(W), _dtype_code(W), n, m, group, _ptr(group_sal),
+                              int(avg_bits), _ptr(bits), _ptr(kl), _ptr(rs), _ptr(ws), ws.numel(),
+                              _stream(W.device)), "slim_sba_search")
+    return bits, kl, rs
+
+
+def sqc_calibrate(W, bits, hinv, group: int, lam: float = 0.1, n_tau: int = 50, want_tau: bool = True):
+    """-> dict(scale, zero [n, k] f32; codes [n, m] u8; mask [n, m/32] i32 bits; tau_idx [n, k] u8)."""
+    torch = _torch()
+    lib = load_library()
+    W, bits, hinv = _dev(W), _dev(bits), _dev(hinv)
+    n, m = W.shape
+    k = m // group
+    dev = W.device
+    out = {
+        "scale": torch.empty((n, k), dtype=torch.float32, device=dev),
+        "zero": torch.empty((n, k), dtype=torch.float32, device=dev),
+        "codes": torch.empty((n, m), dtype=torch.uint8, device=dev),
+        "mask": torch.empty((n, max(m // 32, 1)), dtype=torch.int32, device=dev),
+        "tau_idx": torch.empty((n, k), dtype=torch.uint8, device=dev) if want_tau else None,
+    }
+    check(lib.slim_sqc_calibrate(_ptr(W), _dtype_code(W), n, m, group, _ptr(bits), _ptr(hinv), float(lam),
+                                 int(n_tau), _ptr(out["scale"]), _ptr(out["zero"]), _ptr(out["codes"]),
+                                 _ptr(out["mask"]), _ptr(out["tau_idx"]), _stream(dev)), "slim_sqc_calibrate")
+    return out
+
+
+def pack(codes, bits, group: int, avg_bits: int):
+    """-> (packed int32 words [n*m*N/32] (uint32 bit patterns), info int32 [1])."""
+    torch = _torch()
+    lib = load_library()
+    codes, bits = _dev(codes), _dev(bits)
+    n, m = codes.shape
+    words = lib.slim_pack_words(n, m, avg_bits)
+    if words < 0:
+        raise SlimError("bad pack shape")
+    packed = torch.zeros(max(words, 1), dtype=torch.int32, device=codes.device)
+    info = torch.zeros(1, dtype=torch.int32, device=codes.device)
+    check(lib.slim_pack(_ptr(codes), n, m, group, _ptr(bits), int(avg_bits), _ptr(packed), _ptr(info),
+                        _stream(codes.device)), "slim_pack")
+    return packed[:words], info
+
+
+def tau_table(lam: float = 0.1, n_tau: int = 50) -> np.ndarray:
+    lib = load_library()
+    out = np.zeros(n_tau + 1, dtype=np.float32)
+    check(lib.slim_tau_table(float(lam), int(n_tau), out.ctypes.data_as(ctypes.c_void_p)), "slim_tau_table")
+    return out
+
+
+def timing_enable(on: bool = True):
+    load_library().slim_timing_enable(int(on))
+
+
+def timing_reset():
+    load_library().slim_timing_reset()
+
+
+def timing_read(kernel: str):
+    """-> (total_ms, launches) for a timed kernel since the last reset."""
+    lib = load_library()
+    ms, cnt = ctypes.c_double(), _c_i64()
+    check(lib.slim_timing_read(kernel.encode(), ctypes.byref(ms), ctypes.byref(cnt)), "slim_timing_read")
+    return ms.value, cnt.value

@@ -1,0 +1,245 @@
+// C ABI of libslim: argument checks, workspace sizing, launches, timing.
+// The operations themselves are defined in slim.h and in the kernel sources.
+#include <math.h>
+#include <stdint.h>
+#include <string.h>
+
+#include <mutex>
+#include <vector>
+
+#include "../../include/slim.h"
+#include "kernels.hpp"
+
+namespace {
+
+thread_local int g_last_hip_error = 0;
+
+int hip_fail(hipError_t e) {
+  g_last_hip_error = (int)e;
+  return SLIM_E_HIP;
+}
+
+bool valid_dtype(int dt) { return dt == SLIM_F32 || dt == SLIM_BF16; }
+bool valid_group(int g) { return g == 32 || g == 64 || g == 128; }
+bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+
+// ---- kernel timer ----
+struct TimerSlot {
+  std::vector<std::pair<hipEvent_t, hipEvent_t>> pending;
+  hipEvent_t open = nullptr;
+  double total_ms = 0.0;
+  int64_t launches = 0;
+};
+std::mutex g_timer_mu;
+bool g_timer_on = false;
+TimerSlot g_slots[slim::K_NUM_TIMED];
+const char *g_timer_names[slim::K_NUM_TIMED] = {"hessian_gram", "chol_update", "sba_klgemm", "sqc_calibrate",
+                                                "pack_planes"};
+
+void drain(TimerSlot &s) {
+  for (auto &pr : s.pending) {
+    float ms = 0.0f;
+    if (hipEventSynchronize(pr.second) == hipSuccess && hipEventElapsedTime(&ms, pr.first, pr.second) == hipSuccess) {
+      s.total_ms += ms;
+      s.launches += 1;
+    }
+    (void)hipEventDestroy(pr.first);
+    (void)hipEventDestroy(pr.second);
+  }
+  s.pending.clear();
+}
+
+}  // namespace
+
+namespace slim {
+
+void timer_begin(int id, hipStream_t st) {
+  std::lock_guard<std::mutex> lk(g_timer_mu);
+  if (!g_timer_on) return;
+  hipEvent_t e;
+  if (hipEventCreate(&e) != hipSuccess) return;
+  if (hipEventRecord(e, st) != hipSuccess) {
+    (void)hipEventDestroy(e);
+    return;
+  }
+  g_slots[id].open = e;
+}
+
+void timer_end(int id, hipStream_t st) {
+  std::lock_guard<std::mutex> lk(g_timer_mu);
+  TimerSlot &s = g_slots[id];
+  if (!g_timer_on || !s.open) return;
+  hipEvent_t e;
+  if (hipEventCreate(&e) != hipSuccess) return;
+  if (hipEventRecord(e, st) != hipSuccess) {
+    (void)hipEventDestroy(e);
+    return;
+  }
+  s.pending.emplace_back(s.open, e);
+  s.open = nullptr;
+}
+
+}  // namespace slim
+
+extern "C" {
+
+int slim_version(void) { return SLIM_VERSION; }
+
+const char *slim_status_string(int status) {
+  switch (status) {
+    case SLIM_OK: return "ok";
+    case SLIM_E_NULL: return "a required pointer is NULL";
+    case SLIM_E_SHAPE: return "a size is out of range or sizes are inconsistent";
+    case SLIM_E_DTYPE: return "unsupported storage dtype";
+    case SLIM_E_PARAM: return "a hyper-parameter is out of range";
+    case SLIM_E_WORKSPACE: return "workspace missing or smaller than required";
+    case SLIM_E_HIP: return "a HIP runtime call or launch failed";
+    case SLIM_E_ALIGN: return "a pointer is not 16-byte aligned";
+    default: return "unknown status";
+  }
+}
+
+int slim_last_hip_error(void) { return g_last_hip_error; }
+
+// ---------------------------------------------------------------- Hessian
+size_t slim_hessian_workspace(int64_t t, int64_t m) {
+  if (t < 0 || m < 1 || m > SLIM_MAX_WIDTH) return 0;
+  return slim::hessian_plan(t, m).ws_bytes;
+}
+
+int slim_hessian(const void *X, int xdt, int64_t t, int64_t m, float *H, int accumulate, void *ws, size_t ws_bytes,
+                 void *stream) {
+  if (!H || (t > 0 && !X)) return SLIM_E_NULL;
+  if (!valid_dtype(xdt)) return SLIM_E_DTYPE;
+  if (t < 0 || m < 1 || m > SLIM_MAX_WIDTH) return SLIM_E_SHAPE;
+  if (!aligned16(H) || (t > 0 && !aligned16(X))) return SLIM_E_ALIGN;
+  const slim::HessianPlan p = slim::hessian_plan(t, m);
+  if (!ws || ws_bytes < p.ws_bytes) return SLIM_E_WORKSPACE;
+  if (!aligned16(ws)) return SLIM_E_ALIGN;
+  hipError_t e = slim::launch_hessian(X, xdt == SLIM_BF16, t, m, H, accumulate != 0, ws, p, (hipStream_t)stream);
+  return e == hipSuccess ? SLIM_OK : hip_fail(e);
+}
+
+// ---------------------------------------------------------------- salience
+size_t slim_salience_workspace(int64_t n, int64_t m, int group) {
+  if (n < 1 || m < 1 || m > SLIM_MAX_WIDTH || !valid_group(group) || m % group) return 0;
+  return slim::salience_ws_bytes(n, m, group);
+}
+
+int slim_salience(const float *H, int64_t m, double damp_frac, const void *W, int wdt, int64_t n, int group,
+                  float *hinv_diag, double *group_sal, float *elem_sal, int32_t *info, void *ws, size_t ws_bytes,
+                  void *stream) {
+  if (!H || !W || !hinv_diag || !group_sal || !info) return SLIM_E_NULL;
+  if (!valid_dtype(wdt)) return SLIM_E_DTYPE;
+  if (n < 1 || m < 1 || m > SLIM_MAX_WIDTH) return SLIM_E_SHAPE;
+  if (!valid_group(group) || m % group) return SLIM_E_SHAPE;
+  if (!(damp_frac >= 0.0) || !isfinite(damp_frac)) return SLIM_E_PARAM;
+  if (!aligned16(H) || !aligned16(W) || !aligned16(hinv_diag)) return SLIM_E_ALIGN;
+  const size_t need = slim::salience_ws_bytes(n, m, group);
+  if (!ws || ws_bytes < need) return SLIM_E_WORKSPACE;
+  if (!aligned16(ws)) return SLIM_E_ALIGN;
+  hipError_t e = slim::launch_salience(H, m, damp_frac, W, wdt == SLIM_BF16, n, group, hinv_diag, group_sal, elem_sal,
+                                       info, ws, (hipStream_t)stream);
+  return e == hipSuccess ? SLIM_OK : hip_fail(e);
+}
+
+// ---------------------------------------------------------------- SBA
+size_t slim_sba_workspace(int64_t t, int64_t n, int64_t m, int group, int dtype) {
+  if (t < 1 || n < 1 || m < 1 || m > SLIM_MAX_WIDTH || !valid_group(group) || m % group || !valid_dtype(dtype))
+    return 0;
+  if (m / group > SLIM_MAX_GROUPS) return 0;
+  return slim::sba_plan(t, n, m, group, dtype == SLIM_BF16).ws_bytes;
+}
+
+int slim_sba_search(const void *X, int xdt, int64_t t, const void *W, int wdt, int64_t n, int64_t m, int group,
+                    const double *group_sal, int avg_bits, int8_t *bits, double *kl, int32_t *r_star, void *ws,
+                    size_t ws_bytes, void *stream) {
+  if (!X || !W || !group_sal || !bits || !kl || !r_star) return SLIM_E_NULL;
+  if (!valid_dtype(xdt) || xdt != wdt) return SLIM_E_DTYPE;
+  if (t < 1 || n < 1 || m < 1 || m > SLIM_MAX_WIDTH) return SLIM_E_SHAPE;
+  if (!valid_group(group) || m % group || m / group > SLIM_MAX_GROUPS) return SLIM_E_SHAPE;
+  if (avg_bits < 2 || avg_bits > 7) return SLIM_E_PARAM;
+  if (!aligned16(X) || !aligned16(W)) return SLIM_E_ALIGN;
+  const slim::SbaPlan p = slim::sba_plan(t, n, m, group, xdt == SLIM_BF16);
+  if (!ws || ws_bytes < p.ws_bytes) return SLIM_E_WORKSPACE;
+  if (!aligned16(ws)) return SLIM_E_ALIGN;
+  hipError_t e = slim::launch_sba(X, W, xdt == SLIM_BF16, t, n, m, group, group_sal, avg_bits, bits, kl, r_star, ws, p,
+                                  (hipStream_t)stream);
+  return e == hipSuccess ? SLIM_OK : hip_fail(e);
+}
+
+// ---------------------------------------------------------------- SQC
+int slim_tau_table(double lambda, int n_tau, float *out_host) {
+  if (!out_host) return SLIM_E_NULL;
+  if (n_tau < 1 || n_tau > 255 || !(lambda >= 0.0 && lambda < 1.0)) return SLIM_E_PARAM;
+  slim::TauTable tt;
+  slim::make_tau_table(lambda, n_tau, tt);
+  memcpy(out_host, tt.t, sizeof(float) * (size_t)(n_tau + 1));
+  return SLIM_OK;
+}
+
+int slim_sqc_calibrate(const void *W, int wdt, int64_t n, int64_t m, int group, const int8_t *bits,
+                       const float *hinv_diag, double lambda, int n_tau, float *scale, float *zero, uint8_t *codes,
+                       uint32_t *mask, uint8_t *tau_idx, void *stream) {
+  if (!valid_dtype(wdt)) return SLIM_E_DTYPE;
+  if (n < 0 || m < 1 || m > SLIM_MAX_WIDTH || !valid_group(group) || m % group) return SLIM_E_SHAPE;
+  if (n_tau < 1 || n_tau > 255 || !(lambda >= 0.0 && lambda < 1.0)) return SLIM_E_PARAM;
+  if (n == 0) return SLIM_OK;
+  if (!W || !bits || !hinv_diag || !scale || !zero || !codes || !mask) return SLIM_E_NULL;
+  if (!aligned16(W) || !aligned16(hinv_diag) || !aligned16(codes)) return SLIM_E_ALIGN;
+  slim::TauTable tt;
+  slim::make_tau_table(lambda, n_tau, tt);
+  hipError_t e = slim::launch_sqc(W, wdt == SLIM_BF16, n, m, group, bits, hinv_diag, tt, n_tau, scale, zero, codes,
+                                  mask, tau_idx, (hipStream_t)stream);
+  return e == hipSuccess ? SLIM_OK : hip_fail(e);
+}
+
+// ---------------------------------------------------------------- pack
+int64_t slim_pack_words(int64_t n, int64_t m, int avg_bits) {
+  if (n < 0 || m < 0 || avg_bits < 1 || avg_bits > 8) return -1;
+  return n * m * avg_bits / 32;
+}
+
+int slim_pack(const uint8_t *codes, int64_t n, int64_t m, int group, const int8_t *bits, int avg_bits,
+              uint32_t *packed, int32_t *info, void *stream) {
+  if (n < 0 || m < 1 || m > SLIM_MAX_WIDTH || !valid_group(group) || m % group) return SLIM_E_SHAPE;
+  if (avg_bits < 1 || avg_bits > 8) return SLIM_E_PARAM;
+  if (n == 0) return SLIM_OK;
+  if (!codes || !bits || !packed) return SLIM_E_NULL;
+  if (!aligned16(codes) || !aligned16(packed)) return SLIM_E_ALIGN;
+  hipError_t e = slim::launch_pack(codes, n, m, group, bits, avg_bits, packed, info, (hipStream_t)stream);
+  return e == hipSuccess ? SLIM_OK : hip_fail(e);
+}
+
+// ---------------------------------------------------------------- timing
+int slim_timing_enable(int on) {
+  std::lock_guard<std::mutex> lk(g_timer_mu);
+  g_timer_on = on != 0;
+  return SLIM_OK;
+}
+
+int slim_timing_reset(void) {
+  std::lock_guard<std::mutex> lk(g_timer_mu);
+  for (auto &s : g_slots) {
+    drain(s);
+    s.total_ms = 0.0;
+    s.launches = 0;
+  }
+  return SLIM_OK;
+}
+
+int slim_timing_read(const char *kernel, double *total_ms, int64_t *launches) {
+  if (!kernel || !total_ms || !launches) return SLIM_E_NULL;
+  std::lock_guard<std::mutex> lk(g_timer_mu);
+  for (int i = 0; i < slim::K_NUM_TIMED; ++i) {
+    if (strcmp(kernel, g_timer_names[i]) == 0) {
+      drain(g_slots[i]);
+      *total_ms = g_slots[i].total_ms;
+      *launches = g_slots[i].launches;
+      return SLIM_OK;
+    }
+  }
+  return SLIM_E_PARAM;
+}
+
+}  // extern "C"

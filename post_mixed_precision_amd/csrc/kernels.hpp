@@ -1,0 +1,59 @@
+// Host-side launchers of the gfx950 kernels (internal to libslim).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace slim {
+
+// Kernel timing hooks (capi.cpp): record an event pair around a launch when
+// timing is enabled; no-ops otherwise.
+void timer_begin(int kernel_id, hipStream_t st);
+void timer_end(int kernel_id, hipStream_t st);
+enum TimedKernel { K_HESSIAN = 0, K_CHOL_UPDATE, K_SBA_KLGEMM, K_SQC, K_PACK, K_NUM_TIMED };
+
+inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+// ---- Hessian ----
+struct HessianPlan {
+  int nb, ntiles, nsplit;
+  int64_t tok_per_split;
+  size_t ws_bytes;
+};
+HessianPlan hessian_plan(int64_t t, int64_t m);
+hipError_t launch_hessian(const void *X, bool bf16, int64_t t, int64_t m, float *H, bool accumulate,
+                          void *ws, const HessianPlan &p, hipStream_t st);
+
+// ---- Salience (damped inverse diagonal + group means) ----
+size_t salience_ws_bytes(int64_t n, int64_t m, int group);
+hipError_t launch_salience(const float *H, int64_t m, double damp, const void *W, bool bf16,
+                           int64_t n, int group, float *hinv, double *gsal, float *esal,
+                           int32_t *info, void *ws, hipStream_t st);
+
+// ---- SBA ----
+struct SbaPlan {
+  int k, R, nchunk;          // groups, steps (k/2+1), output chunks of 128
+  int64_t tb;                // tokens per batch
+  int nbatch;
+  int64_t combine_blocks;    // total combine blocks over all batches
+  size_t off_wv, off_order, off_sp, off_sq, off_part, ws_bytes;
+};
+SbaPlan sba_plan(int64_t t, int64_t n, int64_t m, int group, bool bf16);
+hipError_t launch_sba(const void *X, const void *W, bool bf16, int64_t t, int64_t n, int64_t m,
+                      int group, const double *gsal, int avg_bits, int8_t *bits, double *kl,
+                      int32_t *r_star, void *ws, const SbaPlan &p, hipStream_t st);
+
+// ---- SQC ----
+struct TauTable {
+  float t[256];
+};
+void make_tau_table(double lambda, int n_tau, TauTable &tt);
+hipError_t launch_sqc(const void *W, bool bf16, int64_t n, int64_t m, int group, const int8_t *bits,
+                      const float *hinv, const TauTable &tt, int n_tau, float *scale, float *zero,
+                      uint8_t *codes, uint32_t *mask, uint8_t *tau_idx, hipStream_t st);
+
+// ---- Pack ----
+hipError_t launch_pack(const uint8_t *codes, int64_t n, int64_t m, int group, const int8_t *bits,
+                       int avg_bits, uint32_t *packed, int32_t *info, hipStream_t st);
+
+}  // namespace slim

@@ -1,0 +1,402 @@
+// Element and group salience on gfx950.
+//
+// "SliM-LLM" blog digest (rkmt.cn), core design, component one: the salience
+// of w_ij is the SparseGPT elimination error w_ij^2 / [H^-1]_jj^2; the
+// scime.ai summary ("Approach") ranks groups by average salience.  The
+// inverse is taken of H_d = H + damp * mean(diag H) * I (GPTQ-style damping;
+// the pages are silent on it).
+//
+// diag(H_d^-1) in float64.  Blocked right-looking Cholesky with 64-wide panels
+// on an m_p x m_p copy (m_p = m rounded up to 64, padded with the identity so
+// no kernel sees a ragged tile).  The same sweep performs block forward
+// substitution L Z = I: when panel p is factored, its rows of Z = L^-1 become
+// final (Z_p = L_pp^-1 R_p) and every later row block is updated
+// R_i -= L_ip Z_p.  Since H_d^-1 = Z^T Z, d_j is the squared norm of column j of
+// Z, accumulated panel by panel in a fixed order.  Per panel:
+//   chol_diag   (1 workgroup)  factor the 64x64 diagonal block in LDS, invert it
+//   chol_panel  L_ip = A_ip L_pp^-T for the rows below; Z_p = L_pp^-1 R_p and d += col-norms^2
+//   chol_update trailing A_ij -= L_ip L_jp^T (lower tiles) and R_ij -= L_ip Z_pj
+// The two GEMM-shaped kernels use v_mfma_f64_16x16x4_f64 on 64x64 tiles.
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace slim {
+
+constexpr int NBK = 64;   // panel width
+constexpr int SP = 65;    // LDS pitch (doubles) of 64x64 operand tiles
+
+__global__ __launch_bounds__(256) void sal_alpha_kernel(const float *__restrict__ H, int64_t m, double damp,
+                                                        double *__restrict__ alpha, int32_t *__restrict__ info) {
+  __shared__ double red[256];
+  double s = 0.0;
+  for (int64_t j = threadIdx.x; j < m; j += 256) s += (double)H[j * m + j];
+  red[threadIdx.x] = s;
+  __syncthreads();
+  for (int w = 128; w > 0; w >>= 1) {
+    if ((int)threadIdx.x < w) red[threadIdx.x] += red[threadIdx.x + w];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) {
+    alpha[0] = damp * (red[0] / (double)m);
+    info[0] = 0;
+  }
+}
+
+// A = lower(H) mirrored + alpha I (identity in the padding), Z = I, d = 0.
+__global__ __launch_bounds__(256) void sal_init_kernel(const float *__restrict__ H, int64_t m, int64_t mp,
+                                                       const double *__restrict__ alpha, double *__restrict__ A,
+                                                       double *__restrict__ Z, double *__restrict__ d,
+                                                       int32_t *__restrict__ info) {
+  const int64_t total = mp * mp;
+  const double a = alpha[0];
+  bool bad = false;
+  for (int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x; idx < total; idx += (int64_t)gridDim.x * 256) {
+    const int64_t i = idx / mp, j = idx % mp;
+    double v;
+    if (i < m && j < m) {
+      const float h = (j <= i) ? H[i * m + j] : H[j * m + i];
+      if (!isfinite(h)) bad = true;
+      v = (double)h + (i == j ? a : 0.0);
+    } else {
+      v = (i == j) ? 1.0 : 0.0;
+    }
+    A[idx] = v;
+    Z[idx] = (i == j) ? 1.0 : 0.0;
+    if (j == 0) d[i] = 0.0;
+  }
+  if (bad) atomicExch(info, -1);
+}
+
+// Factor the diagonal block of panel p and invert it; writes L_pp into A and
+// (L_pp^-1)^T into TinvT (64 x 64, row k holds column k of the inverse).
+__global__ __launch_bounds__(256) void chol_diag_kernel(double *__restrict__ A, int64_t mp, int p,
+                                                        double *__restrict__ TinvT, int32_t *__restrict__ info) {
+  __shared__ double L[NBK][SP];
+  __shared__ double Ti[NBK][SP];
+  const int tid = threadIdx.x;
+  const int64_t k0 = (int64_t)p * NBK;
+  for (int idx = tid; idx < NBK * NBK; idx += 256) {
+    const int i = idx / NBK, j = idx % NBK;
+    L[i][j] = (j <= i) ? A[(k0 + i) * mp + k0 + j] : 0.0;
+    Ti[i][j] = 0.0;
+  }
+  __syncthreads();
+  for (int j = 0; j < NBK; ++j) {
+    if (tid == 0) {
+      double v = L[j][j];
+      if (!(v > 0.0) || !isfinite(v)) {
+        atomicCAS(info, 0, (int)(k0 + j + 1));
+        v = 1.0;  // keep going with a harmless pivot; outputs are unspecified
+      }
+      L[j][j] = sqrt(v);
+    }
+    __syncthreads();
+    const double djj = L[j][j];
+    for (int i = j + 1 + tid; i < NBK; i += 256) L[i][j] = L[i][j] / djj;
+    __syncthreads();
+    const int r = NBK - 1 - j;
+    for (int idx = tid; idx < r * r; idx += 256) {
+      const int i = j + 1 + idx / r, l = j + 1 + idx % r;
+      if (l <= i) L[i][l] = L[i][l] - L[i][j] * L[l][j];
+    }
+    __syncthreads();
+  }
+  // Inverse of the lower-triangular block, one row at a time, columns in parallel.
+  for (int i = 0; i < NBK; ++i) {
+    if (tid <= i) {
+      const int c = tid;
+      double s = (c == i) ? 1.0 : 0.0;
+      for (int l = c; l < i; ++l) s = s - L[i][l] * Ti[l][c];
+      Ti[i][c] = s / L[i][i];
+    }
+    __syncthreads();
+  }
+  for (int idx = tid; idx < NBK * NBK; idx += 256) {
+    const int i = idx / NBK, j = idx % NBK;
+    if (j <= i) A[(k0 + i) * mp + k0 + j] = L[i][j];
+    TinvT[j * NBK + i] = Ti[i][j];
+  }
+}
+
+// sX[k][i] = src[(r0 + i) * ld + c0 + k]   (row-major source, k contiguous -> transposed)
+__device__ __forceinline__ void load_tile_T(double *sX, const double *__restrict__ src, int64_t ld, int64_t r0,
+                                            int64_t c0, int tid) {
+#pragma unroll 4
+  for (int e = 0; e < 16; ++e) {
+    const int idx = tid + e * 256;
+    const int i = idx >> 6, k = idx & 63;
+    sX[k * SP + i] = src[(r0 + i) * ld + c0 + k];
+  }
+}
+// sX[k][c] = src[(r0 + k) * ld + c0 + c]
+__device__ __forceinline__ void load_tile_N(double *sX, const double *__restrict__ src, int64_t ld, int64_t r0,
+                                            int64_t c0, int tid) {
+#pragma unroll 4
+  for (int e = 0; e < 16; ++e) {
+    const int idx = tid + e * 256;
+    const int k = idx >> 6, c = idx & 63;
+    sX[k * SP + c] = src[(r0 + k) * ld + c0 + c];
+  }
+}
+
+// acc (2x2 blocks of 16x16 per wave) = sA^T-layout x sB over K = 64.
+__device__ __forceinline__ void gemm64(const double *sA, const double *sB, f64x4_t acc[2][2], int lane, int wm,
+                                       int wn) {
+#pragma unroll 4
+  for (int ks = 0; ks < 16; ++ks) {
+    const int k = ks * 4 + (lane >> 4);
+    double a[2], b[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) a[i] = sA[k * SP + wm * 32 + i * 16 + (lane & 15)];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) b[j] = sB[k * SP + wn * 32 + j * 16 + (lane & 15)];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j) acc[i][j] = mfma_f64(a[i], b[j], acc[i][j]);
+  }
+}
+
+__device__ __forceinline__ void zero_acc(f64x4_t acc[2][2]) {
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) acc[i][j][v] = 0.0;
+}
+
+// Panel kernel.  Workgroups [0, nrow): row block ib = p+1+w: L_ib,p = A_ib,p Tinv^T.
+// Workgroups [nrow, nrow+p+1): column block cb: Z_p[:, cb] = Tinv R_p[:, cb], d[cb] += column norms^2.
+__global__ __launch_bounds__(256) void chol_panel_kernel(double *__restrict__ A, double *__restrict__ Z,
+                                                         const double *__restrict__ TinvT, double *__restrict__ d,
+                                                         int64_t mp, int p, int nrow) {
+  __shared__ double sA[NBK * SP];
+  __shared__ double sB[NBK * SP];
+  __shared__ double colsum[2][64];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int64_t k0 = (int64_t)p * NBK;
+  const int w = blockIdx.x;
+  f64x4_t acc[2][2];
+  zero_acc(acc);
+  if (w < nrow) {
+    const int64_t r0 = k0 + (int64_t)(w + 1) * NBK;
+    load_tile_T(sA, A, mp, r0, k0, tid);        // A operand (i, k) = A[r0+i][k0+k]
+    load_tile_N(sB, TinvT, NBK, 0, 0, tid);     // B operand (k, c) = Tinv[c][k]
+    __syncthreads();
+    gemm64(sA, sB, acc, lane, wm, wn);
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const int row = wm * 32 + i * 16 + 4 * v + (lane >> 4);
+          const int col = wn * 32 + j * 16 + (lane & 15);
+          A[(r0 + row) * mp + k0 + col] = acc[i][j][v];
+        }
+  } else {
+    const int64_t c0 = (int64_t)(w - nrow) * NBK;
+    load_tile_N(sA, TinvT, NBK, 0, 0, tid);     // A operand (i, k) = Tinv[i][k] = TinvT[k][i]
+    load_tile_N(sB, Z, mp, k0, c0, tid);        // B operand (k, c) = R[k0+k][c0+c]
+    __syncthreads();
+    gemm64(sA, sB, acc, lane, wm, wn);
+    double cs[2] = {0.0, 0.0};
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const int row = wm * 32 + i * 16 + 4 * v + (lane >> 4);
+          const int col = wn * 32 + j * 16 + (lane & 15);
+          const double z = acc[i][j][v];
+          Z[(k0 + row) * mp + c0 + col] = z;
+          cs[j] += z * z;
+        }
+    // lanes l, l^16, l^32, l^48 hold the same columns
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      cs[j] += __shfl_xor(cs[j], 16, 64);
+      cs[j] += __shfl_xor(cs[j], 32, 64);
+    }
+    if (lane < 16) {
+#pragma unroll
+      for (int j = 0; j < 2; ++j) colsum[wm][wn * 32 + j * 16 + lane] = cs[j];
+    }
+    __syncthreads();
+    if (tid < 64) d[c0 + tid] += colsum[0][tid] + colsum[1][tid];
+  }
+}
+
+// Trailing update.  Workgroups [0, nA): lower tile (ib >= jb > p): A_ij -= L_ip L_jp^T.
+// Workgroups [nA, nA + nZ): tile (ib > p, cb <= p): Z_ib,cb -= L_ip Z_p,cb.
+__global__ __launch_bounds__(256) void chol_update_kernel(double *__restrict__ A, double *__restrict__ Z,
+                                                          int64_t mp, int p, int nr, int64_t nA) {
+  __shared__ double sA[NBK * SP];
+  __shared__ double sB[NBK * SP];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int64_t k0 = (int64_t)p * NBK;
+  const int64_t w = blockIdx.x;
+  double *C;
+  int64_t r0, c0;
+  if (w < nA) {
+    const int id = (int)w;
+    int ii = (int)((sqrt(8.0 * id + 1.0) - 1.0) * 0.5);
+    while ((ii + 1) * (ii + 2) / 2 <= id) ++ii;
+    while (ii * (ii + 1) / 2 > id) --ii;
+    const int jj = id - ii * (ii + 1) / 2;
+    r0 = k0 + (int64_t)(ii + 1) * NBK;
+    c0 = k0 + (int64_t)(jj + 1) * NBK;
+    load_tile_T(sA, A, mp, r0, k0, tid);
+    load_tile_T(sB, A, mp, c0, k0, tid);
+    C = A;
+  } else {
+    const int64_t id = w - nA;
+    const int ib = (int)(id / (p + 1));
+    const int cb = (int)(id % (p + 1));
+    r0 = k0 + (int64_t)(ib + 1) * NBK;
+    c0 = (int64_t)cb * NBK;
+    load_tile_T(sA, A, mp, r0, k0, tid);
+    load_tile_N(sB, Z, mp, k0, c0, tid);
+    C = Z;
+  }
+  __syncthreads();
+  f64x4_t acc[2][2];
+  zero_acc(acc);
+  gemm64(sA, sB, acc, lane, wm, wn);
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int row = wm * 32 + i * 16 + 4 * v + (lane >> 4);
+        const int col = wn * 32 + j * 16 + (lane & 15);
+        double *dst = C + (r0 + row) * mp + c0 + col;
+        *dst = *dst - acc[i][j][v];
+      }
+  (void)nr;
+}
+
+__global__ __launch_bounds__(256) void sal_hinv_out_kernel(const double *__restrict__ d, int64_t m,
+                                                           float *__restrict__ hinv) {
+  const int64_t j = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (j < m) hinv[j] = (float)d[j];
+}
+
+// delta = fl(w*w)/fl(d*d) (float32); per (row block, group) float64 partial sums.
+template <bool BF16>
+__global__ __launch_bounds__(256) void sal_group_partial_kernel(const void *__restrict__ Wv, int64_t n, int64_t m,
+                                                                int g, const float *__restrict__ hinv,
+                                                                float *__restrict__ esal, double *__restrict__ part,
+                                                                int32_t *__restrict__ info) {
+  __shared__ double red[256];
+  const int j = blockIdx.x;       // group
+  const int rb = blockIdx.y;      // 64-row block
+  const int k = gridDim.x;
+  const int tid = threadIdx.x;
+  double s = 0.0;
+  bool bad = false;
+  const int64_t rows = min((int64_t)64, n - (int64_t)rb * 64);
+  for (int idx = tid; idx < rows * g; idx += 256) {
+    const int64_t i = (int64_t)rb * 64 + idx / g;
+    const int64_t col = (int64_t)j * g + idx % g;
+    float w;
+    if (BF16) w = bf16_bits_to_f32(((const uint16_t *)Wv)[i * m + col]);
+    else w = ((const float *)Wv)[i * m + col];
+    if (!isfinite(w)) bad = true;
+    const float dd = hinv[col];
+    const float dsq = dd * dd;
+    const float delta = (w * w) / dsq;
+    if (esal) esal[i * m + col] = delta;
+    s += (double)delta;
+  }
+  red[tid] = s;
+  __syncthreads();
+  for (int w2 = 128; w2 > 0; w2 >>= 1) {
+    if (tid < w2) red[tid] += red[tid + w2];
+    __syncthreads();
+  }
+  if (tid == 0) part[(int64_t)rb * k + j] = red[0];
+  if (bad) atomicExch(info, -1);
+}
+
+__global__ __launch_bounds__(256) void sal_group_final_kernel(const double *__restrict__ part, int nrb, int k,
+                                                              double denom, double *__restrict__ gsal) {
+  const int j = blockIdx.x * 256 + threadIdx.x;
+  if (j >= k) return;
+  double s = 0.0;
+  for (int rb = 0; rb < nrb; ++rb) s += part[(int64_t)rb * k + j];
+  gsal[j] = s / denom;
+}
+
+static int64_t pad64(int64_t m) { return (m + NBK - 1) / NBK * NBK; }
+
+size_t salience_ws_bytes(int64_t n, int64_t m, int group) {
+  const int64_t mp = pad64(m);
+  const int64_t nrb = (n + 63) / 64;
+  const int64_t k = m / group;
+  size_t off = 0;
+  off += align_up((size_t)mp * mp * 8, 256);   // A
+  off += align_up((size_t)mp * mp * 8, 256);   // Z
+  off += align_up((size_t)NBK * NBK * 8, 256);  // TinvT
+  off += align_up((size_t)mp * 8, 256);        // d
+  off += 256;                                   // alpha
+  off += align_up((size_t)nrb * k * 8, 256);   // group partials
+  return off;
+}
+
+hipError_t launch_salience(const float *H, int64_t m, double damp, const void *W, bool bf16, int64_t n, int group,
+                           float *hinv, double *gsal, float *esal, int32_t *info, void *ws, hipStream_t st) {
+  const int64_t mp = pad64(m);
+  const int64_t nrb = (n + 63) / 64;
+  const int k = (int)(m / group);
+  char *base = (char *)ws;
+  size_t off = 0;
+  double *A = (double *)(base + off);
+  off += align_up((size_t)mp * mp * 8, 256);
+  double *Z = (double *)(base + off);
+  off += align_up((size_t)mp * mp * 8, 256);
+  double *TinvT = (double *)(base + off);
+  off += align_up((size_t)NBK * NBK * 8, 256);
+  double *d = (double *)(base + off);
+  off += align_up((size_t)mp * 8, 256);
+  double *alpha = (double *)(base + off);
+  off += 256;
+  double *part = (double *)(base + off);
+
+  sal_alpha_kernel<<<1, 256, 0, st>>>(H, m, damp, alpha, info);
+  {
+    int64_t blocks = (mp * mp + 255) / 256;
+    if (blocks > 65536) blocks = 65536;
+    sal_init_kernel<<<(unsigned)blocks, 256, 0, st>>>(H, m, mp, alpha, A, Z, d, info);
+  }
+  const int NB = (int)(mp / NBK);
+  for (int p = 0; p < NB; ++p) {
+    chol_diag_kernel<<<1, 256, 0, st>>>(A, mp, p, TinvT, info);
+    const int nrow = NB - p - 1;
+    chol_panel_kernel<<<nrow + p + 1, 256, 0, st>>>(A, Z, TinvT, d, mp, p, nrow);
+    if (nrow > 0) {
+      const int64_t nA = (int64_t)nrow * (nrow + 1) / 2;
+      const int64_t nZ = (int64_t)nrow * (p + 1);
+      timer_begin(K_CHOL_UPDATE, st);
+      chol_update_kernel<<<(unsigned)(nA + nZ), 256, 0, st>>>(A, Z, mp, p, nrow, nA);
+      timer_end(K_CHOL_UPDATE, st);
+    }
+  }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  sal_hinv_out_kernel<<<(unsigned)((m + 255) / 256), 256, 0, st>>>(d, m, hinv);
+  dim3 grid(k, (unsigned)nrb);
+  if (bf16)
+    sal_group_partial_kernel<true><<<grid, 256, 0, st>>>(W, n, m, group, hinv, esal, part, info);
+  else
+    sal_group_partial_kernel<false><<<grid, 256, 0, st>>>(W, n, m, group, hinv, esal, part, info);
+  sal_group_final_kernel<<<(k + 255) / 256, 256, 0, st>>>(part, (int)nrb, k, (double)n * group, gsal);
+  return hipGetLastError();
+}
+
+}  // namespace slim

@@ -1,0 +1,537 @@
+// Salience-determined bit allocation (SBA) on gfx950.
+//
+// "SliM-LLM" blog digest (rkmt.cn), core design, component one: bit-widths
+// minimise the KL divergence of the layer output under the balance constraint
+// |G_{N-1}| = |G_{N+1}| (each group raised to N+1 is paired with a group
+// dropped to N-1), searched by two pointers over [0, k/2] (16 iterations for
+// LLaMA-7B); the scime.ai summary ("Approach") ranks groups by average
+// salience.  Every step r = 0..floor(k/2) is scored; step r raises the r most
+// salient groups and lowers the r least salient ones.
+//
+// Work per step.  Trial weights differ from step r-1 in exactly two column
+// groups (rank r-1 goes N -> N+1, rank k-r goes N -> N-1), so with
+// Yhat_r = X What_r^T:
+//     Yhat_r = Yhat_{r-1} + X_u (What^{N+1}_u)^T - X_u (What^N_u)^T
+//                         + X_d (What^{N-1}_d)^T - X_d (What^N_d)^T.
+// Operands stay exact (bf16 trial weights and their negations), and one
+// workgroup keeps its 128-output x 256-token tile of Yhat in MFMA
+// accumulators through the whole scan: Y and Yhat_0 over K = m, then 4g more
+// K columns per step.  Each wave owns 32 tokens x all 128 outputs of the
+// tile, so the softmax statistics of a token are reduced inside the wave
+// (16 values in-lane, then one lane swap) and never cross LDS.
+//
+// KL per token from chunk statistics.  With p = softmax(y), q = softmax(yhat):
+//     KL_t = sum_j p_j (y_j - yhat_j) - LSE(y) + LSE(yhat).
+// For each 128-output chunk c the kernel writes (M_c, Z_c) of y and, for every
+// step, (Mq_c, Zq_c, S_c = sum_j e^{y_j - M_c}(y_j - yhat_j)); a second kernel
+// merges chunks per token with the usual max/rescale rule, forms KL_t in
+// float64 and reduces over tokens in a fixed order.  A last single-workgroup
+// kernel takes the mean, the first argmin and the bit-widths, so nothing
+// returns to the host.
+//
+// XCD-aware launch: consecutive workgroup ids land on different XCDs, so the
+// id is remapped such that each XCD owns a fixed subset of output chunks and
+// walks the token tiles in order; the weight chunks of an XCD then stay in
+// its L2 while every token tile is fetched once per XCD.
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace slim {
+
+constexpr int SBO = 128;    // outputs per workgroup
+constexpr int SBT = 256;    // tokens per workgroup (8 waves x 32)
+constexpr int SBP = 144;    // LDS row pitch in bytes
+constexpr int MAXK = 2048;  // most groups per row supported by the search kernels
+constexpr int STAGE_BYTES = (2 * SBO + SBT) * SBP;
+
+// ---------------------------------------------------------------------------
+// Trial weights at tau = 1 for the three widths N-1, N, N+1: Wv[v][n][m].
+// LPS lanes per row segment, 8 weights per lane.
+template <bool BF16, int LPS>
+__global__ __launch_bounds__(256) void sba_trial_kernel(const void *__restrict__ W, int64_t n, int64_t m, int g,
+                                                        int N, void *__restrict__ Wv) {
+  const int64_t gl = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t seg = gl / LPS;
+  const int lis = (int)(gl % LPS);
+  const int64_t k = m / g;
+  const bool valid = seg < n * k;
+  const int64_t i = valid ? seg / k : 0, j = valid ? seg % k : 0;
+  const int64_t base = i * m + j * g + (int64_t)lis * 8;
+  float w[8];
+  if (BF16) {
+    uint4 v = make_uint4(0, 0, 0, 0);
+    if (valid) v = *(const uint4 *)((const uint16_t *)W + base);
+    const uint32_t u[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      w[2 * e] = __uint_as_float(u[e] << 16);
+      w[2 * e + 1] = __uint_as_float(u[e] & 0xffff0000u);
+    }
+  } else {
+    float4 a = make_float4(0, 0, 0, 0), b = make_float4(0, 0, 0, 0);
+    if (valid) {
+      a = *(const float4 *)((const float *)W + base);
+      b = *(const float4 *)((const float *)W + base + 4);
+    }
+    w[0] = a.x; w[1] = a.y; w[2] = a.z; w[3] = a.w;
+    w[4] = b.x; w[5] = b.y; w[6] = b.z; w[7] = b.w;
+  }
+  float lo = w[0], hi = w[0];
+#pragma unroll
+  for (int e = 1; e < 8; ++e) {
+    lo = fminf(lo, w[e]);
+    hi = fmaxf(hi, w[e]);
+  }
+  lo = group_min<LPS>(lo);
+  hi = group_max<LPS>(hi);
+  if (!valid) return;
+#pragma unroll
+  for (int v = 0; v < 3; ++v) {
+    const int b = N - 1 + v;
+    const float maxq = (float)((1 << b) - 1);
+    float s0 = (hi - lo) / maxq;
+    if (s0 == 0.0f) s0 = 1.0f;
+    const float z0 = (-lo) / s0;
+    const float r = 1.0f / s0;
+    float wh[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      float t = w[e] * r;
+      t = t + z0;
+      float q = rintf(t);
+      q = fminf(fmaxf(q, 0.0f), maxq);
+      const float dq = q - z0;
+      wh[e] = dq * s0;
+    }
+    if (BF16) {
+      uint32_t o[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) o[e] = f32_to_bf16_bits(wh[2 * e]) | (f32_to_bf16_bits(wh[2 * e + 1]) << 16);
+      *(uint4 *)((uint16_t *)Wv + (int64_t)v * n * m + base) = make_uint4(o[0], o[1], o[2], o[3]);
+    } else {
+      float *dst = (float *)Wv + (int64_t)v * n * m + base;
+      *(float4 *)dst = make_float4(wh[0], wh[1], wh[2], wh[3]);
+      *(float4 *)(dst + 4) = make_float4(wh[4], wh[5], wh[6], wh[7]);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// order[rank] = group, descending salience, ties by lower index (NaN ranks last).
+__global__ __launch_bounds__(256) void sba_rank_kernel(const double *__restrict__ S, int k, int *__restrict__ order) {
+  __shared__ double s[MAXK];
+  for (int j = threadIdx.x; j < k; j += 256) {
+    const double v = S[j];
+    s[j] = (v == v) ? v : -INFINITY;
+  }
+  __syncthreads();
+  for (int j = threadIdx.x; j < k; j += 256) {
+    const double sj = s[j];
+    int rank = 0;
+    for (int h = 0; h < k; ++h) {
+      const double sh = s[h];
+      rank += (sh > sj || (sh == sj && h < j)) ? 1 : 0;
+    }
+    order[rank] = j;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// PARTIAL = false: launched over the complete 128-output chunks with the
+// XCD-aware id.  PARTIAL = true: one launch over token tiles for the last,
+// incomplete chunk `c_last` (n % 128 != 0); only it checks output rows.
+template <bool BF16, bool PARTIAL>
+__global__ __launch_bounds__(512, 1) void sba_klgemm_kernel(
+    const void *__restrict__ X, const void *__restrict__ W, const void *__restrict__ Wv,
+    const int *__restrict__ order, int64_t tok_base, int64_t tb, int64_t n, int64_t m, int g, int k, int R,
+    int NC, int NCX, int TT, int c_last, float4 *__restrict__ sq, float2 *__restrict__ sp) {
+  constexpr int ESZ = BF16 ? 2 : 4;
+  constexpr int KT = BF16 ? 64 : 32;  // K elements per stage (128 bytes per row)
+  constexpr int EPP = 16 / ESZ;       // elements per 16-byte piece
+  __shared__ __attribute__((aligned(16))) unsigned char lds[2][STAGE_BYTES];
+  __shared__ int s_order[MAXK];
+  __shared__ int s_rows_ok;   // valid outputs in this chunk (read in the epilogue, never hoisted)
+
+  // XCD-aware id: XCD x = id % 8 owns complete output chunks [x*NCX, x*NCX+NCX).
+  int c, tt;
+  if (PARTIAL) {
+    c = c_last;
+    tt = blockIdx.x;
+  } else {
+    const int pid = blockIdx.x;
+    const int xcd = pid & 7, q = pid >> 3;
+    c = xcd * NCX + (q % NCX);
+    tt = q / NCX;
+    if (c >= c_last || tt >= TT) return;
+  }
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int64_t out0 = (int64_t)c * SBO;
+  const int64_t tok0 = (int64_t)tt * SBT;  // within the batch
+  for (int j = tid; j < k; j += 512) {
+    int o = order[j];
+    s_order[j] = (o >= 0 && o < k) ? o : 0;
+  }
+  if (tid == 0) s_rows_ok = (int)min((int64_t)SBO, n - out0);
+  __syncthreads();
+
+  const int KM = (int)((m + KT - 1) / KT);
+  const int SPR = 2 * g / KT;
+  const int total = KM + (R - 1) * SPR;
+  // Uniform 64-bit bases of this tile; per-thread 32-bit offsets.
+  const size_t rowb = (size_t)m * ESZ;  // bytes per row of W / X
+  const unsigned char *Wt = (const unsigned char *)W + out0 * rowb;
+  const unsigned char *Vt = (const unsigned char *)Wv + out0 * rowb;
+  const size_t vstride = (size_t)n * rowb;  // bytes between trial-weight variants
+  const unsigned char *Xt = (const unsigned char *)X + (tok_base + tok0) * rowb;
+  const int pc = tid & 7;          // 16-byte piece inside a 128-byte K slice (same for all pieces of a thread)
+  const int ra = tid >> 3;         // first row of this thread (0..63)
+  const uint32_t rstep = (uint32_t)(64 * rowb);  // 64 rows
+  const uint32_t roff = (uint32_t)(ra * rowb);
+  const int a_rows_ok = (int)min((int64_t)SBO, n - out0);   // valid weight rows in the tile
+  const int x_rows_ok = (int)min((int64_t)SBT, tb - tok0);  // valid token rows in the tile
+
+  uint4 rg[8];
+  // rg[0..1]: A0 rows ra, ra+64; rg[2..3]: A1 rows ra, ra+64; rg[4..7]: X rows ra + 64 j
+  auto load = [&](int st) {
+    int col;
+    const unsigned char *a0, *a1 = Vt + vstride;
+    if (st < KM) {
+      col = st * KT + pc * EPP;
+      a0 = Wt;
+    } else {
+      const int r = 1 + (st - KM) / SPR;
+      const int cc = ((st - KM) % SPR) * KT + pc * EPP;
+      const bool up = cc < g;
+      col = up ? s_order[r - 1] * g + cc : s_order[k - r] * g + (cc - g);
+      a0 = Vt + (up ? 2 * vstride : 0);
+    }
+    const bool cok = col < m;
+    const uint32_t coff = (uint32_t)col * ESZ;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const bool ok = cok && (ra + 64 * h) < a_rows_ok;
+      const uint32_t off = roff + h * rstep + coff;
+      rg[h] = ok ? *(const uint4 *)(a0 + off) : make_uint4(0, 0, 0, 0);
+      rg[2 + h] = ok ? *(const uint4 *)(a1 + off) : make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const bool ok = cok && (ra + 64 * j) < x_rows_ok;
+      rg[4 + j] = ok ? *(const uint4 *)(Xt + roff + j * rstep + coff) : make_uint4(0, 0, 0, 0);
+    }
+  };
+  auto store = [&](int buf) {
+    unsigned char *L = lds[buf] + ra * SBP + pc * 16;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      *(uint4 *)(L + (h * 64) * SBP) = rg[h];
+      *(uint4 *)(L + (SBO + h * 64) * SBP) = rg[2 + h];
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) *(uint4 *)(L + (2 * SBO + j * 64) * SBP) = rg[4 + j];
+  };
+
+  f32x16_t accY[4], accQ[4];
+#pragma unroll
+  for (int b = 0; b < 4; ++b)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      accY[b][v] = 0.0f;
+      accQ[b][v] = 0.0f;
+    }
+
+  auto compute = [&](int buf, bool main_stage) {
+    const unsigned char *L = lds[buf];
+    const unsigned char *Bt = L + (2 * SBO + wave * 32 + (lane & 31)) * SBP;
+    if (BF16) {
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) {
+        const int off = kk * 32 + (lane >> 5) * 16;
+        const uint4 b = *(const uint4 *)(Bt + off);
+#pragma unroll
+        for (int blk = 0; blk < 4; ++blk) {
+          const uint4 a0 = *(const uint4 *)(L + (blk * 32 + (lane & 31)) * SBP + off);
+          uint4 a1 = *(const uint4 *)(L + (SBO + blk * 32 + (lane & 31)) * SBP + off);
+          if (main_stage) {
+            accY[blk] = mfma_bf16(a0, b, accY[blk]);
+            accQ[blk] = mfma_bf16(a1, b, accQ[blk]);
+          } else {
+            a1.x ^= 0x80008000u; a1.y ^= 0x80008000u; a1.z ^= 0x80008000u; a1.w ^= 0x80008000u;
+            accQ[blk] = mfma_bf16(a0, b, accQ[blk]);
+            accQ[blk] = mfma_bf16(a1, b, accQ[blk]);
+          }
+        }
+      }
+    } else {
+#pragma unroll 4
+      for (int kk = 0; kk < 16; ++kk) {
+        const int off = kk * 8 + (lane >> 5) * 4;
+        const float b = *(const float *)(Bt + off);
+#pragma unroll
+        for (int blk = 0; blk < 4; ++blk) {
+          const float a0 = *(const float *)(L + (blk * 32 + (lane & 31)) * SBP + off);
+          const float a1 = *(const float *)(L + (SBO + blk * 32 + (lane & 31)) * SBP + off);
+          if (main_stage) {
+            accY[blk] = mfma_f32(a0, b, accY[blk]);
+            accQ[blk] = mfma_f32(a1, b, accQ[blk]);
+          } else {
+            accQ[blk] = mfma_f32(a0, b, accQ[blk]);
+            accQ[blk] = mfma_f32(-a1, b, accQ[blk]);
+          }
+        }
+      }
+    }
+  };
+
+  // Per-wave token statistics; lane l and l^32 hold the same token (l % 32).
+  const int64_t tcol = tok0 + wave * 32 + (lane & 31);
+  const bool tvalid = tcol < tb;
+  float sy_tok = 0.0f;
+  auto epilogue = [&](int r) {
+    // Output row of accumulator element (blk, v) is blk*32 + acc32_row(v, lane).
+    const int lim = PARTIAL ? s_rows_ok - 4 * (lane >> 5) : SBO;
+    if (r == 0) {
+      float mx = -INFINITY;
+#pragma unroll
+      for (int blk = 0; blk < 4; ++blk)
+#pragma unroll
+        for (int v = 0; v < 16; ++v)
+          if (!PARTIAL || blk * 32 + 8 * (v >> 2) + (v & 3) < lim) mx = fmaxf(mx, accY[blk][v]);
+      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+      float z = 0.0f, sy = 0.0f;
+#pragma unroll
+      for (int blk = 0; blk < 4; ++blk)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const float y = accY[blk][v];
+          float e = 0.0f;
+          if (!PARTIAL || blk * 32 + 8 * (v >> 2) + (v & 3) < lim) e = __expf(y - mx);
+          accY[blk][v] = e;
+          z += e;
+          sy += e * y;
+        }
+      z += __shfl_xor(z, 32, 64);
+      sy += __shfl_xor(sy, 32, 64);
+      sy_tok = sy;
+      if (lane < 32 && tvalid) sp[(int64_t)c * tb + tcol] = make_float2(mx, z);
+    }
+    float mq = -INFINITY;
+#pragma unroll
+    for (int blk = 0; blk < 4; ++blk)
+#pragma unroll
+      for (int v = 0; v < 16; ++v)
+        if (!PARTIAL || blk * 32 + 8 * (v >> 2) + (v & 3) < lim) mq = fmaxf(mq, accQ[blk][v]);
+    mq = fmaxf(mq, __shfl_xor(mq, 32, 64));
+    float zq = 0.0f, se = 0.0f;
+#pragma unroll
+    for (int blk = 0; blk < 4; ++blk)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const float yh = accQ[blk][v];
+        if (!PARTIAL || blk * 32 + 8 * (v >> 2) + (v & 3) < lim) zq += __expf(yh - mq);
+        se += accY[blk][v] * yh;
+      }
+    zq += __shfl_xor(zq, 32, 64);
+    se += __shfl_xor(se, 32, 64);
+    if (lane < 32 && tvalid) sq[((int64_t)r * NC + c) * tb + tcol] = make_float4(mq, zq, sy_tok - se, 0.0f);
+  };
+
+  load(0);
+  store(0);
+  __syncthreads();
+  for (int st = 0; st < total; ++st) {
+    const bool more = st + 1 < total;
+    if (more) load(st + 1);
+    const bool main_stage = st < KM;
+    compute(st & 1, main_stage);
+    if (st == KM - 1) epilogue(0);
+    else if (!main_stage && (st - KM) % SPR == SPR - 1) epilogue(1 + (st - KM) / SPR);
+    if (more) store((st + 1) & 1);
+    __syncthreads();
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Merge chunk statistics per token, KL_t in float64, per-block sums per step.
+__global__ __launch_bounds__(256) void sba_combine_kernel(const float2 *__restrict__ sp, const float4 *__restrict__ sq,
+                                                          int64_t tb, int NC, int R, double *__restrict__ part,
+                                                          int64_t blk_off) {
+  __shared__ double red[4][1032];
+  const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const bool valid = t < tb;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  float M = -INFINITY;
+  double Z = 0.0;
+  if (valid) {
+    for (int c = 0; c < NC; ++c) {
+      const float2 v = sp[(int64_t)c * tb + t];
+      if (v.x > M) {
+        Z = Z * (double)expf(M - v.x) + (double)v.y;
+        M = v.x;
+      } else {
+        Z += (double)v.y * (double)expf(v.x - M);
+      }
+    }
+  }
+  const double lse_p = (double)M + log(Z);
+  for (int r = 0; r < R; ++r) {
+    double kl = 0.0;
+    if (valid) {
+      float Mq = -INFINITY;
+      double Zq = 0.0, S = 0.0;
+      for (int c = 0; c < NC; ++c) {
+        const float4 v = sq[((int64_t)r * NC + c) * tb + t];
+        const float mc = sp[(int64_t)c * tb + t].x;
+        S += (double)v.z * (double)expf(mc - M);
+        if (v.x > Mq) {
+          Zq = Zq * (double)expf(Mq - v.x) + (double)v.y;
+          Mq = v.x;
+        } else {
+          Zq += (double)v.y * (double)expf(v.x - Mq);
+        }
+      }
+      kl = S / Z - lse_p + ((double)Mq + log(Zq));
+    }
+#pragma unroll
+    for (int d = 32; d > 0; d >>= 1) kl += __shfl_xor(kl, d, 64);
+    if (lane == 0) red[wave][r] = kl;
+  }
+  __syncthreads();
+  for (int r = threadIdx.x; r < R; r += 256)
+    part[(blk_off + blockIdx.x) * R + r] = ((red[0][r] + red[1][r]) + red[2][r]) + red[3][r];
+}
+
+// Mean over tokens, first argmin, bit-widths at r*.
+__global__ __launch_bounds__(256) void sba_finalize_kernel(const double *__restrict__ part, int64_t nblk, int R,
+                                                           int64_t T, const int *__restrict__ order, int k, int N,
+                                                           double *__restrict__ kl, int32_t *__restrict__ r_star,
+                                                           int8_t *__restrict__ bits) {
+  __shared__ double skl[1032];
+  __shared__ int srs;
+  for (int r = threadIdx.x; r < R; r += 256) {
+    double s = 0.0;
+    for (int64_t b = 0; b < nblk; ++b) s += part[b * R + r];
+    s = s / (double)T;
+    skl[r] = s;
+    kl[r] = s;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    int best = 0;
+    for (int r = 1; r < R; ++r)
+      if (skl[r] < skl[best]) best = r;
+    srs = best;
+    r_star[0] = best;
+  }
+  __syncthreads();
+  const int rs = srs;
+  for (int i = threadIdx.x; i < k; i += 256) {
+    const int gidx = order[i];
+    if (gidx < 0 || gidx >= k) continue;
+    int b = N;
+    if (i < rs) b = N + 1;
+    else if (i >= k - rs) b = N - 1;
+    bits[gidx] = (int8_t)b;
+  }
+}
+
+// ---------------------------------------------------------------------------
+SbaPlan sba_plan(int64_t t, int64_t n, int64_t m, int group, bool bf16) {
+  SbaPlan p;
+  const int esz = bf16 ? 2 : 4;
+  p.k = (int)(m / group);
+  p.R = p.k / 2 + 1;
+  p.nchunk = (int)((n + SBO - 1) / SBO);
+  const size_t per_tok = (size_t)p.nchunk * (8 + 16 * (size_t)p.R);
+  const size_t budget = (size_t)1 << 30;  // chunk statistics per batch
+  int64_t tb = (int64_t)(budget / per_tok) / SBT * SBT;
+  if (tb < SBT) tb = SBT;
+  if (tb > t) tb = t;
+  p.tb = tb;
+  p.nbatch = (int)((t + tb - 1) / tb);
+  p.combine_blocks = 0;
+  for (int b = 0; b < p.nbatch; ++b) {
+    const int64_t len = (b == p.nbatch - 1) ? t - (int64_t)b * tb : tb;
+    p.combine_blocks += (len + 255) / 256;
+  }
+  size_t off = 0;
+  p.off_wv = off;
+  off += align_up((size_t)3 * n * m * esz, 256);
+  p.off_order = off;
+  off += align_up((size_t)p.k * 4, 256);
+  p.off_sp = off;
+  off += align_up((size_t)p.nchunk * tb * 8, 256);
+  p.off_sq = off;
+  off += align_up((size_t)p.R * p.nchunk * tb * 16, 256);
+  p.off_part = off;
+  off += align_up((size_t)p.combine_blocks * p.R * 8, 256);
+  p.ws_bytes = off;
+  return p;
+}
+
+hipError_t launch_sba(const void *X, const void *W, bool bf16, int64_t t, int64_t n, int64_t m, int group,
+                      const double *gsal, int avg_bits, int8_t *bits, double *kl, int32_t *r_star, void *ws,
+                      const SbaPlan &p, hipStream_t st) {
+  char *base = (char *)ws;
+  void *Wv = base + p.off_wv;
+  int *order = (int *)(base + p.off_order);
+  float2 *sp = (float2 *)(base + p.off_sp);
+  float4 *sq = (float4 *)(base + p.off_sq);
+  double *part = (double *)(base + p.off_part);
+
+  // trial weights
+  {
+    const int lps = group / 8;
+    const int64_t lanes = n * (m / group) * lps;
+    const unsigned blocks = (unsigned)((lanes + 255) / 256);
+#define SLIM_TRIAL(L)                                                                                   \
+  if (bf16) sba_trial_kernel<true, L><<<blocks, 256, 0, st>>>(W, n, m, group, avg_bits, Wv);          \
+  else sba_trial_kernel<false, L><<<blocks, 256, 0, st>>>(W, n, m, group, avg_bits, Wv);
+    if (lps == 16) { SLIM_TRIAL(16) }
+    else if (lps == 8) { SLIM_TRIAL(8) }
+    else { SLIM_TRIAL(4) }
+#undef SLIM_TRIAL
+  }
+  sba_rank_kernel<<<1, 256, 0, st>>>(gsal, p.k, order);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+
+  const int NC = p.nchunk;
+  const int NCF = (int)(n / SBO);          // complete chunks
+  const int NCX = (NCF + 7) / 8;
+  int64_t blk_off = 0;
+  for (int b = 0; b < p.nbatch; ++b) {
+    const int64_t t0 = (int64_t)b * p.tb;
+    const int64_t len = (b == p.nbatch - 1) ? t - t0 : p.tb;
+    const int TT = (int)((len + SBT - 1) / SBT);
+    timer_begin(K_SBA_KLGEMM, st);
+    if (NCF > 0) {
+      const unsigned grid = (unsigned)(8 * NCX * TT);
+      if (bf16)
+        sba_klgemm_kernel<true, false><<<grid, 512, 0, st>>>(X, W, Wv, order, t0, len, n, m, group, p.k, p.R, NC, NCX,
+                                                             TT, NCF, sq, sp);
+      else
+        sba_klgemm_kernel<false, false><<<grid, 512, 0, st>>>(X, W, Wv, order, t0, len, n, m, group, p.k, p.R, NC,
+                                                              NCX, TT, NCF, sq, sp);
+    }
+    if (NC > NCF) {
+      if (bf16)
+        sba_klgemm_kernel<true, true><<<TT, 512, 0, st>>>(X, W, Wv, order, t0, len, n, m, group, p.k, p.R, NC, NCX, TT,
+                                                          NCF, sq, sp);
+      else
+        sba_klgemm_kernel<false, true><<<TT, 512, 0, st>>>(X, W, Wv, order, t0, len, n, m, group, p.k, p.R, NC, NCX,
+                                                           TT, NCF, sq, sp);
+    }
+    timer_end(K_SBA_KLGEMM, st);
+    const unsigned cb = (unsigned)((len + 255) / 256);
+    sba_combine_kernel<<<cb, 256, 0, st>>>(sp, sq, len, NC, p.R, part, blk_off);
+    blk_off += cb;
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  sba_finalize_kernel<<<1, 256, 0, st>>>(part, blk_off, p.R, t, order, p.k, avg_bits, kl, r_star, bits);
+  return hipGetLastError();
+}
+
+}  // namespace slim

@@ -1,0 +1,24 @@
+"""One linear layer through the whole path, enqueued on the current stream.
+
+Stage order as in the SliM-LLM blog digest (rkmt.cn), core design: Hessian
+from calibration activations, salience, SBA bit allocation, SQC calibration,
+then group-structured storage.  Nothing is copied back to the host between
+stages; the caller synchronises once and may inspect ``info``.
+"""
+from __future__ import annotations
+
+from . import _lib
+
+
+def quantize_layer(X, W, group: int = 128, avg_bits: int = 2, lam: float = 0.1, n_tau: int = 50,
+                   damp_frac: float = 0.01, H=None):
+    """X [T, m], W [n, m] (bf16 or f32, GPU).  If H is given the Hessian stage is
+    skipped (a Hessian shared by several linears of one input width)."""
+    if H is None:
+        H = _lib.hessian(X)
+    hinv, gsal, info, _ = _lib.salience(H, W, group, damp_frac)
+    bits, kl, r_star = _lib.sba_search(X, W, gsal, group, avg_bits)
+    sq = _lib.sqc_calibrate(W, bits, hinv, group, lam, n_tau)
+    packed, pinfo = _lib.pack(sq["codes"], bits, group, avg_bits)
+    return {"H": H, "hinv": hinv, "group_sal": gsal, "info": info, "bits": bits, "kl": kl, "r_star": r_star,
+            "pack_info": pinfo, "packed": packed, **sq}
