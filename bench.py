@@ -1,0 +1,221 @@
+"""Throughput of the SliM-LLM per-layer quantizer path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--linear I]
+
+A step is one pass of the whole path over one linear layer whose inputs are
+already resident in HBM: Hessian 2X^TX, damped inverse-diagonal salience and
+group means, the SBA scan scored by output KL, SQC calibration and bit-plane
+packing.  The default workload is the LLaMA-7B-shaped attention projection:
+W 4096 x 4096 bf16 ~ N(0, 0.02^2), X 262144 calibration tokens (128 sequences
+of 2048) x 4096 bf16 with 1% clustered outlier channels, group 128, 2-bit
+average over {1, 2, 3}; synthetic, seeded (synth/).  value = n*m / 1e6 /
+seconds per step (Mparams quantized per second).
+
+The JSON line also carries the roofline of the dominant kernel (the fused
+SBA GEMM + KL kernel, timed live with HIP events on its own launch stream)
+and the CPU oracle timed on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_FLOPS = 2.5e15   # MI355X dense bf16 MFMA
+PEAK_HBM_BPS = 8.0e12      # MI355X HBM3E
+
+
+def _dev(a, torch):
+    if a.dtype == np.uint16:
+        return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to("cuda:0")
+    return torch.from_numpy(a).to("cuda:0")
+
+
+def run_step(slim, X, W, group, N, ev=None):
+    """One pass of the whole path; optional event list records stage boundaries."""
+    def mark(i):
+        if ev is not None:
+            ev[i].record()
+    mark(0)
+    H = slim.hessian(X)
+    mark(1)
+    hinv, gsal, info, _ = slim.salience(H, W, group, 0.01)
+    mark(2)
+    bits, kl, rs = slim.sba_search(X, W, gsal, group, N)
+    mark(3)
+    sq = slim.sqc_calibrate(W, bits, hinv, group, 0.1, 50, want_tau=False)
+    mark(4)
+    packed, pinfo = slim.pack(sq["codes"], bits, group, N)
+    mark(5)
+    return info, pinfo, rs, kl
+
+
+def cpu_baseline(wl, lin_idx, group, N, Xh, Wh, budget_s=20.0):
+    """The oracle as it stands, on a bounded sample; stage costs scaled to the layer."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:  # pragma: no cover
+        threads = len(os.sched_getaffinity(0))
+    lin = wl.linears[lin_idx]
+    n, m, T = lin.n, lin.m, wl.tokens
+    storage = wl.dtype
+    t_h = 2048
+    t0 = time.perf_counter()
+    oracle.hessian(Xh[:t_h])
+    s_hess = (time.perf_counter() - t0) * T / t_h
+    # salience needs a full-width H; the sample's H stands in (same cost)
+    t0 = time.perf_counter()
+    H = oracle.hessian(Xh[:t_h])
+    t_hsmp = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    d32, S, info = oracle.salience(H, Wh, group, 0.01)
+    s_sal = time.perf_counter() - t0
+    # SBA: per-token cost of the scan on a token slice
+    t_s = 384
+    t0 = time.perf_counter()
+    bits, kl, rs = oracle.sba_search(Xh[:t_s], Wh, S, N, group, storage)
+    s_sba_slice = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    oracle.trial_weights(Wh, bits, group, storage)
+    s_trial = time.perf_counter() - t0
+    k = m // group
+    per_tok = max(s_sba_slice - 3 * s_trial, 1e-9) / t_s
+    s_sba = per_tok * T + 3 * s_trial
+    # SQC on a row sample
+    rows = min(n, 128)
+    t0 = time.perf_counter()
+    sq = oracle.sqc_calibrate(Wh, bits, d32, group, 0.1, 50, rows=np.arange(rows))
+    s_sqc = (time.perf_counter() - t0) * n / rows
+    codes = np.zeros((n, m), dtype=np.uint8)
+    codes[:rows] = sq["codes"]
+    t0 = time.perf_counter()
+    oracle.pack_bitplanes(codes, bits, group)
+    s_pack = time.perf_counter() - t0
+    total = s_hess + s_sal + s_sba + s_sqc + s_pack
+    return {
+        "value": n * m / 1e6 / total, "unit": "Mparams/s", "cores": int(threads), "kind": "oracle",
+        "sample": (f"Hessian on {t_h} tokens (x{T // t_h}); salience at full width {m}; SBA scan over all "
+                   f"{k // 2 + 1} steps on {t_s} tokens (per-token cost x{T}) plus 3 trial quantizations; "
+                   f"SQC on {rows} of {n} rows (x{n / rows:.0f}); packing in full"),
+        "seconds_extrapolated": {"hessian": s_hess, "salience": s_sal, "sba": s_sba, "sqc": s_sqc,
+                                 "pack": s_pack, "total": total},
+        "seconds_measured": round(s_hess * t_h / T + t_hsmp + s_sal + s_sba_slice + s_trial
+                                  + s_sqc * rows / n + s_pack, 2),
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--workload", default="llama7b-attn-4096")
+    ap.add_argument("--linear", type=int, default=0)
+    ap.add_argument("--group", type=int, default=None)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: this path runs one layer per GPU and the build targets "
+              "single-GPU boxes; run with --gpus 1 (sharding is described in DESIGN.md).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import synth
+    import post_mixed_precision_amd as slim
+    if not os.path.exists(os.path.join(ROOT, "post_mixed_precision_amd", "libslim.so")):
+        from post_mixed_precision_amd import build as _b
+        _b.build()
+    slim.load_library()
+
+    wl = synth.WORKLOADS[args.workload]
+    lin = wl.linears[args.linear]
+    group = args.group or wl.groups[0]
+    N = wl.avg_bits
+    n, m, T = lin.n, lin.m, wl.tokens
+    print(f"# generating {args.workload}/{lin.name}: W {n}x{m}, X {T}x{m} {wl.dtype}", file=sys.stderr, flush=True)
+    Xh = synth.make_x(wl, m)
+    Wh = synth.make_w(wl, args.linear)
+    X, W = _dev(Xh, torch), _dev(Wh, torch)
+    torch.cuda.synchronize()
+
+    for i in range(args.warmup):
+        info, pinfo, rs, kl = run_step(slim, X, W, group, N)
+        torch.cuda.synchronize()
+        print(f"# warmup {i}: info={int(info.item())} r*={int(rs.item())}", file=sys.stderr, flush=True)
+    assert int(info.item()) == 0 and int(pinfo.item()) == 0
+
+    # timed region: K whole steps, synchronised on both sides
+    slim.timing_enable(True)
+    slim.timing_reset()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        run_step(slim, X, W, group, N, evs[s])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    slim.timing_enable(False)
+    sec = wall / args.steps
+    names = ["hessian", "salience", "sba", "sqc", "pack"]
+    stages = {nm: float(np.median([evs[s][i].elapsed_time(evs[s][i + 1]) for s in range(args.steps)]))
+              for i, nm in enumerate(names)}
+    kms, klaunch = slim.timing_read("sba_klgemm")
+    ms_per_launch = kms / max(klaunch, 1)
+    launches_per_step = klaunch / args.steps
+    # algorithmic work of the scan: 6*T*m*n flops per layer (Y, Yhat_0 and every
+    # group's one change of width), split evenly over the launches of a step
+    flops_per_launch = 6.0 * T * m * n / launches_per_step
+    achieved = flops_per_launch / (ms_per_launch * 1e-3)
+    hms, hl = slim.timing_read("hessian_gram")
+    qms, ql = slim.timing_read("sqc_calibrate")
+    pms, pl = slim.timing_read("pack_planes")
+    cms, cl = slim.timing_read("chol_update")
+    print(f"# sba_klgemm {ms_per_launch:.3f} ms/launch ({launches_per_step:.0f}/step); "
+          f"stages ms {json.dumps({k: round(v, 3) for k, v in stages.items()})}", file=sys.stderr, flush=True)
+
+    value = n * m / 1e6 / sec
+    out = {
+        "metric": "Mparams quantized/s per linear layer; % of MFMA and HBM roofline",
+        "value": round(value, 3), "unit": "Mparams/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(sec * 1e3, 3), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16" if wl.dtype == "bf16" else "f32",
+        "data": "synthetic (seeded; stands in for 128x2048 WikiText2 tokens and LLaMA weights)",
+        "config": {"workload": args.workload, "linear": lin.name, "n": n, "m": m, "tokens": T,
+                   "group": group, "avg_bits": N, "tau_lambda": wl.tau_lambda, "tau_steps": wl.tau_steps},
+        "roofline": {"bound": "mfma", "kernel": "sba_klgemm", "achieved": round(achieved / 1e12, 2),
+                     "peak": PEAK_BF16_FLOPS / 1e12, "unit": "TFLOP/s",
+                     "frac": round(achieved / PEAK_BF16_FLOPS, 4), "traffic": None,
+                     "ms_per_launch": round(ms_per_launch, 3), "algorithmic_flops_per_launch": flops_per_launch},
+        "stages_ms": {k: round(v, 3) for k, v in stages.items()},
+        "kernels_ms_per_step": {"sba_klgemm": round(kms / args.steps, 3),
+                                "hessian_gram": round(hms / args.steps, 3),
+                                "chol_update": round(cms / args.steps, 3),
+                                "sqc_calibrate": round(qms / args.steps, 3),
+                                "pack_planes": round(pms / args.steps, 3)},
+    }
+    hess_flops = T * m * (m + 1)
+    if hl:
+        out["roofline_other"] = {
+            "hessian_gram": {"bound": "mfma", "achieved_tflops": round(hess_flops / (hms / hl * 1e-3) / 1e12, 2),
+                             "frac": round(hess_flops / (hms / hl * 1e-3) / PEAK_BF16_FLOPS, 4)},
+            "sqc_calibrate": {"bound": "alu", "hbm_gbps": round(n * m * (2 + 1 + 0.125) / (qms / ql * 1e-3) / 1e9, 1)},
+            "pack_planes": {"bound": "hbm", "achieved_gbps": round(n * m * (1 + N / 8) / (pms / pl * 1e-3) / 1e9, 1),
+                            "frac": round(n * m * (1 + N / 8) / (pms / pl * 1e-3) / PEAK_HBM_BPS, 4)},
+        }
+    if not args.no_cpu_baseline:
+        print("# timing the CPU oracle on a bounded sample", file=sys.stderr, flush=True)
+        out["cpu_baseline"] = cpu_baseline(wl, args.linear, group, N, Xh, Wh)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -129,7 +129,9 @@ int slim_salience(const float *H, int64_t m, double damp_frac, const void *W, in
  *
  * X: [t, m] (dtype xdt), W: [n, m] (dtype wdt == xdt); group_sal float64 [k];
  * bits int8 [k]; kl float64 [floor(k/2)+1]; r_star int32 [1].
- * Requires t >= 1, n >= 1, m % group == 0.
+ * Requires t >= 1, n >= 1, m % group == 0, k <= SLIM_MAX_GROUPS and
+ * 3 * n * m * sizeof(element) < 2^31 (the trial weights are addressed with
+ * 32-bit offsets; 28672 x 8192 bf16 uses 1.4 GB).
  * ---------------------------------------------------------------------- */
 size_t slim_sba_workspace(int64_t t, int64_t n, int64_t m, int group, int dtype);
 int slim_sba_search(const void *X, int xdt, int64_t t, const void *W, int wdt, int64_t n, int64_t m,

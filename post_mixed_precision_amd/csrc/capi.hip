@@ -159,6 +159,8 @@ int slim_sba_search(const void *X, int xdt, int64_t t, const void *W, int wdt, i
   if (t < 1 || n < 1 || m < 1 || m > SLIM_MAX_WIDTH) return SLIM_E_SHAPE;
   if (!valid_group(group) || m % group || m / group > SLIM_MAX_GROUPS) return SLIM_E_SHAPE;
   if (avg_bits < 2 || avg_bits > 7) return SLIM_E_PARAM;
+  // the three trial-weight variants are addressed with 32-bit buffer offsets
+  if ((double)n * (double)m * (xdt == SLIM_BF16 ? 2.0 : 4.0) * 3.0 > 2147483647.0) return SLIM_E_SHAPE;
   if (!aligned16(X) || !aligned16(W)) return SLIM_E_ALIGN;
   const slim::SbaPlan p = slim::sba_plan(t, n, m, group, xdt == SLIM_BF16);
   if (!ws || ws_bytes < p.ws_bytes) return SLIM_E_WORKSPACE;

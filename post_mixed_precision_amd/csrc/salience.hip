@@ -69,52 +69,52 @@ __global__ __launch_bounds__(256) void sal_init_kernel(const float *__restrict__
 
 // Factor the diagonal block of panel p and invert it; writes L_pp into A and
 // (L_pp^-1)^T into TinvT (64 x 64, row k holds column k of the inverse).
+//
+// One sweep of 64 steps with one barrier each.  Step j eliminates column j
+// from the unscaled block (A <- A - a_j a_j^T / a_jj on the trailing part)
+// and applies the same row operation to a right-hand side R that starts as
+// the identity (R_i <- R_i - (a_ij / a_jj) R_j), so that afterwards
+// L_ij = a_ij / sqrt(a_jj) and (L^-1)_jc = R_jc / sqrt(a_jj).  Step j reads
+// only column j of A and row j of R, which step j does not write.
 __global__ __launch_bounds__(256) void chol_diag_kernel(double *__restrict__ A, int64_t mp, int p,
                                                         double *__restrict__ TinvT, int32_t *__restrict__ info) {
   __shared__ double L[NBK][SP];
-  __shared__ double Ti[NBK][SP];
+  __shared__ double Rm[NBK][SP];
+  __shared__ double piv[NBK];
   const int tid = threadIdx.x;
   const int64_t k0 = (int64_t)p * NBK;
   for (int idx = tid; idx < NBK * NBK; idx += 256) {
     const int i = idx / NBK, j = idx % NBK;
     L[i][j] = (j <= i) ? A[(k0 + i) * mp + k0 + j] : 0.0;
-    Ti[i][j] = 0.0;
+    Rm[i][j] = (i == j) ? 1.0 : 0.0;
   }
   __syncthreads();
+  // Thread t owns row i = t / 4 of both arrays, columns (t % 4) + 4 q.
+  const int oi = tid >> 2, oc = tid & 3;
   for (int j = 0; j < NBK; ++j) {
-    if (tid == 0) {
-      double v = L[j][j];
-      if (!(v > 0.0) || !isfinite(v)) {
-        atomicCAS(info, 0, (int)(k0 + j + 1));
-        v = 1.0;  // keep going with a harmless pivot; outputs are unspecified
+    double a = L[j][j];
+    if (!(a > 0.0) || !isfinite(a)) a = 1.0;  // reported below; a harmless pivot keeps the sweep finite
+    if (oi > j) {
+      const double f = L[oi][j] / a;
+#pragma unroll
+      for (int q = 0; q < 16; ++q) {
+        const int c = oc + 4 * q;
+        if (c > j && c <= oi) L[oi][c] = L[oi][c] - f * L[c][j];
+        if (c <= j) Rm[oi][c] = Rm[oi][c] - f * Rm[j][c];
       }
-      L[j][j] = sqrt(v);
     }
-    __syncthreads();
-    const double djj = L[j][j];
-    for (int i = j + 1 + tid; i < NBK; i += 256) L[i][j] = L[i][j] / djj;
-    __syncthreads();
-    const int r = NBK - 1 - j;
-    for (int idx = tid; idx < r * r; idx += 256) {
-      const int i = j + 1 + idx / r, l = j + 1 + idx % r;
-      if (l <= i) L[i][l] = L[i][l] - L[i][j] * L[l][j];
-    }
-    __syncthreads();
-  }
-  // Inverse of the lower-triangular block, one row at a time, columns in parallel.
-  for (int i = 0; i < NBK; ++i) {
-    if (tid <= i) {
-      const int c = tid;
-      double s = (c == i) ? 1.0 : 0.0;
-      for (int l = c; l < i; ++l) s = s - L[i][l] * Ti[l][c];
-      Ti[i][c] = s / L[i][i];
+    if (tid == 0) {
+      piv[j] = a;
+      if (!(L[j][j] > 0.0 && isfinite(L[j][j]))) atomicCAS(info, 0, (int)(k0 + j + 1));
     }
     __syncthreads();
   }
   for (int idx = tid; idx < NBK * NBK; idx += 256) {
     const int i = idx / NBK, j = idx % NBK;
-    if (j <= i) A[(k0 + i) * mp + k0 + j] = L[i][j];
-    TinvT[j * NBK + i] = Ti[i][j];
+    const double sj = sqrt(piv[j]);
+    if (j <= i) A[(k0 + i) * mp + k0 + j] = L[i][j] / sj;     // L_ij = a_ij / sqrt(a_jj)
+    const double si = sqrt(piv[i]);
+    TinvT[j * NBK + i] = (j <= i) ? Rm[i][j] / si : 0.0;     // (L^-1)_ij = R_ij / sqrt(a_ii)
   }
 }
 

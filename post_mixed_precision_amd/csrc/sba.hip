@@ -40,9 +40,13 @@ namespace slim {
 
 constexpr int SBO = 128;    // outputs per workgroup
 constexpr int SBT = 256;    // tokens per workgroup (8 waves x 32)
-constexpr int SBP = 144;    // LDS row pitch in bytes
+constexpr int SBP = 128;    // LDS row pitch in bytes (16-byte slots XOR-swizzled by row & 7)
 constexpr int MAXK = 2048;  // most groups per row supported by the search kernels
 constexpr int STAGE_BYTES = (2 * SBO + SBT) * SBP;
+constexpr uint32_t RSRC_FLAGS = 0x00020000u;   // raw buffer, 32-bit dwords (gfx9 buffer resource word 3)
+constexpr uint32_t OOB = 0x7ffffff0u;          // offset beyond every range: the load returns zeros
+
+typedef __attribute__((address_space(3))) void lds_void_t;
 
 // ---------------------------------------------------------------------------
 // Trial weights at tau = 1 for the three widths N-1, N, N+1: Wv[v][n][m].
@@ -178,58 +182,56 @@ __global__ __launch_bounds__(512, 1) void sba_klgemm_kernel(
   const int KM = (int)((m + KT - 1) / KT);
   const int SPR = 2 * g / KT;
   const int total = KM + (R - 1) * SPR;
-  // Uniform 64-bit bases of this tile; per-thread 32-bit offsets.
-  const size_t rowb = (size_t)m * ESZ;  // bytes per row of W / X
-  const unsigned char *Wt = (const unsigned char *)W + out0 * rowb;
-  const unsigned char *Vt = (const unsigned char *)Wv + out0 * rowb;
-  const size_t vstride = (size_t)n * rowb;  // bytes between trial-weight variants
-  const unsigned char *Xt = (const unsigned char *)X + (tok_base + tok0) * rowb;
-  const int pc = tid & 7;          // 16-byte piece inside a 128-byte K slice (same for all pieces of a thread)
-  const int ra = tid >> 3;         // first row of this thread (0..63)
-  const uint32_t rstep = (uint32_t)(64 * rowb);  // 64 rows
-  const uint32_t roff = (uint32_t)(ra * rowb);
-  const int a_rows_ok = (int)min((int64_t)SBO, n - out0);   // valid weight rows in the tile
-  const int x_rows_ok = (int)min((int64_t)SBT, tb - tok0);  // valid token rows in the tile
+  // Buffer resources over this tile's rows: W, the three trial-weight
+  // variants (one resource, variant v at v * vstride) and the token rows.
+  const uint32_t rowb = (uint32_t)(m * ESZ);          // bytes per row of W / X
+  const int a_rows_ok = (int)min((int64_t)SBO, n - out0);
+  const int x_rows_ok = (int)min((int64_t)SBT, tb - tok0);
+  const uint32_t vstride = (uint32_t)(n * rowb);
+  const __amdgpu_buffer_rsrc_t rW = __builtin_amdgcn_make_buffer_rsrc(
+      (void *)((const unsigned char *)W + out0 * rowb), (short)0, (int)(a_rows_ok * rowb), RSRC_FLAGS);
+  const __amdgpu_buffer_rsrc_t rV = __builtin_amdgcn_make_buffer_rsrc(
+      (void *)((const unsigned char *)Wv + out0 * rowb), (short)0, (int)(2 * vstride + a_rows_ok * rowb), RSRC_FLAGS);
+  const __amdgpu_buffer_rsrc_t rX = __builtin_amdgcn_make_buffer_rsrc(
+      (void *)((const unsigned char *)X + (tok_base + tok0) * (int64_t)rowb), (short)0, (int)(x_rows_ok * rowb),
+      RSRC_FLAGS);
+  // Wave w fetches 64 consecutive rows of one operand (8 chunks of 8 rows x 128 B):
+  // waves 0-1 the first A operand, 2-3 the second, 4-7 the token rows.
+  const int kind = wave < 2 ? 0 : (wave < 4 ? 1 : 2);
+  const int rbase = (kind == 2 ? wave - 4 : (wave & 1)) * 64 + (lane >> 3);   // my row for chunk 0
+  const int lds_row0 = (kind == 0 ? 0 : (kind == 1 ? SBO : 2 * SBO)) + (kind == 2 ? wave - 4 : (wave & 1)) * 64;
+  const int slot = (lane & 7) ^ (lane >> 3);        // logical 16-byte slot this lane fetches
+  const int rows_ok = kind == 2 ? x_rows_ok : a_rows_ok;
 
-  uint4 rg[8];
-  // rg[0..1]: A0 rows ra, ra+64; rg[2..3]: A1 rows ra, ra+64; rg[4..7]: X rows ra + 64 j
-  auto load = [&](int st) {
+  auto issue = [&](int st, int buf) {
     int col;
-    const unsigned char *a0, *a1 = Vt + vstride;
+    uint32_t var = 0;
     if (st < KM) {
-      col = st * KT + pc * EPP;
-      a0 = Wt;
+      col = st * KT + slot * EPP;
+      var = vstride;                                  // main stage: second operand = variant N
     } else {
       const int r = 1 + (st - KM) / SPR;
-      const int cc = ((st - KM) % SPR) * KT + pc * EPP;
+      const int cc = ((st - KM) % SPR) * KT + slot * EPP;
       const bool up = cc < g;
       col = up ? s_order[r - 1] * g + cc : s_order[k - r] * g + (cc - g);
-      a0 = Vt + (up ? 2 * vstride : 0);
+      var = kind == 1 ? vstride : (up ? 2 * vstride : 0);
     }
     const bool cok = col < m;
-    const uint32_t coff = (uint32_t)col * ESZ;
+    unsigned char *dst = lds[buf] + lds_row0 * SBP;
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const bool ok = cok && (ra + 64 * h) < a_rows_ok;
-      const uint32_t off = roff + h * rstep + coff;
-      rg[h] = ok ? *(const uint4 *)(a0 + off) : make_uint4(0, 0, 0, 0);
-      rg[2 + h] = ok ? *(const uint4 *)(a1 + off) : make_uint4(0, 0, 0, 0);
+    for (int q = 0; q < 8; ++q) {
+      const int row = rbase + 8 * q;
+      uint32_t off = (cok && row < rows_ok) ? (uint32_t)row * rowb + (uint32_t)col * ESZ : OOB;
+      lds_void_t *d = (lds_void_t *)(dst + q * 8 * SBP);
+      if (kind == 2) {
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rX, d, 16, (int)off, 0, 0, 0);
+      } else if (kind == 0 && st < KM) {
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rW, d, 16, (int)off, 0, 0, 0);
+      } else {
+        if (off != OOB) off += var;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rV, d, 16, (int)off, 0, 0, 0);
+      }
     }
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const bool ok = cok && (ra + 64 * j) < x_rows_ok;
-      rg[4 + j] = ok ? *(const uint4 *)(Xt + roff + j * rstep + coff) : make_uint4(0, 0, 0, 0);
-    }
-  };
-  auto store = [&](int buf) {
-    unsigned char *L = lds[buf] + ra * SBP + pc * 16;
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      *(uint4 *)(L + (h * 64) * SBP) = rg[h];
-      *(uint4 *)(L + (SBO + h * 64) * SBP) = rg[2 + h];
-    }
-#pragma unroll
-    for (int j = 0; j < 4; ++j) *(uint4 *)(L + (2 * SBO + j * 64) * SBP) = rg[4 + j];
   };
 
   f32x16_t accY[4], accQ[4];
@@ -241,18 +243,23 @@ __global__ __launch_bounds__(512, 1) void sba_klgemm_kernel(
       accQ[b][v] = 0.0f;
     }
 
+  // Operand fragments: row r, logical slot sl lives at r * 128 + ((sl ^ (r & 7)) * 16); every
+  // fragment row here has r & 7 == lane & 7.
+  const int sw = lane & 7;
   auto compute = [&](int buf, bool main_stage) {
     const unsigned char *L = lds[buf];
     const unsigned char *Bt = L + (2 * SBO + wave * 32 + (lane & 31)) * SBP;
+    const unsigned char *A0 = L + (lane & 31) * SBP;
+    const unsigned char *A1 = L + (SBO + (lane & 31)) * SBP;
     if (BF16) {
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk) {
-        const int off = kk * 32 + (lane >> 5) * 16;
+        const int off = (((2 * kk + (lane >> 5)) ^ sw) * 16);
         const uint4 b = *(const uint4 *)(Bt + off);
 #pragma unroll
         for (int blk = 0; blk < 4; ++blk) {
-          const uint4 a0 = *(const uint4 *)(L + (blk * 32 + (lane & 31)) * SBP + off);
-          uint4 a1 = *(const uint4 *)(L + (SBO + blk * 32 + (lane & 31)) * SBP + off);
+          const uint4 a0 = *(const uint4 *)(A0 + blk * 32 * SBP + off);
+          uint4 a1 = *(const uint4 *)(A1 + blk * 32 * SBP + off);
           if (main_stage) {
             accY[blk] = mfma_bf16(a0, b, accY[blk]);
             accQ[blk] = mfma_bf16(a1, b, accQ[blk]);
@@ -266,12 +273,13 @@ __global__ __launch_bounds__(512, 1) void sba_klgemm_kernel(
     } else {
 #pragma unroll 4
       for (int kk = 0; kk < 16; ++kk) {
-        const int off = kk * 8 + (lane >> 5) * 4;
+        const int e = 2 * kk + (lane >> 5);
+        const int off = (((e >> 2) ^ sw) * 16) + (e & 3) * 4;
         const float b = *(const float *)(Bt + off);
 #pragma unroll
         for (int blk = 0; blk < 4; ++blk) {
-          const float a0 = *(const float *)(L + (blk * 32 + (lane & 31)) * SBP + off);
-          const float a1 = *(const float *)(L + (SBO + blk * 32 + (lane & 31)) * SBP + off);
+          const float a0 = *(const float *)(A0 + blk * 32 * SBP + off);
+          const float a1 = *(const float *)(A1 + blk * 32 * SBP + off);
           if (main_stage) {
             accY[blk] = mfma_f32(a0, b, accY[blk]);
             accQ[blk] = mfma_f32(a1, b, accQ[blk]);
@@ -337,17 +345,17 @@ __global__ __launch_bounds__(512, 1) void sba_klgemm_kernel(
     if (lane < 32 && tvalid) sq[((int64_t)r * NC + c) * tb + tcol] = make_float4(mq, zq, sy_tok - se, 0.0f);
   };
 
-  load(0);
-  store(0);
+  issue(0, 0);
+  __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   for (int st = 0; st < total; ++st) {
     const bool more = st + 1 < total;
-    if (more) load(st + 1);
+    if (more) issue(st + 1, (st + 1) & 1);   // DMA of the next stage overlaps this one's MFMAs
     const bool main_stage = st < KM;
     compute(st & 1, main_stage);
     if (st == KM - 1) epilogue(0);
     else if (!main_stage && (st - KM) % SPR == SPR - 1) epilogue(1 + (st - KM) / SPR);
-    if (more) store((st + 1) & 1);
+    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
   }
 }
@@ -444,9 +452,12 @@ SbaPlan sba_plan(int64_t t, int64_t n, int64_t m, int group, bool bf16) {
   p.R = p.k / 2 + 1;
   p.nchunk = (int)((n + SBO - 1) / SBO);
   const size_t per_tok = (size_t)p.nchunk * (8 + 16 * (size_t)p.R);
-  const size_t budget = (size_t)1 << 30;  // chunk statistics per batch
-  int64_t tb = (int64_t)(budget / per_tok) / SBT * SBT;
-  if (tb < SBT) tb = SBT;
+  const size_t budget = (size_t)4 << 30;  // chunk statistics per batch (HBM is 288 GB)
+  int64_t cap = (int64_t)(budget / per_tok) / SBT * SBT;
+  if (cap < SBT) cap = SBT;
+  p.nbatch = (int)((t + cap - 1) / cap);
+  int64_t tb = (t + p.nbatch - 1) / p.nbatch;   // equal batches, a multiple of the token tile
+  tb = (tb + SBT - 1) / SBT * SBT;
   if (tb > t) tb = t;
   p.tb = tb;
   p.nbatch = (int)((t + tb - 1) / tb);
