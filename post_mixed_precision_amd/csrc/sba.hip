@@ -169,7 +169,8 @@ __global__ __launch_bounds__(512, 1) void sba_klgemm_kernel(
     if (c >= c_last || tt >= TT) return;
   }
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform (scalar) by construction
   const int64_t out0 = (int64_t)c * SBO;
   const int64_t tok0 = (int64_t)tt * SBT;  // within the batch
   for (int j = tid; j < k; j += 512) {
@@ -200,35 +201,45 @@ __global__ __launch_bounds__(512, 1) void sba_klgemm_kernel(
   const int kind = wave < 2 ? 0 : (wave < 4 ? 1 : 2);
   const int rbase = (kind == 2 ? wave - 4 : (wave & 1)) * 64 + (lane >> 3);   // my row for chunk 0
   const int lds_row0 = (kind == 0 ? 0 : (kind == 1 ? SBO : 2 * SBO)) + (kind == 2 ? wave - 4 : (wave & 1)) * 64;
-  const int slot = (lane & 7) ^ (lane >> 3);        // logical 16-byte slot this lane fetches
+  // LDS swizzle: row r, logical 16-byte slot sl sits in physical slot sl ^ ((r >> 1) & 7), so the
+  // 16 rows of one 256-byte LDS pass at a fixed logical slot hit 16 distinct bank groups.  Lane L
+  // of a chunk writes physical slot L % 8 of chunk row L / 8.
   const int rows_ok = kind == 2 ? x_rows_ok : a_rows_ok;
 
   auto issue = [&](int st, int buf) {
-    int col;
-    uint32_t var = 0;
-    if (st < KM) {
-      col = st * KT + slot * EPP;
-      var = vstride;                                  // main stage: second operand = variant N
+    int c0, gu = 0, gd = 0;
+    const bool main_stage = st < KM;
+    if (main_stage) {
+      c0 = st * KT;
     } else {
       const int r = 1 + (st - KM) / SPR;
-      const int cc = ((st - KM) % SPR) * KT + slot * EPP;
-      const bool up = cc < g;
-      col = up ? s_order[r - 1] * g + cc : s_order[k - r] * g + (cc - g);
-      var = kind == 1 ? vstride : (up ? 2 * vstride : 0);
+      c0 = ((st - KM) % SPR) * KT;
+      gu = s_order[r - 1];
+      gd = s_order[k - r];
     }
-    const bool cok = col < m;
     unsigned char *dst = lds[buf] + lds_row0 * SBP;
 #pragma unroll
     for (int q = 0; q < 8; ++q) {
-      const int row = rbase + 8 * q;
-      uint32_t off = (cok && row < rows_ok) ? (uint32_t)row * rowb + (uint32_t)col * ESZ : OOB;
+      const int row = rbase + 8 * q;                     // tile-local row of this lane
+      const int lrow = lds_row0 + 8 * q + (lane >> 3);   // LDS row it lands in
+      const int sl = (lane & 7) ^ ((lrow >> 1) & 7);     // logical slot to fetch
+      const int cc = c0 + sl * EPP;
+      int col, var_new = 1;
+      if (main_stage) {
+        col = cc;
+      } else {
+        const bool up = cc < g;
+        col = up ? gu * g + cc : gd * g + (cc - g);
+        var_new = up ? 2 : 0;
+      }
+      uint32_t off = (col < m && row < rows_ok) ? (uint32_t)row * rowb + (uint32_t)col * ESZ : OOB;
       lds_void_t *d = (lds_void_t *)(dst + q * 8 * SBP);
       if (kind == 2) {
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rX, d, 16, (int)off, 0, 0, 0);
-      } else if (kind == 0 && st < KM) {
+      } else if (kind == 0 && main_stage) {
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rW, d, 16, (int)off, 0, 0, 0);
       } else {
-        if (off != OOB) off += var;
+        if (off != OOB) off += (kind == 1 ? 1u : (uint32_t)var_new) * vstride;
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rV, d, 16, (int)off, 0, 0, 0);
       }
     }
@@ -243,10 +254,10 @@ __global__ __launch_bounds__(512, 1) void sba_klgemm_kernel(
       accQ[b][v] = 0.0f;
     }
 
-  // Operand fragments: row r, logical slot sl lives at r * 128 + ((sl ^ (r & 7)) * 16); every
-  // fragment row here has r & 7 == lane & 7.
-  const int sw = lane & 7;
-  auto compute = [&](int buf, bool main_stage) {
+  // Fragment row r (A rows blk*32 + lane%32, token rows 256 + wave*32 + lane%32) has
+  // (r >> 1) & 7 == ((lane & 31) >> 1) & 7.
+  const int sw = (lane >> 1) & 7;
+  auto compute_main = [&](int buf) {
     const unsigned char *L = lds[buf];
     const unsigned char *Bt = L + (2 * SBO + wave * 32 + (lane & 31)) * SBP;
     const unsigned char *A0 = L + (lane & 31) * SBP;
@@ -254,39 +265,56 @@ __global__ __launch_bounds__(512, 1) void sba_klgemm_kernel(
     if (BF16) {
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk) {
-        const int off = (((2 * kk + (lane >> 5)) ^ sw) * 16);
+        const int off = ((2 * kk + (lane >> 5)) ^ sw) * 16;
         const uint4 b = *(const uint4 *)(Bt + off);
 #pragma unroll
         for (int blk = 0; blk < 4; ++blk) {
-          const uint4 a0 = *(const uint4 *)(A0 + blk * 32 * SBP + off);
-          uint4 a1 = *(const uint4 *)(A1 + blk * 32 * SBP + off);
-          if (main_stage) {
-            accY[blk] = mfma_bf16(a0, b, accY[blk]);
-            accQ[blk] = mfma_bf16(a1, b, accQ[blk]);
-          } else {
-            a1.x ^= 0x80008000u; a1.y ^= 0x80008000u; a1.z ^= 0x80008000u; a1.w ^= 0x80008000u;
-            accQ[blk] = mfma_bf16(a0, b, accQ[blk]);
-            accQ[blk] = mfma_bf16(a1, b, accQ[blk]);
-          }
+          accY[blk] = mfma_bf16(*(const uint4 *)(A0 + blk * 32 * SBP + off), b, accY[blk]);
+          accQ[blk] = mfma_bf16(*(const uint4 *)(A1 + blk * 32 * SBP + off), b, accQ[blk]);
         }
       }
     } else {
 #pragma unroll 4
       for (int kk = 0; kk < 16; ++kk) {
         const int e = 2 * kk + (lane >> 5);
-        const int off = (((e >> 2) ^ sw) * 16) + (e & 3) * 4;
+        const int off = ((e >> 2) ^ sw) * 16 + (e & 3) * 4;
         const float b = *(const float *)(Bt + off);
 #pragma unroll
         for (int blk = 0; blk < 4; ++blk) {
-          const float a0 = *(const float *)(A0 + blk * 32 * SBP + off);
-          const float a1 = *(const float *)(A1 + blk * 32 * SBP + off);
-          if (main_stage) {
-            accY[blk] = mfma_f32(a0, b, accY[blk]);
-            accQ[blk] = mfma_f32(a1, b, accQ[blk]);
-          } else {
-            accQ[blk] = mfma_f32(a0, b, accQ[blk]);
-            accQ[blk] = mfma_f32(-a1, b, accQ[blk]);
-          }
+          accY[blk] = mfma_f32(*(const float *)(A0 + blk * 32 * SBP + off), b, accY[blk]);
+          accQ[blk] = mfma_f32(*(const float *)(A1 + blk * 32 * SBP + off), b, accQ[blk]);
+        }
+      }
+    }
+  };
+  auto compute_update = [&](int buf) {
+    const unsigned char *L = lds[buf];
+    const unsigned char *Bt = L + (2 * SBO + wave * 32 + (lane & 31)) * SBP;
+    const unsigned char *A0 = L + (lane & 31) * SBP;
+    const unsigned char *A1 = L + (SBO + (lane & 31)) * SBP;
+    if (BF16) {
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) {
+        const int off = ((2 * kk + (lane >> 5)) ^ sw) * 16;
+        const uint4 b = *(const uint4 *)(Bt + off);
+#pragma unroll
+        for (int blk = 0; blk < 4; ++blk) {
+          uint4 a1 = *(const uint4 *)(A1 + blk * 32 * SBP + off);
+          a1.x ^= 0x80008000u; a1.y ^= 0x80008000u; a1.z ^= 0x80008000u; a1.w ^= 0x80008000u;
+          accQ[blk] = mfma_bf16(*(const uint4 *)(A0 + blk * 32 * SBP + off), b, accQ[blk]);
+          accQ[blk] = mfma_bf16(a1, b, accQ[blk]);
+        }
+      }
+    } else {
+#pragma unroll 4
+      for (int kk = 0; kk < 16; ++kk) {
+        const int e = 2 * kk + (lane >> 5);
+        const int off = ((e >> 2) ^ sw) * 16 + (e & 3) * 4;
+        const float b = *(const float *)(Bt + off);
+#pragma unroll
+        for (int blk = 0; blk < 4; ++blk) {
+          accQ[blk] = mfma_f32(*(const float *)(A0 + blk * 32 * SBP + off), b, accQ[blk]);
+          accQ[blk] = mfma_f32(-*(const float *)(A1 + blk * 32 * SBP + off), b, accQ[blk]);
         }
       }
     }
@@ -345,18 +373,28 @@ __global__ __launch_bounds__(512, 1) void sba_klgemm_kernel(
     if (lane < 32 && tvalid) sq[((int64_t)r * NC + c) * tb + tcol] = make_float4(mq, zq, sy_tok - se, 0.0f);
   };
 
+  // Phase 1: Y and Yhat_0 over K = m.  Phase 2: for every step r, its 2g/KT
+  // slab-update stages, then the step's statistics.  The stage index runs on
+  // across both phases; the DMA of stage st+1 is issued before stage st computes.
   issue(0, 0);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
-  for (int st = 0; st < total; ++st) {
-    const bool more = st + 1 < total;
-    if (more) issue(st + 1, (st + 1) & 1);   // DMA of the next stage overlaps this one's MFMAs
-    const bool main_stage = st < KM;
-    compute(st & 1, main_stage);
-    if (st == KM - 1) epilogue(0);
-    else if (!main_stage && (st - KM) % SPR == SPR - 1) epilogue(1 + (st - KM) / SPR);
+  for (int st = 0; st < KM; ++st) {
+    if (st + 1 < total) issue(st + 1, (st + 1) & 1);
+    compute_main(st & 1);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
+  }
+  epilogue(0);
+  for (int r = 1; r < R; ++r) {
+    for (int s = 0; s < SPR; ++s) {
+      const int st = KM + (r - 1) * SPR + s;
+      if (st + 1 < total) issue(st + 1, (st + 1) & 1);
+      compute_update(st & 1);
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+    }
+    epilogue(r);
   }
 }
 
