@@ -152,7 +152,12 @@ __global__ __launch_bounds__(512, 1) void sba_klgemm_kernel(
   constexpr int ESZ = BF16 ? 2 : 4;
   constexpr int KT = BF16 ? 64 : 32;  // K elements per stage (128 bytes per row)
   constexpr int EPP = 16 / ESZ;       // elements per 16-byte piece
-  __shared__ __attribute__((aligned(16))) unsigned char lds[2][STAGE_BYTES];
+  // Two distinct LDS objects rather than one array indexed at run time: each
+  // stage below names its buffers statically, so the compiler can tell the DMA
+  // into one buffer from the fragment reads of the other and need not wait for
+  // the prefetch before computing.
+  __shared__ __attribute__((aligned(16))) unsigned char lds0[STAGE_BYTES];
+  __shared__ __attribute__((aligned(16))) unsigned char lds1[STAGE_BYTES];
   __shared__ int s_order[MAXK];
   __shared__ int s_rows_ok;   // valid outputs in this chunk (read in the epilogue, never hoisted)
 
@@ -206,7 +211,7 @@ __global__ __launch_bounds__(512, 1) void sba_klgemm_kernel(
   // of a chunk writes physical slot L % 8 of chunk row L / 8.
   const int rows_ok = kind == 2 ? x_rows_ok : a_rows_ok;
 
-  auto issue = [&](int st, int buf) {
+  auto issue = [&](int st, unsigned char *buf) __attribute__((always_inline)) {
     int c0, gu = 0, gd = 0;
     const bool main_stage = st < KM;
     if (main_stage) {
@@ -217,7 +222,7 @@ __global__ __launch_bounds__(512, 1) void sba_klgemm_kernel(
       gu = s_order[r - 1];
       gd = s_order[k - r];
     }
-    unsigned char *dst = lds[buf] + lds_row0 * SBP;
+    unsigned char *dst = buf + lds_row0 * SBP;
 #pragma unroll
     for (int q = 0; q < 8; ++q) {
       const int row = rbase + 8 * q;                     // tile-local row of this lane
@@ -257,8 +262,7 @@ __global__ __launch_bounds__(512, 1) void sba_klgemm_kernel(
   // Fragment row r (A rows blk*32 + lane%32, token rows 256 + wave*32 + lane%32) has
   // (r >> 1) & 7 == ((lane & 31) >> 1) & 7.
   const int sw = (lane >> 1) & 7;
-  auto compute_main = [&](int buf) {
-    const unsigned char *L = lds[buf];
+  auto compute_main = [&](const unsigned char *L) __attribute__((always_inline)) {
     const unsigned char *Bt = L + (2 * SBO + wave * 32 + (lane & 31)) * SBP;
     const unsigned char *A0 = L + (lane & 31) * SBP;
     const unsigned char *A1 = L + (SBO + (lane & 31)) * SBP;
@@ -287,8 +291,7 @@ __global__ __launch_bounds__(512, 1) void sba_klgemm_kernel(
       }
     }
   };
-  auto compute_update = [&](int buf) {
-    const unsigned char *L = lds[buf];
+  auto compute_update = [&](const unsigned char *L) __attribute__((always_inline)) {
     const unsigned char *Bt = L + (2 * SBO + wave * 32 + (lane & 31)) * SBP;
     const unsigned char *A0 = L + (lane & 31) * SBP;
     const unsigned char *A1 = L + (SBO + (lane & 31)) * SBP;
@@ -324,7 +327,7 @@ __global__ __launch_bounds__(512, 1) void sba_klgemm_kernel(
   const int64_t tcol = tok0 + wave * 32 + (lane & 31);
   const bool tvalid = tcol < tb;
   float sy_tok = 0.0f;
-  auto epilogue = [&](int r) {
+  auto epilogue = [&](int r) __attribute__((always_inline)) {
     // Output row of accumulator element (blk, v) is blk*32 + acc32_row(v, lane).
     const int lim = PARTIAL ? s_rows_ok - 4 * (lane >> 5) : SBO;
     if (r == 0) {
@@ -376,26 +379,43 @@ __global__ __launch_bounds__(512, 1) void sba_klgemm_kernel(
   // Phase 1: Y and Yhat_0 over K = m.  Phase 2: for every step r, its 2g/KT
   // slab-update stages, then the step's statistics.  The stage index runs on
   // across both phases; the DMA of stage st+1 is issued before stage st computes.
-  issue(0, 0);
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
-  for (int st = 0; st < KM; ++st) {
-    if (st + 1 < total) issue(st + 1, (st + 1) & 1);
-    compute_main(st & 1);
+  // Stage st lives in lds0 when st is even and in lds1 when odd.  Both loops
+  // are unrolled by two so every stage names its buffers statically.
+  auto main_stage = [&](int st, const unsigned char *cur, unsigned char *nxt) __attribute__((always_inline)) {
+    if (st + 1 < total) issue(st + 1, nxt);
+    compute_main(cur);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
+  };
+  auto update_stage = [&](int st, const unsigned char *cur, unsigned char *nxt) __attribute__((always_inline)) {
+    if (st + 1 < total) issue(st + 1, nxt);
+    compute_update(cur);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if ((st - KM) % SPR == SPR - 1) epilogue(1 + (st - KM) / SPR);
+  };
+  issue(0, lds0);
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  int st = 0;
+  for (; st + 1 < KM; st += 2) {
+    main_stage(st, lds0, lds1);
+    main_stage(st + 1, lds1, lds0);
+  }
+  if (st < KM) {
+    main_stage(st, lds0, lds1);
+    ++st;
   }
   epilogue(0);
-  for (int r = 1; r < R; ++r) {
-    for (int s = 0; s < SPR; ++s) {
-      const int st = KM + (r - 1) * SPR + s;
-      if (st + 1 < total) issue(st + 1, (st + 1) & 1);
-      compute_update(st & 1);
-      __builtin_amdgcn_s_waitcnt(0);
-      __syncthreads();
-    }
-    epilogue(r);
+  if (st < total && (st & 1)) {
+    update_stage(st, lds1, lds0);
+    ++st;
   }
+  for (; st + 1 < total; st += 2) {
+    update_stage(st, lds0, lds1);
+    update_stage(st + 1, lds1, lds0);
+  }
+  if (st < total) update_stage(st, lds0, lds1);
 }
 
 // ---------------------------------------------------------------------------
