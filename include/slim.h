@@ -87,7 +87,7 @@ int slim_last_hip_error(void);
  * token splits in a fixed order, so results are bitwise reproducible.
  * Requires t >= 0, m >= 1.
  * ---------------------------------------------------------------------- */
-size_t slim_hessian_workspace(int64_t t, int64_t m);
+size_t slim_hessian_workspace(int64_t t, int64_t m, int xdt);
 int slim_hessian(const void *X, int xdt, int64_t t, int64_t m, float *H, int accumulate,
                  void *ws, size_t ws_bytes, void *stream);
 

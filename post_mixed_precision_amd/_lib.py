@@ -25,7 +25,7 @@ _SIGS = {
     "slim_version": (_c_int, []),
     "slim_status_string": (ctypes.c_char_p, [_c_int]),
     "slim_last_hip_error": (_c_int, []),
-    "slim_hessian_workspace": (_c_sz, [_c_i64, _c_i64]),
+    "slim_hessian_workspace": (_c_sz, [_c_i64, _c_i64, _c_int]),
     "slim_hessian": (_c_int, [_c_vp, _c_int, _c_i64, _c_i64, _c_vp, _c_int, _c_vp, _c_sz, _c_vp]),
     "slim_salience_workspace": (_c_sz, [_c_i64, _c_i64, _c_int]),
     "slim_salience": (_c_int, [_c_vp, _c_i64, _c_dbl, _c_vp, _c_int, _c_i64, _c_int, _c_vp, _c_vp, _c_vp,
@@ -124,7 +124,7 @@ def hessian(X, H=None, accumulate: bool = False):
     T, m = X.shape
     if H is None:
         H = torch.empty((m, m), dtype=torch.float32, device=X.device)
-    ws = _ws(lib.slim_hessian_workspace(T, m), X.device)
+    ws = _ws(lib.slim_hessian_workspace(T, m, _dtype_code(X)), X.device)
     check(lib.slim_hessian(_ptr(X), _dtype_code(X), T, m, _ptr(H), int(accumulate), _ptr(ws), ws.numel(),
                            _stream(X.device)), "slim_hessian")
     return H

@@ -102,9 +102,9 @@ const char *slim_status_string(int status) {
 int slim_last_hip_error(void) { return g_last_hip_error; }
 
 // ---------------------------------------------------------------- Hessian
-size_t slim_hessian_workspace(int64_t t, int64_t m) {
-  if (t < 0 || m < 1 || m > SLIM_MAX_WIDTH) return 0;
-  return slim::hessian_plan(t, m).ws_bytes;
+size_t slim_hessian_workspace(int64_t t, int64_t m, int xdt) {
+  if (t < 0 || m < 1 || m > SLIM_MAX_WIDTH || !valid_dtype(xdt)) return 0;
+  return slim::hessian_plan(t, m, xdt == SLIM_BF16).ws_bytes;
 }
 
 int slim_hessian(const void *X, int xdt, int64_t t, int64_t m, float *H, int accumulate, void *ws, size_t ws_bytes,
@@ -113,7 +113,7 @@ int slim_hessian(const void *X, int xdt, int64_t t, int64_t m, float *H, int acc
   if (!valid_dtype(xdt)) return SLIM_E_DTYPE;
   if (t < 0 || m < 1 || m > SLIM_MAX_WIDTH) return SLIM_E_SHAPE;
   if (!aligned16(H) || (t > 0 && !aligned16(X))) return SLIM_E_ALIGN;
-  const slim::HessianPlan p = slim::hessian_plan(t, m);
+  const slim::HessianPlan p = slim::hessian_plan(t, m, xdt == SLIM_BF16);
   if (!ws || ws_bytes < p.ws_bytes) return SLIM_E_WORKSPACE;
   if (!aligned16(ws)) return SLIM_E_ALIGN;
   hipError_t e = slim::launch_hessian(X, xdt == SLIM_BF16, t, m, H, accumulate != 0, ws, p, (hipStream_t)stream);

@@ -181,24 +181,152 @@ __global__ __launch_bounds__(256, 2) void hessian_gram_kernel(const void *__rest
       }
 }
 
+// bf16 fast path: 256 x 256 lower tiles, 8 waves (each 128 x 64 = 4 x 2 MFMA
+// blocks).  X rows are DMA'd into LDS as they are stored (token-major), and the
+// MFMA operands -- 8 consecutive tokens of one column per lane -- are read with
+// the gfx950 transposing LDS load ds_read_b64_tr_b16: within a group of 16
+// lanes, lane L points at token row t0 + L/4, columns c0 + 4 (L % 4), and lane i
+// receives tokens t0..t0+3 of column c0 + i.  Two such loads make one operand.
+// LDS rows (one token, 256 columns = 512 bytes) are swizzled per 16-byte slot
+// with slot ^ (4 (row & 3)), so the four token rows read by one 256-byte LDS
+// pass land in four distinct 64-byte bank windows.
+constexpr int HT2 = 256;                   // tile edge
+constexpr int HK2 = 64;                    // tokens per stage
+constexpr int HROW2 = HT2 * 2;             // bytes per LDS token row of one operand
+constexpr int HOP2 = HK2 * HROW2;          // bytes of one operand per stage (32 KB)
+constexpr uint32_t HOOB = 0x7ffffff0u;     // buffer offset that reads as zero
+
+typedef short v4i16_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4i16_t lds_v4i16_t;
+typedef __attribute__((address_space(3))) void lds_void2_t;
+
+__global__ __launch_bounds__(512, 1) void hessian_gram_tr_kernel(const uint16_t *__restrict__ X, int64_t T,
+                                                                 int64_t m, int64_t tok_per_split, int ntiles,
+                                                                 float *__restrict__ part) {
+  __shared__ __attribute__((aligned(16))) unsigned char lds0[2 * HOP2];
+  __shared__ __attribute__((aligned(16))) unsigned char lds1[2 * HOP2];
+  int bi, bj;
+  tri_decode(blockIdx.x, bi, bj);
+  const int split = blockIdx.y;
+  const int64_t tbeg = (int64_t)split * tok_per_split;
+  const int64_t tend = min(T, tbeg + tok_per_split);
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave >> 2, wn = wave & 3;   // wave tile: rows wm*128 .. +128 (block bi), cols wn*64 .. +64 (block bj)
+  const uint32_t rowb = (uint32_t)(m * 2);
+  // Loader: wave w fetches 8 chunks of 1 KB (2 token rows x 512 bytes) per stage:
+  // waves 0-3 operand A (columns of block bi), waves 4-7 operand B (block bj).
+  const int opnd = wave >> 2;
+  const int64_t col0 = (int64_t)(opnd ? bj : bi) * HT2;
+  const int cols_ok = (int)min((int64_t)HT2, m - col0);
+  const int rsub = lane >> 5;                // row inside a chunk
+  const int pslot = lane & 31;               // physical 16-byte slot this lane fills
+  auto issue = [&](int64_t t0, unsigned char *buf) __attribute__((always_inline)) {
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+        (void *)(X + t0 * m), (short)0, (int)min((int64_t)HK2 * rowb, (tend - t0) * (int64_t)rowb), 0x00020000);
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      const int row = (wave & 3) * 16 + 2 * q + rsub;   // token row within the stage
+      const int lslot = pslot ^ (4 * (row & 3));         // logical slot = 8 columns
+      const int cl = lslot * 8;
+      const uint32_t off = (cl < cols_ok) ? (uint32_t)row * rowb + (uint32_t)(col0 + cl) * 2 : HOOB;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rs, (lds_void2_t *)(buf + opnd * HOP2 + ((wave & 3) * 16 + 2 * q) * HROW2), 16, (int)off, 0, 0, 0);
+    }
+  };
+  f32x16_t acc[4][2];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
+  // transposing fragment read: 8 tokens (kt .. kt+7) of column c for this lane
+  const int li = lane & 15;
+  auto frag = [&](const unsigned char *opbase, int c16, int kt) __attribute__((always_inline)) -> uint4 {
+    // lane group (16 lanes) reads rows kt + li/4 (+4), columns c16 + 4 (li % 4)
+    const int col = c16 + 4 * (li & 3);
+    const int r0 = kt + (li >> 2);
+    const int r1 = r0 + 4;
+    const int s0 = ((col >> 3) ^ (4 * (r0 & 3))) * 16 + (col & 7) * 2;
+    const int s1 = ((col >> 3) ^ (4 * (r1 & 3))) * 16 + (col & 7) * 2;
+    const v4i16_t a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t *)(opbase + r0 * HROW2 + s0));
+    const v4i16_t b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t *)(opbase + r1 * HROW2 + s1));
+    uint4 o;
+    o.x = (uint32_t)(uint16_t)a.x | ((uint32_t)(uint16_t)a.y << 16);
+    o.y = (uint32_t)(uint16_t)a.z | ((uint32_t)(uint16_t)a.w << 16);
+    o.z = (uint32_t)(uint16_t)b.x | ((uint32_t)(uint16_t)b.y << 16);
+    o.w = (uint32_t)(uint16_t)b.z | ((uint32_t)(uint16_t)b.w << 16);
+    return o;
+  };
+  auto compute = [&](const unsigned char *L) __attribute__((always_inline)) {
+    const unsigned char *A = L, *B = L + HOP2;
+    // lane l: column offset 16 ((l / 16) % 2) inside a 32-block, tokens 8 (l / 32) + 0..7
+    const int csub = 16 * ((lane >> 4) & 1);
+#pragma unroll
+    for (int kk = 0; kk < HK2 / 16; ++kk) {
+      const int kt = kk * 16 + 8 * (lane >> 5);
+      uint4 a[4], b[2];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) a[i] = frag(A, wm * 128 + i * 32 + csub, kt);
+#pragma unroll
+      for (int j = 0; j < 2; ++j) b[j] = frag(B, wn * 64 + j * 32 + csub, kt);
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) acc[i][j] = mfma_bf16(a[i], b[j], acc[i][j]);
+    }
+  };
+  auto stage = [&](int64_t t0, const unsigned char *cur, unsigned char *nxt) __attribute__((always_inline)) {
+    if (t0 + HK2 < tend) issue(t0 + HK2, nxt);
+    compute(cur);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+  };
+  if (tbeg < tend) {
+    issue(tbeg, lds0);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    int64_t t0 = tbeg;
+    for (; t0 + HK2 < tend; t0 += 2 * HK2) {
+      stage(t0, lds0, lds1);
+      stage(t0 + HK2, lds1, lds0);
+    }
+    if (t0 < tend) stage(t0, lds0, lds1);
+  }
+  float *out = part + ((size_t)split * ntiles + blockIdx.x) * (HT2 * HT2);
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int row = wm * 128 + i * 32 + acc32_row(v, lane);
+        const int col = wn * 64 + j * 32 + (lane & 31);
+        out[row * HT2 + col] = acc[i][j][v];
+      }
+}
+
 // Sum the split partials in split order, double, write the lower tile and its
 // mirror (diagonal tiles: the lower triangle and its mirror).
+template <int TILE>
 __global__ __launch_bounds__(256) void hessian_reduce_kernel(const float *__restrict__ part, int nsplit,
-                                                             int ntiles, int64_t m,
-                                                             float *__restrict__ H, bool accumulate) {
-  __shared__ float tr[32][HT + 1];
+                                                             int ntiles, int64_t m, float *__restrict__ H,
+                                                             bool accumulate) {
+  __shared__ float tr[32][TILE + 1];
   int bi, bj;
   tri_decode(blockIdx.x, bi, bj);
   const int tid = threadIdx.x;
-  for (int r0 = 0; r0 < HT; r0 += 32) {
+  constexpr int PER = 32 * TILE / 256;
+  for (int r0 = 0; r0 < TILE; r0 += 32) {
 #pragma unroll 4
-    for (int e = 0; e < 16; ++e) {
+    for (int e = 0; e < PER; ++e) {
       const int idx = tid + e * 256;
-      const int r = r0 + idx / HT, c = idx % HT;
+      const int r = r0 + idx / TILE, c = idx % TILE;
       float s = 0.0f;
-      for (int sp = 0; sp < nsplit; ++sp) s += part[((size_t)sp * ntiles + blockIdx.x) * (HT * HT) + r * HT + c];
+      for (int sp = 0; sp < nsplit; ++sp) s += part[((size_t)sp * ntiles + blockIdx.x) * (TILE * TILE) + r * TILE + c];
       float v = 2.0f * s;
-      const int64_t gi = (int64_t)bi * HT + r, gj = (int64_t)bj * HT + c;
+      const int64_t gi = (int64_t)bi * TILE + r, gj = (int64_t)bj * TILE + c;
       if (gi < m && gj < m && (bi != bj || r >= c)) {
         if (accumulate) v += H[gi * m + gj];
         H[gi * m + gj] = v;
@@ -207,20 +335,22 @@ __global__ __launch_bounds__(256) void hessian_reduce_kernel(const float *__rest
     }
     __syncthreads();
 #pragma unroll 4
-    for (int e = 0; e < 16; ++e) {
+    for (int e = 0; e < PER; ++e) {
       const int idx = tid + e * 256;
       const int c = idx / 32, rr = idx % 32;
       const int r = r0 + rr;
-      const int64_t gi = (int64_t)bi * HT + r, gj = (int64_t)bj * HT + c;
+      const int64_t gi = (int64_t)bi * TILE + r, gj = (int64_t)bj * TILE + c;
       if (gi < m && gj < m && (bi != bj || r > c)) H[gj * m + gi] = tr[rr][c];
     }
     __syncthreads();
   }
 }
 
-HessianPlan hessian_plan(int64_t t, int64_t m) {
+HessianPlan hessian_plan(int64_t t, int64_t m, bool bf16) {
   HessianPlan p;
-  p.nb = (int)((m + HT - 1) / HT);
+  p.tr = bf16 && (m % 8 == 0);                 // DMA + transposing-read kernel
+  p.tile = p.tr ? HT2 : HT;
+  p.nb = (int)((m + p.tile - 1) / p.tile);
   p.ntiles = p.nb * (p.nb + 1) / 2;
   const int64_t want = (1024 + p.ntiles - 1) / p.ntiles;       // fill the chip several times over
   const int64_t cap = (t + 4095) / 4096;                         // >= 4096 tokens per split
@@ -230,24 +360,31 @@ HessianPlan hessian_plan(int64_t t, int64_t m) {
   per = (per + 63) / 64 * 64;
   if (per < 64) per = 64;
   p.tok_per_split = per;
-  p.ws_bytes = (size_t)p.nsplit * p.ntiles * HT * HT * sizeof(float);
+  p.ws_bytes = (size_t)p.nsplit * p.ntiles * p.tile * p.tile * sizeof(float);
   return p;
 }
 
 hipError_t launch_hessian(const void *X, bool bf16, int64_t t, int64_t m, float *H, bool accumulate,
                           void *ws, const HessianPlan &p, hipStream_t st) {
   float *part = (float *)ws;
-  const bool aligned = bf16 ? (m % 8 == 0) : (m % 4 == 0);
   dim3 grid(p.ntiles, p.nsplit);
   timer_begin(K_HESSIAN, st);
-  if (bf16)
-    hessian_gram_kernel<true><<<grid, 256, 0, st>>>(X, t, m, p.tok_per_split, p.ntiles, aligned, part);
-  else
-    hessian_gram_kernel<false><<<grid, 256, 0, st>>>(X, t, m, p.tok_per_split, p.ntiles, aligned, part);
+  if (p.tr) {
+    hessian_gram_tr_kernel<<<grid, 512, 0, st>>>((const uint16_t *)X, t, m, p.tok_per_split, p.ntiles, part);
+  } else {
+    const bool aligned = bf16 ? (m % 8 == 0) : (m % 4 == 0);
+    if (bf16)
+      hessian_gram_kernel<true><<<grid, 256, 0, st>>>(X, t, m, p.tok_per_split, p.ntiles, aligned, part);
+    else
+      hessian_gram_kernel<false><<<grid, 256, 0, st>>>(X, t, m, p.tok_per_split, p.ntiles, aligned, part);
+  }
   timer_end(K_HESSIAN, st);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hessian_reduce_kernel<<<p.ntiles, 256, 0, st>>>(part, p.nsplit, p.ntiles, m, H, accumulate);
+  if (p.tr)
+    hessian_reduce_kernel<HT2><<<p.ntiles, 256, 0, st>>>(part, p.nsplit, p.ntiles, m, H, accumulate);
+  else
+    hessian_reduce_kernel<HT><<<p.ntiles, 256, 0, st>>>(part, p.nsplit, p.ntiles, m, H, accumulate);
   return hipGetLastError();
 }
 

@@ -16,11 +16,12 @@ inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
 // ---- Hessian ----
 struct HessianPlan {
-  int nb, ntiles, nsplit;
+  bool tr;                 // bf16 with m % 8 == 0: DMA + transposing-read kernel, 256-wide tiles
+  int tile, nb, ntiles, nsplit;
   int64_t tok_per_split;
   size_t ws_bytes;
 };
-HessianPlan hessian_plan(int64_t t, int64_t m);
+HessianPlan hessian_plan(int64_t t, int64_t m, bool bf16);
 hipError_t launch_hessian(const void *X, bool bf16, int64_t t, int64_t m, float *H, bool accumulate,
                           void *ws, const HessianPlan &p, hipStream_t st);
 

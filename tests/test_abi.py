@@ -63,8 +63,9 @@ def test_hessian_validation(lib):
     assert lib.slim_hessian(FAKE, 1, 10, 0, FAKE, 0, FAKE, 1 << 30, None) == -2
     assert lib.slim_hessian(ctypes.c_void_p(4098), 1, 10, 16, FAKE, 0, FAKE, 1 << 30, None) == -7
     assert lib.slim_hessian(FAKE, 1, 10, 16, FAKE, 0, FAKE, 1, None) == -5
-    assert lib.slim_hessian_workspace(4096, 4096) > 0
-    assert lib.slim_hessian_workspace(-1, 4096) == 0
+    assert lib.slim_hessian_workspace(4096, 4096, 1) > 0
+    assert lib.slim_hessian_workspace(-1, 4096, 1) == 0
+    assert lib.slim_hessian_workspace(4096, 4096, 5) == 0
 
 
 def test_salience_validation(lib):

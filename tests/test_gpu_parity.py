@@ -47,6 +47,8 @@ def _case_inputs(T, n, m, dtype, dist="normal", wid=50, avg_bits=2):
     (130, 70, "bf16"),       # width not a multiple of 8: unaligned element path
     (301, 100, "f32"),       # ragged f32
     (1, 33, "f32"),          # single token
+    (20000, 768, "bf16"),    # 256-wide tiles, several token splits
+    (4100, 520, "bf16"),     # ragged 256-tile and ragged last split
 ])
 def test_hessian_parity(slim, T, m, dtype):
     print(f"hessian T={T} m={m} {dtype}", flush=True)
