@@ -70,51 +70,83 @@ __global__ __launch_bounds__(256) void sal_init_kernel(const float *__restrict__
 // Factor the diagonal block of panel p and invert it; writes L_pp into A and
 // (L_pp^-1)^T into TinvT (64 x 64, row k holds column k of the inverse).
 //
-// One sweep of 64 steps with one barrier each.  Step j eliminates column j
-// from the unscaled block (A <- A - a_j a_j^T / a_jj on the trailing part)
-// and applies the same row operation to a right-hand side R that starts as
-// the identity (R_i <- R_i - (a_ij / a_jj) R_j), so that afterwards
-// L_ij = a_ij / sqrt(a_jj) and (L^-1)_jc = R_jc / sqrt(a_jj).  Step j reads
-// only column j of A and row j of R, which step j does not write.
-__global__ __launch_bounds__(256) void chol_diag_kernel(double *__restrict__ A, int64_t mp, int p,
+// One sweep of 64 steps.  Step j eliminates column j from the unscaled block
+// (A <- A - a_j a_j^T / a_jj on the trailing part) and applies the same row
+// operation to a right-hand side R that starts as the identity
+// (R_i <- R_i - (a_ij / a_jj) R_j); afterwards L_ij = a_ij / sqrt(a_jj) and
+// (L^-1)_ij = R_ij / sqrt(a_ii).  Thread t keeps its cells of row t / 8
+// (8 contiguous columns) of both arrays in registers; each step only column j
+// of A and row j of R travel through LDS, read unconditionally as 16-byte
+// broadcasts, and the updates are selects rather than branches.
+constexpr int DCOLS = 8;   // columns per thread in chol_diag (512 threads: 64 rows x 8 column strips)
+
+__global__ __launch_bounds__(512) void chol_diag_kernel(double *__restrict__ A, int64_t mp, int p,
                                                         double *__restrict__ TinvT, int32_t *__restrict__ info) {
-  __shared__ double L[NBK][SP];
-  __shared__ double Rm[NBK][SP];
+  __shared__ __attribute__((aligned(16))) double colj[NBK];   // column j of the working block
+  __shared__ __attribute__((aligned(16))) double rowj[NBK];   // row j of the right-hand side
   __shared__ double piv[NBK];
   const int tid = threadIdx.x;
+  const int oi = tid >> 3, c0 = DCOLS * (tid & 7);   // this thread: row oi, columns c0 .. c0 + 7
   const int64_t k0 = (int64_t)p * NBK;
-  for (int idx = tid; idx < NBK * NBK; idx += 256) {
-    const int i = idx / NBK, j = idx % NBK;
-    L[i][j] = (j <= i) ? A[(k0 + i) * mp + k0 + j] : 0.0;
-    Rm[i][j] = (i == j) ? 1.0 : 0.0;
+  double Lr[DCOLS], Rr[DCOLS];
+#pragma unroll
+  for (int q = 0; q < DCOLS; ++q) {
+    const int c = c0 + q;
+    Lr[q] = (c <= oi) ? A[(k0 + oi) * mp + k0 + c] : 0.0;
+    Rr[q] = (c == oi) ? 1.0 : 0.0;
+  }
+  if (c0 == 0) colj[oi] = Lr[0];
+  if (oi == 0) {
+#pragma unroll
+    for (int q = 0; q < DCOLS; ++q) rowj[c0 + q] = Rr[q];
   }
   __syncthreads();
-  // Thread t owns row i = t / 4 of both arrays, columns (t % 4) + 4 q.
-  const int oi = tid >> 2, oc = tid & 3;
   for (int j = 0; j < NBK; ++j) {
-    double a = L[j][j];
-    if (!(a > 0.0) || !isfinite(a)) a = 1.0;  // reported below; a harmless pivot keeps the sweep finite
-    if (oi > j) {
-      const double f = L[oi][j] / a;
+    double a = colj[j];
+    const bool bad = !(a > 0.0) || !isfinite(a);
+    if (bad) a = 1.0;  // reported below; a harmless pivot keeps the sweep finite
+    // Unconditional broadcast reads (contiguous), then branch-free updates.
+    double cv[DCOLS], rv[DCOLS];
 #pragma unroll
-      for (int q = 0; q < 16; ++q) {
-        const int c = oc + 4 * q;
-        if (c > j && c <= oi) L[oi][c] = L[oi][c] - f * L[c][j];
-        if (c <= j) Rm[oi][c] = Rm[oi][c] - f * Rm[j][c];
-      }
+    for (int q = 0; q < DCOLS; q += 2) {
+      const double2 x = *(const double2 *)&colj[c0 + q];
+      const double2 y = *(const double2 *)&rowj[c0 + q];
+      cv[q] = x.x; cv[q + 1] = x.y;
+      rv[q] = y.x; rv[q + 1] = y.y;
+    }
+    const double f = (oi > j) ? -(colj[oi] / a) : 0.0;
+#pragma unroll
+    for (int q = 0; q < DCOLS; ++q) {
+      const int c = c0 + q;
+      const double nl = __fma_rn(f, cv[q], Lr[q]);
+      const double nr = __fma_rn(f, rv[q], Rr[q]);
+      Lr[q] = (c > j && c <= oi) ? nl : Lr[q];
+      Rr[q] = (c <= j) ? nr : Rr[q];
     }
     if (tid == 0) {
       piv[j] = a;
-      if (!(L[j][j] > 0.0 && isfinite(L[j][j]))) atomicCAS(info, 0, (int)(k0 + j + 1));
+      if (bad) atomicCAS(info, 0, (int)(k0 + j + 1));
+    }
+    __syncthreads();
+    const int jn = j + 1;
+    if (jn < NBK) {
+      double pv = 0.0;
+#pragma unroll
+      for (int q = 0; q < DCOLS; ++q) pv = (c0 + q == jn) ? Lr[q] : pv;
+      if (jn >= c0 && jn < c0 + DCOLS) colj[oi] = pv;
+      if (oi == jn) {
+#pragma unroll
+        for (int q = 0; q < DCOLS; q += 2) *(double2 *)&rowj[c0 + q] = make_double2(Rr[q], Rr[q + 1]);
+      }
     }
     __syncthreads();
   }
-  for (int idx = tid; idx < NBK * NBK; idx += 256) {
-    const int i = idx / NBK, j = idx % NBK;
-    const double sj = sqrt(piv[j]);
-    if (j <= i) A[(k0 + i) * mp + k0 + j] = L[i][j] / sj;     // L_ij = a_ij / sqrt(a_jj)
-    const double si = sqrt(piv[i]);
-    TinvT[j * NBK + i] = (j <= i) ? Rm[i][j] / si : 0.0;     // (L^-1)_ij = R_ij / sqrt(a_ii)
+  const double si = sqrt(piv[oi]);
+#pragma unroll
+  for (int q = 0; q < DCOLS; ++q) {
+    const int c = c0 + q;
+    if (c <= oi) A[(k0 + oi) * mp + k0 + c] = Lr[q] / sqrt(piv[c]);   // L_ij = a_ij / sqrt(a_jj)
+    TinvT[c * NBK + oi] = (c <= oi) ? Rr[q] / si : 0.0;               // (L^-1)_ij = R_ij / sqrt(a_ii)
   }
 }
 
@@ -376,7 +408,7 @@ hipError_t launch_salience(const float *H, int64_t m, double damp, const void *W
   }
   const int NB = (int)(mp / NBK);
   for (int p = 0; p < NB; ++p) {
-    chol_diag_kernel<<<1, 256, 0, st>>>(A, mp, p, TinvT, info);
+    chol_diag_kernel<<<1, 512, 0, st>>>(A, mp, p, TinvT, info);
     const int nrow = NB - p - 1;
     chol_panel_kernel<<<nrow + p + 1, 256, 0, st>>>(A, Z, TinvT, d, mp, p, nrow);
     if (nrow > 0) {
