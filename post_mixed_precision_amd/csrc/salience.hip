@@ -82,8 +82,11 @@ constexpr int DCOLS = 8;   // columns per thread in chol_diag (512 threads: 64 r
 
 __global__ __launch_bounds__(512) void chol_diag_kernel(double *__restrict__ A, int64_t mp, int p,
                                                         double *__restrict__ TinvT, int32_t *__restrict__ info) {
-  __shared__ __attribute__((aligned(16))) double colj[NBK];   // column j of the working block
-  __shared__ __attribute__((aligned(16))) double rowj[NBK];   // row j of the right-hand side
+  // Ping-pong broadcast buffers: step j reads set j & 1 and publishes step
+  // j + 1's column and row into the other set, so one barrier per step keeps
+  // readers and writers apart.
+  __shared__ __attribute__((aligned(16))) double colj[2][NBK];   // column j of the working block
+  __shared__ __attribute__((aligned(16))) double rowj[2][NBK];   // row j of the right-hand side
   __shared__ double piv[NBK];
   const int tid = threadIdx.x;
   const int oi = tid >> 3, c0 = DCOLS * (tid & 7);   // this thread: row oi, columns c0 .. c0 + 7
@@ -95,26 +98,32 @@ __global__ __launch_bounds__(512) void chol_diag_kernel(double *__restrict__ A, 
     Lr[q] = (c <= oi) ? A[(k0 + oi) * mp + k0 + c] : 0.0;
     Rr[q] = (c == oi) ? 1.0 : 0.0;
   }
-  if (c0 == 0) colj[oi] = Lr[0];
+  if (c0 == 0) colj[0][oi] = Lr[0];
   if (oi == 0) {
 #pragma unroll
-    for (int q = 0; q < DCOLS; ++q) rowj[c0 + q] = Rr[q];
+    for (int q = 0; q < DCOLS; ++q) rowj[0][c0 + q] = Rr[q];
   }
   __syncthreads();
   for (int j = 0; j < NBK; ++j) {
-    double a = colj[j];
+    const double *cj = colj[j & 1];
+    const double *rj = rowj[j & 1];
+    double a = cj[j];
     const bool bad = !(a > 0.0) || !isfinite(a);
     if (bad) a = 1.0;  // reported below; a harmless pivot keeps the sweep finite
+    // 1/a: hardware reciprocal refined by two Newton steps (full double accuracy)
+    double inv = __builtin_amdgcn_rcp(a);
+    inv = __fma_rn(inv, __fma_rn(-a, inv, 1.0), inv);
+    inv = __fma_rn(inv, __fma_rn(-a, inv, 1.0), inv);
     // Unconditional broadcast reads (contiguous), then branch-free updates.
     double cv[DCOLS], rv[DCOLS];
 #pragma unroll
     for (int q = 0; q < DCOLS; q += 2) {
-      const double2 x = *(const double2 *)&colj[c0 + q];
-      const double2 y = *(const double2 *)&rowj[c0 + q];
+      const double2 x = *(const double2 *)&cj[c0 + q];
+      const double2 y = *(const double2 *)&rj[c0 + q];
       cv[q] = x.x; cv[q + 1] = x.y;
       rv[q] = y.x; rv[q + 1] = y.y;
     }
-    const double f = (oi > j) ? -(colj[oi] / a) : 0.0;
+    const double f = (oi > j) ? -(cj[oi] * inv) : 0.0;
 #pragma unroll
     for (int q = 0; q < DCOLS; ++q) {
       const int c = c0 + q;
@@ -127,16 +136,17 @@ __global__ __launch_bounds__(512) void chol_diag_kernel(double *__restrict__ A, 
       piv[j] = a;
       if (bad) atomicCAS(info, 0, (int)(k0 + j + 1));
     }
-    __syncthreads();
     const int jn = j + 1;
     if (jn < NBK) {
+      double *cn = colj[jn & 1];
+      double *rn = rowj[jn & 1];
       double pv = 0.0;
 #pragma unroll
       for (int q = 0; q < DCOLS; ++q) pv = (c0 + q == jn) ? Lr[q] : pv;
-      if (jn >= c0 && jn < c0 + DCOLS) colj[oi] = pv;
+      if (jn >= c0 && jn < c0 + DCOLS) cn[oi] = pv;
       if (oi == jn) {
 #pragma unroll
-        for (int q = 0; q < DCOLS; q += 2) *(double2 *)&rowj[c0 + q] = make_double2(Rr[q], Rr[q + 1]);
+        for (int q = 0; q < DCOLS; q += 2) *(double2 *)&rn[c0 + q] = make_double2(Rr[q], Rr[q + 1]);
       }
     }
     __syncthreads();
