@@ -7,7 +7,7 @@
 #include <mutex>
 #include <vector>
 
-#include "../../include/slim.h"
+#include "slim.h"
 #include "kernels.hpp"
 
 namespace {

@@ -147,7 +147,7 @@ __global__ __launch_bounds__(256) void sba_rank_kernel(const double *__restrict_
 template <bool BF16, bool PARTIAL>
 __global__ __launch_bounds__(512, 1) void sba_klgemm_kernel(
     const void *__restrict__ X, const void *__restrict__ W, const void *__restrict__ Wv,
-    const int *__restrict__ order, int64_t tok_base, int64_t tb, int64_t n, int64_t m, int g, int k, int R,
+    const int *__restrict__ order, int64_t tok_base, int64_t tb_len, int64_t n, int64_t m, int g, int k, int R,
     int NC, int NCX, int TT, int c_last, float4 *__restrict__ sq, float2 *__restrict__ sp) {
   constexpr int ESZ = BF16 ? 2 : 4;
   constexpr int KT = BF16 ? 64 : 32;  // K elements per stage (128 bytes per row)
@@ -160,6 +160,9 @@ __global__ __launch_bounds__(512, 1) void sba_klgemm_kernel(
   __shared__ __attribute__((aligned(16))) unsigned char lds1[STAGE_BYTES];
   __shared__ int s_order[MAXK];
   __shared__ int s_rows_ok;   // valid outputs in this chunk (read in the epilogue, never hoisted)
+  // Per-token statistics of the two 64-output halves of the tile, merged in the epilogue.
+  __shared__ float4 xq[2][SBT];   // (max yhat, sum exp, S, -) per half
+  __shared__ float2 xp[2][SBT];   // (max y, sum exp) per half
 
   // XCD-aware id: XCD x = id % 8 owns complete output chunks [x*NCX, x*NCX+NCX).
   int c, tt;
@@ -192,7 +195,7 @@ __global__ __launch_bounds__(512, 1) void sba_klgemm_kernel(
   // variants (one resource, variant v at v * vstride) and the token rows.
   const uint32_t rowb = (uint32_t)(m * ESZ);          // bytes per row of W / X
   const int a_rows_ok = (int)min((int64_t)SBO, n - out0);
-  const int x_rows_ok = (int)min((int64_t)SBT, tb - tok0);
+  const int x_rows_ok = (int)min((int64_t)SBT, tb_len - tok0);
   const uint32_t vstride = (uint32_t)(n * rowb);
   const __amdgpu_buffer_rsrc_t rW = __builtin_amdgcn_make_buffer_rsrc(
       (void *)((const unsigned char *)W + out0 * rowb), (short)0, (int)(a_rows_ok * rowb), RSRC_FLAGS);
@@ -259,126 +262,191 @@ __global__ __launch_bounds__(512, 1) void sba_klgemm_kernel(
       accQ[b][v] = 0.0f;
     }
 
-  // Fragment row r (A rows blk*32 + lane%32, token rows 256 + wave*32 + lane%32) has
-  // (r >> 1) & 7 == ((lane & 31) >> 1) & 7.
+  // Wave tile: 64 outputs (half wo) x 64 tokens (quarter wt) = 2 x 2 MFMA blocks,
+  // so one K step reads 4 weight and 2 token fragments for 8 MFMAs.
+  // Fragment row r (all block bases are multiples of 32) has (r >> 1) & 7 == ((lane & 31) >> 1) & 7.
+  const int wo = wave & 1, wt = wave >> 1;
   const int sw = (lane >> 1) & 7;
   auto compute_main = [&](const unsigned char *L) __attribute__((always_inline)) {
-    const unsigned char *Bt = L + (2 * SBO + wave * 32 + (lane & 31)) * SBP;
-    const unsigned char *A0 = L + (lane & 31) * SBP;
-    const unsigned char *A1 = L + (SBO + (lane & 31)) * SBP;
+    const unsigned char *Bt = L + (2 * SBO + wt * 64 + (lane & 31)) * SBP;
+    const unsigned char *A0 = L + (wo * 64 + (lane & 31)) * SBP;
+    const unsigned char *A1 = L + (SBO + wo * 64 + (lane & 31)) * SBP;
     if (BF16) {
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk) {
         const int off = ((2 * kk + (lane >> 5)) ^ sw) * 16;
-        const uint4 b = *(const uint4 *)(Bt + off);
+        uint4 b[2], a0[2], a1[2];
 #pragma unroll
-        for (int blk = 0; blk < 4; ++blk) {
-          accY[blk] = mfma_bf16(*(const uint4 *)(A0 + blk * 32 * SBP + off), b, accY[blk]);
-          accQ[blk] = mfma_bf16(*(const uint4 *)(A1 + blk * 32 * SBP + off), b, accQ[blk]);
+        for (int i = 0; i < 2; ++i) {
+          b[i] = *(const uint4 *)(Bt + i * 32 * SBP + off);
+          a0[i] = *(const uint4 *)(A0 + i * 32 * SBP + off);
+          a1[i] = *(const uint4 *)(A1 + i * 32 * SBP + off);
         }
+#pragma unroll
+        for (int ob = 0; ob < 2; ++ob)
+#pragma unroll
+          for (int tb = 0; tb < 2; ++tb) {
+            accY[ob * 2 + tb] = mfma_bf16(a0[ob], b[tb], accY[ob * 2 + tb]);
+            accQ[ob * 2 + tb] = mfma_bf16(a1[ob], b[tb], accQ[ob * 2 + tb]);
+          }
       }
     } else {
 #pragma unroll 4
       for (int kk = 0; kk < 16; ++kk) {
         const int e = 2 * kk + (lane >> 5);
         const int off = ((e >> 2) ^ sw) * 16 + (e & 3) * 4;
-        const float b = *(const float *)(Bt + off);
+        float b[2], a0[2], a1[2];
 #pragma unroll
-        for (int blk = 0; blk < 4; ++blk) {
-          accY[blk] = mfma_f32(*(const float *)(A0 + blk * 32 * SBP + off), b, accY[blk]);
-          accQ[blk] = mfma_f32(*(const float *)(A1 + blk * 32 * SBP + off), b, accQ[blk]);
+        for (int i = 0; i < 2; ++i) {
+          b[i] = *(const float *)(Bt + i * 32 * SBP + off);
+          a0[i] = *(const float *)(A0 + i * 32 * SBP + off);
+          a1[i] = *(const float *)(A1 + i * 32 * SBP + off);
         }
+#pragma unroll
+        for (int ob = 0; ob < 2; ++ob)
+#pragma unroll
+          for (int tb = 0; tb < 2; ++tb) {
+            accY[ob * 2 + tb] = mfma_f32(a0[ob], b[tb], accY[ob * 2 + tb]);
+            accQ[ob * 2 + tb] = mfma_f32(a1[ob], b[tb], accQ[ob * 2 + tb]);
+          }
       }
     }
   };
   auto compute_update = [&](const unsigned char *L) __attribute__((always_inline)) {
-    const unsigned char *Bt = L + (2 * SBO + wave * 32 + (lane & 31)) * SBP;
-    const unsigned char *A0 = L + (lane & 31) * SBP;
-    const unsigned char *A1 = L + (SBO + (lane & 31)) * SBP;
+    const unsigned char *Bt = L + (2 * SBO + wt * 64 + (lane & 31)) * SBP;
+    const unsigned char *A0 = L + (wo * 64 + (lane & 31)) * SBP;
+    const unsigned char *A1 = L + (SBO + wo * 64 + (lane & 31)) * SBP;
     if (BF16) {
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk) {
         const int off = ((2 * kk + (lane >> 5)) ^ sw) * 16;
-        const uint4 b = *(const uint4 *)(Bt + off);
+        uint4 b[2], a0[2], a1[2];
 #pragma unroll
-        for (int blk = 0; blk < 4; ++blk) {
-          uint4 a1 = *(const uint4 *)(A1 + blk * 32 * SBP + off);
-          a1.x ^= 0x80008000u; a1.y ^= 0x80008000u; a1.z ^= 0x80008000u; a1.w ^= 0x80008000u;
-          accQ[blk] = mfma_bf16(*(const uint4 *)(A0 + blk * 32 * SBP + off), b, accQ[blk]);
-          accQ[blk] = mfma_bf16(a1, b, accQ[blk]);
+        for (int i = 0; i < 2; ++i) {
+          b[i] = *(const uint4 *)(Bt + i * 32 * SBP + off);
+          a0[i] = *(const uint4 *)(A0 + i * 32 * SBP + off);
+          a1[i] = *(const uint4 *)(A1 + i * 32 * SBP + off);
+          a1[i].x ^= 0x80008000u; a1[i].y ^= 0x80008000u; a1[i].z ^= 0x80008000u; a1[i].w ^= 0x80008000u;
         }
+#pragma unroll
+        for (int ob = 0; ob < 2; ++ob)
+#pragma unroll
+          for (int tb = 0; tb < 2; ++tb) {
+            accQ[ob * 2 + tb] = mfma_bf16(a0[ob], b[tb], accQ[ob * 2 + tb]);
+            accQ[ob * 2 + tb] = mfma_bf16(a1[ob], b[tb], accQ[ob * 2 + tb]);
+          }
       }
     } else {
 #pragma unroll 4
       for (int kk = 0; kk < 16; ++kk) {
         const int e = 2 * kk + (lane >> 5);
         const int off = ((e >> 2) ^ sw) * 16 + (e & 3) * 4;
-        const float b = *(const float *)(Bt + off);
+        float b[2], a0[2], a1[2];
 #pragma unroll
-        for (int blk = 0; blk < 4; ++blk) {
-          accQ[blk] = mfma_f32(*(const float *)(A0 + blk * 32 * SBP + off), b, accQ[blk]);
-          accQ[blk] = mfma_f32(-*(const float *)(A1 + blk * 32 * SBP + off), b, accQ[blk]);
+        for (int i = 0; i < 2; ++i) {
+          b[i] = *(const float *)(Bt + i * 32 * SBP + off);
+          a0[i] = *(const float *)(A0 + i * 32 * SBP + off);
+          a1[i] = -*(const float *)(A1 + i * 32 * SBP + off);
         }
+#pragma unroll
+        for (int ob = 0; ob < 2; ++ob)
+#pragma unroll
+          for (int tb = 0; tb < 2; ++tb) {
+            accQ[ob * 2 + tb] = mfma_f32(a0[ob], b[tb], accQ[ob * 2 + tb]);
+            accQ[ob * 2 + tb] = mfma_f32(a1[ob], b[tb], accQ[ob * 2 + tb]);
+          }
       }
     }
   };
 
-  // Per-wave token statistics; lane l and l^32 hold the same token (l % 32).
-  const int64_t tcol = tok0 + wave * 32 + (lane & 31);
-  const bool tvalid = tcol < tb;
-  float sy_tok = 0.0f;
+  // Per-token statistics.  Lane l holds, for token blocks tb = 0, 1, the token
+  // tok0 + wt*64 + tb*32 + l%32 and 32 of the wave's 64 outputs (lanes l and
+  // l^32 hold the other 32).  Each half wo first reduces over its 64 outputs
+  // relative to its own maxima; the halves are then merged through LDS:
+  //   M = max(m0, m1), Z = sum_h z_h e^{m_h - M}, S = sum_h S_h e^{m_h - M}.
+  float m_own[2] = {-INFINITY, -INFINITY}, sy_own[2] = {0.0f, 0.0f};
   auto epilogue = [&](int r) __attribute__((always_inline)) {
-    // Output row of accumulator element (blk, v) is blk*32 + acc32_row(v, lane).
-    const int lim = PARTIAL ? s_rows_ok - 4 * (lane >> 5) : SBO;
-    if (r == 0) {
-      float mx = -INFINITY;
+    // output row inside the half of accumulator element (ob, v): ob*32 + acc32_row(v, lane)
+    const int lim = PARTIAL ? s_rows_ok - wo * 64 - 4 * (lane >> 5) : 64;
+    float pz[2] = {0.0f, 0.0f}, qm[2], qz[2], qs[2];
 #pragma unroll
-      for (int blk = 0; blk < 4; ++blk)
+    for (int tb = 0; tb < 2; ++tb) {
+      if (r == 0) {
+        float mx = -INFINITY;
+#pragma unroll
+        for (int ob = 0; ob < 2; ++ob)
+#pragma unroll
+          for (int v = 0; v < 16; ++v)
+            if (!PARTIAL || ob * 32 + 8 * (v >> 2) + (v & 3) < lim) mx = fmaxf(mx, accY[ob * 2 + tb][v]);
+        mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+        float z = 0.0f, sy = 0.0f;
+#pragma unroll
+        for (int ob = 0; ob < 2; ++ob)
+#pragma unroll
+          for (int v = 0; v < 16; ++v) {
+            const float y = accY[ob * 2 + tb][v];
+            float e = 0.0f;
+            if (!PARTIAL || ob * 32 + 8 * (v >> 2) + (v & 3) < lim) e = __expf(y - mx);
+            accY[ob * 2 + tb][v] = e;
+            z += e;
+            sy += e * y;
+          }
+        z += __shfl_xor(z, 32, 64);
+        sy += __shfl_xor(sy, 32, 64);
+        m_own[tb] = mx;
+        sy_own[tb] = sy;
+        pz[tb] = z;
+      }
+      float mq = -INFINITY;
+#pragma unroll
+      for (int ob = 0; ob < 2; ++ob)
 #pragma unroll
         for (int v = 0; v < 16; ++v)
-          if (!PARTIAL || blk * 32 + 8 * (v >> 2) + (v & 3) < lim) mx = fmaxf(mx, accY[blk][v]);
-      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-      float z = 0.0f, sy = 0.0f;
+          if (!PARTIAL || ob * 32 + 8 * (v >> 2) + (v & 3) < lim) mq = fmaxf(mq, accQ[ob * 2 + tb][v]);
+      mq = fmaxf(mq, __shfl_xor(mq, 32, 64));
+      float zq = 0.0f, se = 0.0f;
 #pragma unroll
-      for (int blk = 0; blk < 4; ++blk)
+      for (int ob = 0; ob < 2; ++ob)
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
-          const float y = accY[blk][v];
-          float e = 0.0f;
-          if (!PARTIAL || blk * 32 + 8 * (v >> 2) + (v & 3) < lim) e = __expf(y - mx);
-          accY[blk][v] = e;
-          z += e;
-          sy += e * y;
+          const float yh = accQ[ob * 2 + tb][v];
+          if (!PARTIAL || ob * 32 + 8 * (v >> 2) + (v & 3) < lim) zq += __expf(yh - mq);
+          se += accY[ob * 2 + tb][v] * yh;
         }
-      z += __shfl_xor(z, 32, 64);
-      sy += __shfl_xor(sy, 32, 64);
-      sy_tok = sy;
-      if (lane < 32 && tvalid) sp[(int64_t)c * tb + tcol] = make_float2(mx, z);
+      zq += __shfl_xor(zq, 32, 64);
+      se += __shfl_xor(se, 32, 64);
+      qm[tb] = mq;
+      qz[tb] = zq;
+      qs[tb] = sy_own[tb] - se;
     }
-    float mq = -INFINITY;
+    if (lane < 32) {
 #pragma unroll
-    for (int blk = 0; blk < 4; ++blk)
-#pragma unroll
-      for (int v = 0; v < 16; ++v)
-        if (!PARTIAL || blk * 32 + 8 * (v >> 2) + (v & 3) < lim) mq = fmaxf(mq, accQ[blk][v]);
-    mq = fmaxf(mq, __shfl_xor(mq, 32, 64));
-    float zq = 0.0f, se = 0.0f;
-#pragma unroll
-    for (int blk = 0; blk < 4; ++blk)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const float yh = accQ[blk][v];
-        if (!PARTIAL || blk * 32 + 8 * (v >> 2) + (v & 3) < lim) zq += __expf(yh - mq);
-        se += accY[blk][v] * yh;
+      for (int tb = 0; tb < 2; ++tb) {
+        const int tok = wt * 64 + tb * 32 + lane;
+        xq[wo][tok] = make_float4(qm[tb], qz[tb], qs[tb], 0.0f);
+        if (r == 0) xp[wo][tok] = make_float2(m_own[tb], pz[tb]);
       }
-    zq += __shfl_xor(zq, 32, 64);
-    se += __shfl_xor(se, 32, 64);
-    if (lane < 32 && tvalid) sq[((int64_t)r * NC + c) * tb + tcol] = make_float4(mq, zq, sy_tok - se, 0.0f);
+    }
+    __syncthreads();
+    if (wo == 0 && lane < 32) {
+#pragma unroll
+      for (int tb = 0; tb < 2; ++tb) {
+        const int tok = wt * 64 + tb * 32 + lane;
+        const int64_t tg = tok0 + tok;
+        if (tg < tb_len) {
+          const float2 p0 = xp[0][tok], p1 = xp[1][tok];
+          const float M = fmaxf(p0.x, p1.x);
+          const float a0 = __expf(p0.x - M), a1 = __expf(p1.x - M);
+          if (r == 0) sp[(int64_t)c * tb_len + tg] = make_float2(M, p0.y * a0 + p1.y * a1);
+          const float4 q0 = xq[0][tok], q1 = xq[1][tok];
+          const float Mq = fmaxf(q0.x, q1.x);
+          const float Zq = q0.y * __expf(q0.x - Mq) + q1.y * __expf(q1.x - Mq);
+          sq[((int64_t)r * NC + c) * tb_len + tg] = make_float4(Mq, Zq, q0.z * a0 + q1.z * a1, 0.0f);
+        }
+      }
+    }
   };
 
-  // Phase 1: Y and Yhat_0 over K = m.  Phase 2: for every step r, its 2g/KT
-  // slab-update stages, then the step's statistics.  The stage index runs on
-  // across both phases; the DMA of stage st+1 is issued before stage st computes.
   // Stage st lives in lds0 when st is even and in lds1 when odd.  Both loops
   // are unrolled by two so every stage names its buffers statically.
   auto main_stage = [&](int st, const unsigned char *cur, unsigned char *nxt) __attribute__((always_inline)) {
