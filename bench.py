@@ -38,6 +38,49 @@ def _dev(a, torch):
     return torch.from_numpy(a).to("cuda:0")
 
 
+# Sources that make up the SBA GEMM + KL kernel: HBM traffic measured with
+# counters is only reported while these are byte-identical to what was profiled.
+SBA_SOURCES = ("post_mixed_precision_amd/csrc/sba.hip", "post_mixed_precision_amd/csrc/common.hpp",
+               "post_mixed_precision_amd/csrc/kernels.hpp")
+
+
+def sba_source_digest() -> str:
+    """Digest of the kernel's code with comments and blank space removed."""
+    import hashlib
+    import re
+    h = hashlib.sha256()
+    for rel in SBA_SOURCES:
+        with open(os.path.join(ROOT, rel), encoding="utf-8") as f:
+            src = f.read()
+        src = re.sub(r"/\*.*?\*/", " ", src, flags=re.S)
+        src = re.sub(r"//[^\n]*", " ", src)
+        h.update(" ".join(src.split()).encode())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload: str, linear: str, group: int):
+    """HBM bytes per launch of the SBA kernel from the committed counter summary
+    (FETCH_SIZE and WRITE_SIZE runs, scaled by a plain copy of known size), or
+    None when there is no summary for this workload or the kernel has changed."""
+    path = os.path.join(ROOT, "profiles", f"sba_klgemm.{workload}.traffic.txt")
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    for line in open(path):
+        if ":" in line and not line.startswith((" ", "#", "\t")):
+            key, _, val = line.partition(":")
+            kv[key.strip()] = val.strip()
+    try:
+        if (kv.get("source_digest") != sba_source_digest() or kv.get("linear") != linear
+                or int(kv.get("group", -1)) != group):
+            return None
+        return {"fetch_bytes": float(kv["fetch_bytes_per_launch"]),
+                "write_bytes": float(kv["write_bytes_per_launch"]),
+                "copy_scale": float(kv["copy_scale"]), "source_digest": kv["source_digest"]}
+    except (KeyError, ValueError):
+        return None
+
+
 def run_step(slim, X, W, group, N, ev=None):
     """One pass of the whole path; optional event list records stage boundaries."""
     def mark(i):
@@ -57,7 +100,7 @@ def run_step(slim, X, W, group, N, ev=None):
     return info, pinfo, rs, kl
 
 
-def cpu_baseline(wl, lin_idx, group, N, Xh, Wh, budget_s=20.0):
+def cpu_baseline(wl, lin_idx, group, N, Xh, Wh):
     """The oracle as it stands, on a bounded sample; stage costs scaled to the layer."""
     import oracle
     try:
@@ -68,19 +111,17 @@ def cpu_baseline(wl, lin_idx, group, N, Xh, Wh, budget_s=20.0):
     lin = wl.linears[lin_idx]
     n, m, T = lin.n, lin.m, wl.tokens
     storage = wl.dtype
-    t_h = 2048
-    t0 = time.perf_counter()
-    oracle.hessian(Xh[:t_h])
-    s_hess = (time.perf_counter() - t0) * T / t_h
-    # salience needs a full-width H; the sample's H stands in (same cost)
+    t_h = min(T, 16384)
     t0 = time.perf_counter()
     H = oracle.hessian(Xh[:t_h])
     t_hsmp = time.perf_counter() - t0
+    s_hess = t_hsmp * T / t_h
+    # salience needs a full-width H; the sample's H stands in (same cost)
     t0 = time.perf_counter()
     d32, S, info = oracle.salience(H, Wh, group, 0.01)
     s_sal = time.perf_counter() - t0
     # SBA: per-token cost of the scan on a token slice
-    t_s = 384
+    t_s = min(T, 16384)
     t0 = time.perf_counter()
     bits, kl, rs = oracle.sba_search(Xh[:t_s], Wh, S, N, group, storage)
     s_sba_slice = time.perf_counter() - t0
@@ -91,7 +132,7 @@ def cpu_baseline(wl, lin_idx, group, N, Xh, Wh, budget_s=20.0):
     per_tok = max(s_sba_slice - 3 * s_trial, 1e-9) / t_s
     s_sba = per_tok * T + 3 * s_trial
     # SQC on a row sample
-    rows = min(n, 128)
+    rows = min(n, 1024)
     t0 = time.perf_counter()
     sq = oracle.sqc_calibrate(Wh, bits, d32, group, 0.1, 50, rows=np.arange(rows))
     s_sqc = (time.perf_counter() - t0) * n / rows
@@ -103,13 +144,12 @@ def cpu_baseline(wl, lin_idx, group, N, Xh, Wh, budget_s=20.0):
     total = s_hess + s_sal + s_sba + s_sqc + s_pack
     return {
         "value": n * m / 1e6 / total, "unit": "Mparams/s", "cores": int(threads), "kind": "oracle",
-        "sample": (f"Hessian on {t_h} tokens (x{T // t_h}); salience at full width {m}; SBA scan over all "
+        "sample": (f"Hessian on {t_h} tokens (x{T / t_h:g}); salience at full width {m}; SBA scan over all "
                    f"{k // 2 + 1} steps on {t_s} tokens (per-token cost x{T}) plus 3 trial quantizations; "
                    f"SQC on {rows} of {n} rows (x{n / rows:.0f}); packing in full"),
         "seconds_extrapolated": {"hessian": s_hess, "salience": s_sal, "sba": s_sba, "sqc": s_sqc,
                                  "pack": s_pack, "total": total},
-        "seconds_measured": round(s_hess * t_h / T + t_hsmp + s_sal + s_sba_slice + s_trial
-                                  + s_sqc * rows / n + s_pack, 2),
+        "seconds_measured": round(t_hsmp + s_sal + s_sba_slice + s_trial + s_sqc * rows / n + s_pack, 2),
     }
 
 
@@ -122,10 +162,12 @@ def main():
     ap.add_argument("--linear", type=int, default=0)
     ap.add_argument("--group", type=int, default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="run one plain device copy of this many MiB before the steps (counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU: this path runs one layer per GPU and the build targets "
-              "single-GPU boxes; run with --gpus 1 (sharding is described in DESIGN.md).", file=sys.stderr)
+        print("bench.py measures one GPU only: the quantizer runs one layer on one device here, and "
+              "multi-GPU figures are not produced; run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
 
     import torch
@@ -146,6 +188,17 @@ def main():
     Wh = synth.make_w(wl, args.linear)
     X, W = _dev(Xh, torch), _dev(Wh, torch)
     torch.cuda.synchronize()
+    if args.copy_probe_mib > 0:
+        # A plain copy of known size: its FETCH_SIZE / WRITE_SIZE in a counter
+        # run calibrate the counters' units against bytes actually moved.
+        nbytes = args.copy_probe_mib << 20
+        src = torch.ones(nbytes, dtype=torch.uint8, device="cuda:0")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        print(f"# copy probe: {nbytes} bytes read and written", file=sys.stderr, flush=True)
+        del src, dst
 
     for i in range(args.warmup):
         info, pinfo, rs, kl = run_step(slim, X, W, group, N)
@@ -202,6 +255,16 @@ def main():
                                 "sqc_calibrate": round(qms / args.steps, 3),
                                 "pack_planes": round(pms / args.steps, 3)},
     }
+    tr = measured_traffic(args.workload, lin.name, group)
+    if tr is not None:
+        out["roofline"]["traffic"] = round(tr["fetch_bytes"] + tr["write_bytes"])
+        out["roofline"]["traffic_detail"] = {
+            "unit": "bytes per launch", "fetch": round(tr["fetch_bytes"]), "write": round(tr["write_bytes"]),
+            "copy_scale": tr["copy_scale"], "source_digest": tr["source_digest"],
+            "algorithmic_bytes": 2 * (T * m + 4 * n * m) / launches_per_step}
+    out["roofline"]["source_digest"] = sba_source_digest()
+    from post_mixed_precision_amd import _lib as _slim_lib
+    out["library_built_from_tree"] = _slim_lib.library_is_current()
     hess_flops = T * m * (m + 1)
     if hl:
         out["roofline_other"] = {

@@ -74,8 +74,8 @@ const char *slim_status_string(int status);
 int slim_last_hip_error(void);
 
 /* ------------------------------------------------------------------------
- * Hessian proxy (component one: "the Hessian is approximated from the
- * calibration activations, no back-propagation").
+ * Hessian proxy (rkmt.cn digest, "core design", component one: the Hessian
+ * is estimated from the calibration activations alone, without gradients).
  *
  *   H[m, m] (+)= 2 * X^T X,   X[t, m] token-major in dtype xdt.
  *

@@ -61,6 +61,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         import torch  # noqa: F401  (loads torch's HIP runtime first: same soname, one runtime)
     except Exception:  # pragma: no cover
         pass
+    _warn_if_stale(path)
     lib = ctypes.CDLL(path)
     for name, (res, args) in _SIGS.items():
         fn = getattr(lib, name)
@@ -68,6 +69,23 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         fn.argtypes = args
     _lib = lib
     return lib
+
+
+def library_is_current(path: str = LIB_PATH) -> bool:
+    """True when the library was built from the sources now in the tree."""
+    from . import build
+    try:
+        with open(path + ".sources") as f:
+            return f.read().strip() == build.source_digest()
+    except OSError:
+        return False
+
+
+def _warn_if_stale(path: str):
+    if not library_is_current(path):
+        import sys
+        print(f"warning: {path} was not built from the current csrc/ and include/ sources; "
+              "rebuild with post_mixed_precision_amd.build.build()", file=sys.stderr, flush=True)
 
 
 def check(status: int, what: str):

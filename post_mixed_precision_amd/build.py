@@ -21,6 +21,7 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 OBJDIR = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libslim.so")
+STAMP = LIB + ".sources"     # digest of the sources the library was built from
 ROCM = os.environ.get("ROCM_PATH", "/opt/rocm")
 
 FLAGS = [
@@ -37,9 +38,23 @@ def _hipcc() -> str:
     return p
 
 
+def source_digest() -> str:
+    """sha256 over every file the library is compiled from (csrc/ and include/)."""
+    import hashlib
+    h = hashlib.sha256()
+    files = sorted(glob.glob(os.path.join(CSRC, "*"))) + sorted(glob.glob(os.path.join(INCLUDE, "*.h")))
+    for path in files:
+        if os.path.isfile(path):
+            h.update(os.path.basename(path).encode())
+            with open(path, "rb") as f:
+                h.update(f.read())
+    return h.hexdigest()
+
+
 def build(verbose: bool = False, jobs: int = 8) -> str:
     """Compile every csrc/*.hip for gfx950 and link libslim.so; returns its path."""
     hipcc = _hipcc()
+    digest = source_digest()     # taken before compiling: the stamp names what was compiled
     os.makedirs(OBJDIR, exist_ok=True)
     srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
 
@@ -64,6 +79,8 @@ def build(verbose: bool = False, jobs: int = 8) -> str:
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stdout}{r.stderr}")
     os.replace(tmp, LIB)
+    with open(STAMP, "w") as f:
+        f.write(digest + "\n")
     return LIB
 
 

@@ -16,9 +16,10 @@
 // Operands stay exact (bf16 trial weights and their negations), and one
 // workgroup keeps its 128-output x 256-token tile of Yhat in MFMA
 // accumulators through the whole scan: Y and Yhat_0 over K = m, then 4g more
-// K columns per step.  Each wave owns 32 tokens x all 128 outputs of the
-// tile, so the softmax statistics of a token are reduced inside the wave
-// (16 values in-lane, then one lane swap) and never cross LDS.
+// K columns per step.  Each of the 8 waves owns 64 outputs x 64 tokens of the
+// tile (2 x 2 blocks of 32 x 32); a token's softmax statistics over its wave's
+// 64 outputs are reduced in registers and lane swaps, and the two halves of
+// the tile are merged once per step through a small LDS exchange.
 //
 // KL per token from chunk statistics.  With p = softmax(y), q = softmax(yhat):
 //     KL_t = sum_j p_j (y_j - yhat_j) - LSE(y) + LSE(yhat).
@@ -39,7 +40,7 @@
 namespace slim {
 
 constexpr int SBO = 128;    // outputs per workgroup
-constexpr int SBT = 256;    // tokens per workgroup (8 waves x 32)
+constexpr int SBT = 256;    // tokens per workgroup (4 wave columns x 64)
 constexpr int SBP = 128;    // LDS row pitch in bytes (16-byte slots XOR-swizzled by row & 7)
 constexpr int MAXK = 2048;  // most groups per row supported by the search kernels
 constexpr int STAGE_BYTES = (2 * SBO + SBT) * SBP;
