@@ -1,0 +1,285 @@
+"""Parity at the full layer sizes, through the C ABI.
+
+The benchmark's layer (W 4096 x 4096 bf16, 262144 calibration tokens) runs
+here exactly as the benchmark launches it: whole-layer calls on
+device-resident inputs.  The oracle cannot redo such a layer in seconds, so
+at these sizes the HIP results are checked
+
+* on sampled outputs the oracle computes one by one: Hessian entries on a
+  spread of columns over all tokens; SQC on sampled rows of the whole weight;
+  the SBA scan on token slices of the full-width layer (the scan's objective
+  is a mean over tokens, so every token slice is a complete instance);
+* through properties that hold at any size: H exactly symmetric with
+  trace(H) = 2 ||X||_F^2; the SBA balance |G_{N-1}| = |G_{N+1}| = r* with
+  sum(bits) = k N, r* the first argmin of the returned KL curve, and the
+  full-token KL curve equal to the mean of the curves of a split of the
+  tokens (each token's KL does not depend on the launch it is computed in);
+* at the real widths of the other layer shapes (11008-wide MLP halves, group
+  sizes 64 and 32, the 13B and 70B MLPs): Hessian and salience at full width
+  from token slices, SQC on sampled rows, packing of the whole layer, the SBA
+  scan on token slices, and the 70B layer's SBA at all 262144 tokens (token
+  batches of the statistics workspace) on the properties above.
+
+Tolerances are those of the small-size parity tests.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from gpu_helpers import dev, host, hessian_err, rel_err, kl_near_tie, compare_sqc
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(scope="module")
+def slim():
+    import post_mixed_precision_amd as s
+    s.load_library()
+    return s
+
+
+def _sync():
+    torch.cuda.synchronize()
+
+
+def _say(msg):
+    print(msg, flush=True)
+
+
+# -------------------------------------------------------------- the benchmark's layer
+@pytest.fixture(scope="module")
+def attn():
+    wl = synth.WORKLOADS["llama7b-attn-4096"]
+    _say("generating the 4096 x 4096 layer and 262144 x 4096 tokens")
+    X = synth.make_x(wl, 4096)
+    W = synth.make_w(wl, 0)
+    return wl, X, W
+
+
+@pytest.fixture(scope="module")
+def attn_oracle(attn):
+    """The oracle's H (first 8192 tokens), d and group salience at full width."""
+    wl, X, W = attn
+    H = oracle.hessian(X[:8192]).astype(np.float32)
+    d, S, info = oracle.salience(H, W, 128, 0.01)
+    assert info == 0
+    return H, d, S
+
+
+def _sample_columns(m, rng, extra=()):
+    cols = {0, 1, 31, 32, 127, 128, 255, 256, m // 2, m - 257, m - 256, m - 2, m - 1, *extra}
+    cols |= set(rng.choice(m, 24, replace=False).tolist())
+    return np.array(sorted(c for c in cols if 0 <= c < m))
+
+
+def test_attn_hessian_full_tokens(slim, attn):
+    wl, X, W = attn
+    T, m = X.shape
+    _say(f"hessian T={T} m={m} bf16 (full layer)")
+    Hg = host(slim.hessian(dev(X, torch, True)))
+    _sync()
+    assert np.array_equal(Hg, Hg.T)
+    ch, _ = synth.outlier_layout(wl, m)
+    cols = _sample_columns(m, np.random.default_rng(7), extra=(int(ch[0]), int(ch[len(ch) // 2]), int(ch[-1])))
+    Ho = oracle.hessian(X[:, cols])                      # 2 X_c^T X_c over all tokens, float64
+    assert hessian_err(Hg[np.ix_(cols, cols)], Ho) <= 1e-3
+    # trace(H) = 2 ||X||_F^2 over all tokens and columns
+    fro = 0.0
+    for t0 in range(0, T, 16384):
+        xs = synth.as_float(X[t0:t0 + 16384]).astype(np.float64)
+        fro += float(np.einsum("ij,ij->", xs, xs))
+    tr = float(np.trace(Hg.astype(np.float64)))
+    assert abs(tr - 2.0 * fro) <= 1e-3 * 2.0 * fro
+
+
+def test_attn_salience_full_width(slim, attn, attn_oracle):
+    wl, X, W = attn
+    H, d_o, S_o = attn_oracle
+    _say("salience m=4096 n=4096 g=128 (full layer)")
+    hinv, gsal, info, _ = slim.salience(dev(H, torch, False), dev(W, torch, True), 128, 0.01)
+    _sync()
+    assert int(info.item()) == 0
+    assert rel_err(host(hinv), d_o) <= 1e-3
+    assert rel_err(host(gsal), S_o) <= 1e-3
+    np.testing.assert_array_equal(np.argsort(-host(gsal), kind="stable"), oracle.rank_groups(S_o))
+
+
+def _sba(slim, X, W, S, g, N, bf16=True):
+    bits, kl, rs = slim.sba_search(dev(X, torch, bf16) if isinstance(X, np.ndarray) else X,
+                                   dev(W, torch, bf16) if isinstance(W, np.ndarray) else W,
+                                   torch.from_numpy(np.asarray(S, dtype=np.float64)).to("cuda:0"), g, N)
+    _sync()
+    return host(bits).astype(int), host(kl), int(host(rs)[0])
+
+
+def _check_sba_properties(bits, kl, rs, S, N):
+    k = len(S)
+    assert len(kl) == k // 2 + 1
+    assert np.all(np.isfinite(kl)) and np.all(kl >= 0.0)
+    assert rs == int(np.argmin(kl))                      # first argmin
+    assert (bits == N + 1).sum() == (bits == N - 1).sum() == rs and bits.sum() == k * N
+    np.testing.assert_array_equal(bits, oracle.allocation(oracle.rank_groups(S), rs, N))
+
+
+def test_attn_sba_full_tokens(slim, attn, attn_oracle):
+    wl, X, W = attn
+    _, _, S = attn_oracle
+    T = X.shape[0]
+    _say(f"sba T={T} n=4096 m=4096 g=128 N=2 (full layer) and its two token halves")
+    Xd, Wd = dev(X, torch, True), dev(W, torch, True)
+    bits, kl, rs = _sba(slim, Xd, Wd, S, 128, 2)
+    _check_sba_properties(bits, kl, rs, S, 2)
+    assert kl[0] > 0.0
+    h = T // 2
+    _, kl_a, _ = _sba(slim, Xd[:h], Wd, S, 128, 2)
+    _, kl_b, _ = _sba(slim, Xd[h:], Wd, S, 128, 2)
+    np.testing.assert_allclose(kl, 0.5 * (kl_a + kl_b), rtol=1e-9, atol=0)
+
+
+def _sba_slice_vs_oracle(slim, Xs, W, S, g, N):
+    bits, kl, rs = _sba(slim, Xs, W, S, g, N)
+    bits_o, kl_o, rs_o = oracle.sba_search(Xs, W, S, N, g, "bf16")
+    err = float(np.max(np.abs(kl - kl_o) / np.maximum(np.abs(kl_o), 1e-12)))
+    assert err <= 1e-3, (err, kl, kl_o)
+    if not kl_near_tie(kl_o):
+        assert rs == rs_o
+        np.testing.assert_array_equal(bits, bits_o)
+    _check_sba_properties(bits, kl, rs, S, N)
+
+
+@pytest.mark.parametrize("t0,t1", [(0, 512), (262144 - 300, 262144)])
+def test_attn_sba_token_slice_vs_oracle(slim, attn, attn_oracle, t0, t1):
+    wl, X, W = attn
+    _, _, S = attn_oracle
+    _say(f"sba tokens [{t0}, {t1}) of the full-width layer vs oracle")
+    _sba_slice_vs_oracle(slim, X[t0:t1], W, S, 128, 2)
+
+
+def _sample_rows(n, rng, count):
+    rows = {0, 1, 63, 64, 127, 128, n // 2, n - 129, n - 128, n - 2, n - 1}
+    rows |= set(rng.choice(n, count, replace=False).tolist())
+    return np.array(sorted(r for r in rows if 0 <= r < n))
+
+
+def _sqc_sampled(slim, W, bits, d32, g, rows):
+    out = slim.sqc_calibrate(dev(W, torch, True), torch.from_numpy(bits).to("cuda:0"),
+                             torch.from_numpy(d32).to("cuda:0"), g, 0.1, 50)
+    _sync()
+    g_out = {kk: host(v)[rows] for kk, v in out.items()}
+    o_out = oracle.sqc_calibrate(W, bits, d32, g, 0.1, 50, rows=rows)
+    compare_sqc(g_out, o_out, g)
+
+
+def test_attn_sqc_sampled_rows(slim, attn, attn_oracle):
+    wl, X, W = attn
+    _, d, S = attn_oracle
+    n, m = W.shape
+    bits = oracle.allocation(oracle.rank_groups(S), 6, 2)
+    rows = _sample_rows(n, np.random.default_rng(11), 53)
+    _say(f"sqc n={n} m={m} g=128 (full layer), {len(rows)} rows checked")
+    _sqc_sampled(slim, W, bits, d.astype(np.float32), 128, rows)
+
+
+def _pack_full(slim, n, m, g, N, seed):
+    rng = np.random.default_rng(seed)
+    k = m // g
+    bits = oracle.allocation(rng.permutation(k), k // 3, N)
+    codes = np.empty((n, m), dtype=np.uint8)
+    for j in range(k):
+        codes[:, j * g:(j + 1) * g] = rng.integers(0, 2 ** int(bits[j]), size=(n, g), dtype=np.uint8)
+    packed, info = slim.pack(torch.from_numpy(codes).to("cuda:0"), torch.from_numpy(bits).to("cuda:0"), g, N)
+    _sync()
+    assert int(info.item()) == 0
+    words = host(packed).view(np.uint32)
+    assert words.nbytes == n * m * N // 8
+    np.testing.assert_array_equal(words, oracle.pack_bitplanes(codes, bits, g))
+
+
+def test_attn_pack_full(slim):
+    _say("pack n=4096 m=4096 g=128 N=2 (full layer)")
+    _pack_full(slim, 4096, 4096, 128, 2, seed=21)
+
+
+# -------------------------------------------------------------- the other layer shapes
+# (workload, linear index, group): full-width weights, token slices of X.
+OTHER = [
+    ("llama7b-mlp-pair", 0, 128),          # up 11008 x 4096, avg 3 bits
+    ("llama7b-mlp-pair", 1, 128),          # down 4096 x 11008, k = 86
+    ("llama7b-decoder-layer", 0, 64),      # q 4096 x 4096, g = 64
+    ("llama7b-decoder-layer", 6, 32),      # down 4096 x 11008, g = 32, k = 344
+    ("large-13b-70b", 0, 128),             # 13824 x 5120
+    ("large-13b-70b", 1, 128),             # 28672 x 8192
+]
+_IDS = [f"{w}-{i}-g{g}" for w, i, g in OTHER]
+
+
+@pytest.fixture(scope="module", params=OTHER, ids=_IDS)
+def layer(request):
+    """One full-width layer with the oracle's H (2048 tokens), d and S."""
+    name, idx, g = request.param
+    wl = synth.WORKLOADS[name]
+    lin = wl.linears[idx]
+    _say(f"generating {name}/{lin.name} {lin.n}x{lin.m}")
+    W = synth.make_w(wl, idx)
+    Xh = synth.make_x(wl, lin.m, 0, 2048)
+    H64 = oracle.hessian(Xh)
+    H = H64.astype(np.float32)
+    d, S, info = oracle.salience(H, W, g, 0.01)
+    assert info == 0
+    return name, g, wl, lin, W, Xh, H64, H, d, S
+
+
+def test_shape_hessian_and_salience(slim, layer):
+    name, g, wl, lin, W, Xh, H64, H, d, S = layer
+    _say(f"hessian + salience {name}/{lin.name} m={lin.m} g={g}")
+    Hg = host(slim.hessian(dev(Xh, torch, True)))
+    _sync()
+    assert np.array_equal(Hg, Hg.T)
+    assert hessian_err(Hg, H64) <= 1e-3
+    hinv, gsal, info, _ = slim.salience(dev(H, torch, False), dev(W, torch, True), g, 0.01)
+    _sync()
+    assert int(info.item()) == 0
+    assert rel_err(host(hinv), d) <= 1e-3
+    assert rel_err(host(gsal), S) <= 1e-3
+
+
+def test_shape_sqc_rows_and_pack(slim, layer):
+    name, g, wl, lin, W, Xh, H64, H, d, S = layer
+    N = wl.avg_bits
+    k = lin.m // g
+    bits = oracle.allocation(oracle.rank_groups(S), k // 3, N)
+    rows = _sample_rows(lin.n, np.random.default_rng(lin.n + g), 21)
+    _say(f"sqc {name}/{lin.name} {lin.n}x{lin.m} g={g} N={N}, {len(rows)} rows; pack whole layer")
+    _sqc_sampled(slim, W, bits, d.astype(np.float32), g, rows)
+    _pack_full(slim, lin.n, lin.m, g, N, seed=lin.n * 7 + g)
+
+
+def test_shape_sba(slim, layer):
+    """Token slice against the oracle; for the 70B MLP, all tokens on properties.
+
+    The oracle's scan recomputes the whole trial layer for every step; on the
+    70B MLP (33 steps over 235 M weights) that is minutes of CPU, so there the
+    scan runs over all 262144 tokens (eight batches of the statistics
+    workspace) and is checked on the properties and on a split of the tokens."""
+    name, g, wl, lin, W, Xh, H64, H, d, S = layer
+    N, T = wl.avg_bits, wl.tokens
+    if lin.n * lin.m < 200_000_000:
+        Xs = synth.make_x(wl, lin.m, T - 256, T)
+        _say(f"sba {name}/{lin.name} {lin.n}x{lin.m} g={g} N={N}: last 256 tokens vs oracle")
+        _sba_slice_vs_oracle(slim, Xs, W, S, g, N)
+        return
+    _say(f"sba {name}/{lin.name} {lin.n}x{lin.m} over all {T} tokens and two token halves")
+    X = synth.make_x(wl, lin.m)
+    Xd, Wd = dev(X, torch, True), dev(W, torch, True)
+    del X
+    bits, kl, rs = _sba(slim, Xd, Wd, S, g, N)
+    _check_sba_properties(bits, kl, rs, S, N)
+    h = T // 2
+    _, kl_a, _ = _sba(slim, Xd[:h], Wd, S, g, N)
+    _, kl_b, _ = _sba(slim, Xd[h:], Wd, S, g, N)
+    np.testing.assert_allclose(kl, 0.5 * (kl_a + kl_b), rtol=1e-9, atol=0)
+    del Xd, Wd
+    torch.cuda.empty_cache()
