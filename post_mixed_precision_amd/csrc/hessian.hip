@@ -12,10 +12,10 @@
 // an 8-token x 8-column block with 16-byte row loads (coalesced along the
 // row) and transposes it in registers so that LDS rows hold tokens
 // contiguously, which is what one MFMA operand lane reads (16 bytes).  Tokens
-// are split over grid.y when there are too few tiles to fill 256 CUs; the
-// partial tiles are summed in split order by a second kernel that also
-// doubles, mirrors the lower tile to the upper triangle and optionally
-// accumulates, so H is exactly symmetric and bitwise reproducible.
+// are split into ranges (the count chosen so the workgroups fill whole rounds
+// of the 256 CUs); the partial tiles are summed in split order by a second
+// kernel that also doubles, mirrors the lower tile to the upper triangle and
+// optionally accumulates, so H is exactly symmetric and bitwise reproducible.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -43,9 +43,10 @@ __global__ __launch_bounds__(256, 2) void hessian_gram_kernel(const void *__rest
   constexpr int NPIECE = BF16 ? 1 : 2;  // 16-byte pieces per loader row (8 columns)
   __shared__ __attribute__((aligned(16))) unsigned char lds[2][2][HT * HPITCH];
 
+  // workgroup id -> (lower tile, token split), tiles varying fastest
+  const int tile = (int)(blockIdx.x % (unsigned)ntiles), split = (int)(blockIdx.x / (unsigned)ntiles);
   int bi, bj;
-  tri_decode(blockIdx.x, bi, bj);
-  const int split = blockIdx.y;
+  tri_decode(tile, bi, bj);
   const int64_t tbeg = (int64_t)split * tok_per_split;
   const int64_t tend = min(T, tbeg + tok_per_split);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -168,7 +169,7 @@ __global__ __launch_bounds__(256, 2) void hessian_gram_kernel(const void *__rest
     }
   }
 
-  float *out = part + ((size_t)split * ntiles + blockIdx.x) * (HT * HT);
+  float *out = part + ((size_t)split * ntiles + tile) * (HT * HT);
 #pragma unroll
   for (int i = 0; i < 2; ++i)
 #pragma unroll
@@ -205,9 +206,10 @@ __global__ __launch_bounds__(512, 1) void hessian_gram_tr_kernel(const uint16_t 
                                                                  float *__restrict__ part) {
   __shared__ __attribute__((aligned(16))) unsigned char lds0[2 * HOP2];
   __shared__ __attribute__((aligned(16))) unsigned char lds1[2 * HOP2];
+  // workgroup id -> (lower tile, token split), tiles varying fastest
+  const int tile = (int)(blockIdx.x % (unsigned)ntiles), split = (int)(blockIdx.x / (unsigned)ntiles);
   int bi, bj;
-  tri_decode(blockIdx.x, bi, bj);
-  const int split = blockIdx.y;
+  tri_decode(tile, bi, bj);
   const int64_t tbeg = (int64_t)split * tok_per_split;
   const int64_t tend = min(T, tbeg + tok_per_split);
   const int tid = threadIdx.x, lane = tid & 63;
@@ -294,7 +296,7 @@ __global__ __launch_bounds__(512, 1) void hessian_gram_tr_kernel(const uint16_t 
     }
     if (t0 < tend) stage(t0, lds0, lds1);
   }
-  float *out = part + ((size_t)split * ntiles + blockIdx.x) * (HT2 * HT2);
+  float *out = part + ((size_t)split * ntiles + tile) * (HT2 * HT2);
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -308,7 +310,8 @@ __global__ __launch_bounds__(512, 1) void hessian_gram_tr_kernel(const uint16_t 
 }
 
 // Sum the split partials in split order, double, write the lower tile and its
-// mirror (diagonal tiles: the lower triangle and its mirror).
+// mirror (diagonal tiles: the lower triangle and its mirror).  One workgroup
+// per 32-row strip of a tile; 16-byte loads, the splits' loads independent.
 template <int TILE>
 __global__ __launch_bounds__(256) void hessian_reduce_kernel(const float *__restrict__ part, int nsplit,
                                                              int ntiles, int64_t m, float *__restrict__ H,
@@ -317,32 +320,45 @@ __global__ __launch_bounds__(256) void hessian_reduce_kernel(const float *__rest
   int bi, bj;
   tri_decode(blockIdx.x, bi, bj);
   const int tid = threadIdx.x;
-  constexpr int PER = 32 * TILE / 256;
-  for (int r0 = 0; r0 < TILE; r0 += 32) {
-#pragma unroll 4
-    for (int e = 0; e < PER; ++e) {
-      const int idx = tid + e * 256;
-      const int r = r0 + idx / TILE, c = idx % TILE;
-      float s = 0.0f;
-      for (int sp = 0; sp < nsplit; ++sp) s += part[((size_t)sp * ntiles + blockIdx.x) * (TILE * TILE) + r * TILE + c];
-      float v = 2.0f * s;
-      const int64_t gi = (int64_t)bi * TILE + r, gj = (int64_t)bj * TILE + c;
-      if (gi < m && gj < m && (bi != bj || r >= c)) {
+  const int r0 = blockIdx.y * 32;
+  constexpr int Q = TILE / 4;             // float4 per tile row
+  constexpr int PER = 32 * Q / 256;       // float4 per thread
+  const float4 *src = (const float4 *)(part + (size_t)blockIdx.x * (TILE * TILE) + (size_t)r0 * TILE);
+  const size_t sstride = (size_t)ntiles * (TILE * TILE / 4);
+#pragma unroll
+  for (int e = 0; e < PER; ++e) {
+    const int idx = tid + e * 256;
+    const int rr = idx / Q, c = (idx % Q) * 4;
+    float4 s = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+    for (int sp = 0; sp < nsplit; ++sp) {
+      const float4 v = src[sp * sstride + idx];
+      s.x += v.x;
+      s.y += v.y;
+      s.z += v.z;
+      s.w += v.w;
+    }
+    const float vv[4] = {2.0f * s.x, 2.0f * s.y, 2.0f * s.z, 2.0f * s.w};
+    const int r = r0 + rr;
+    const int64_t gi = (int64_t)bi * TILE + r;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      float v = vv[q];
+      const int64_t gj = (int64_t)bj * TILE + c + q;
+      if (gi < m && gj < m && (bi != bj || r >= c + q)) {
         if (accumulate) v += H[gi * m + gj];
         H[gi * m + gj] = v;
       }
-      tr[r - r0][c] = v;
+      tr[rr][c + q] = v;
     }
-    __syncthreads();
+  }
+  __syncthreads();
 #pragma unroll 4
-    for (int e = 0; e < PER; ++e) {
-      const int idx = tid + e * 256;
-      const int c = idx / 32, rr = idx % 32;
-      const int r = r0 + rr;
-      const int64_t gi = (int64_t)bi * TILE + r, gj = (int64_t)bj * TILE + c;
-      if (gi < m && gj < m && (bi != bj || r > c)) H[gj * m + gi] = tr[rr][c];
-    }
-    __syncthreads();
+  for (int e = 0; e < 32 * TILE / 256; ++e) {
+    const int idx = tid + e * 256;
+    const int c = idx / 32, rr = idx % 32;
+    const int r = r0 + rr;
+    const int64_t gi = (int64_t)bi * TILE + r, gj = (int64_t)bj * TILE + c;
+    if (gi < m && gj < m && (bi != bj || r > c)) H[gj * m + gi] = tr[rr][c];
   }
 }
 
@@ -352,10 +368,24 @@ HessianPlan hessian_plan(int64_t t, int64_t m, bool bf16) {
   p.tile = p.tr ? HT2 : HT;
   p.nb = (int)((m + p.tile - 1) / p.tile);
   p.ntiles = p.nb * (p.nb + 1) / 2;
-  const int64_t want = (1024 + p.ntiles - 1) / p.ntiles;       // fill the chip several times over
-  const int64_t cap = (t + 4095) / 4096;                         // >= 4096 tokens per split
-  p.nsplit = (int)(want < cap ? want : cap);
-  if (p.nsplit < 1) p.nsplit = 1;
+  // Token splits: the count that minimises an estimate of the time, namely
+  // rounds of workgroups over the 256 CUs times tokens per split, plus writing
+  // and re-reading the split partials.  Splits keep >= 4096 tokens and the
+  // partials stay under 4 GB.
+  const int64_t cap = (t + 4095) / 4096;
+  const double tile_bytes = (double)p.tile * p.tile * 4.0;
+  const double per_tok = p.tr ? 27.5e-9 : 8.0e-9;     // seconds per token per workgroup (measured scale)
+  double best = -1.0;
+  p.nsplit = 1;
+  for (int64_t s = 1; s <= 64 && s <= cap; ++s) {
+    if (s > 1 && (double)s * p.ntiles * tile_bytes > 4.0e9) break;
+    const double rounds = (double)((p.ntiles * s + 255) / 256);
+    const double est = rounds * (double)((t + s - 1) / s) * per_tok + (double)s * p.ntiles * 2.0 * tile_bytes / 4.0e12;
+    if (best < 0.0 || est < best) {
+      best = est;
+      p.nsplit = (int)s;
+    }
+  }
   int64_t per = (t + p.nsplit - 1) / p.nsplit;
   per = (per + 63) / 64 * 64;
   if (per < 64) per = 64;
@@ -367,7 +397,7 @@ HessianPlan hessian_plan(int64_t t, int64_t m, bool bf16) {
 hipError_t launch_hessian(const void *X, bool bf16, int64_t t, int64_t m, float *H, bool accumulate,
                           void *ws, const HessianPlan &p, hipStream_t st) {
   float *part = (float *)ws;
-  dim3 grid(p.ntiles, p.nsplit);
+  const unsigned grid = (unsigned)(p.ntiles * p.nsplit);
   timer_begin(K_HESSIAN, st);
   if (p.tr) {
     hessian_gram_tr_kernel<<<grid, 512, 0, st>>>((const uint16_t *)X, t, m, p.tok_per_split, p.ntiles, part);
@@ -382,9 +412,9 @@ hipError_t launch_hessian(const void *X, bool bf16, int64_t t, int64_t m, float 
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (p.tr)
-    hessian_reduce_kernel<HT2><<<p.ntiles, 256, 0, st>>>(part, p.nsplit, p.ntiles, m, H, accumulate);
+    hessian_reduce_kernel<HT2><<<dim3(p.ntiles, HT2 / 32), 256, 0, st>>>(part, p.nsplit, p.ntiles, m, H, accumulate);
   else
-    hessian_reduce_kernel<HT><<<p.ntiles, 256, 0, st>>>(part, p.nsplit, p.ntiles, m, H, accumulate);
+    hessian_reduce_kernel<HT><<<dim3(p.ntiles, HT / 32), 256, 0, st>>>(part, p.nsplit, p.ntiles, m, H, accumulate);
   return hipGetLastError();
 }
 
