@@ -214,42 +214,65 @@ __global__ __launch_bounds__(512, 1) void sba_klgemm_kernel(
   // 16 rows of one 256-byte LDS pass at a fixed logical slot hit 16 distinct bank groups.  Lane L
   // of a chunk writes physical slot L % 8 of chunk row L / 8.
   const int rows_ok = kind == 2 ? x_rows_ok : a_rows_ok;
+  // Every DMA offset is a per-lane part fixed for the whole kernel (tile row and
+  // 16-byte slot; OOB for rows past the tile's valid rows) plus a wave-uniform
+  // part per stage (the column, and the trial-weight variant), passed as the
+  // scalar offset.  The descriptor of each phase is fixed per wave.
+  uint32_t voff[8];
+#pragma unroll
+  for (int q = 0; q < 8; ++q) {
+    const int row = rbase + 8 * q;
+    const int sl = (lane & 7) ^ (((lds_row0 + 8 * q + (lane >> 3)) >> 1) & 7);
+    voff[q] = row < rows_ok ? (uint32_t)row * rowb + (uint32_t)(sl * 16) : OOB;
+  }
+  const __amdgpu_buffer_rsrc_t rMain = kind == 2 ? rX : (kind == 0 ? rW : rV);
+  const __amdgpu_buffer_rsrc_t rUpd = kind == 2 ? rX : rV;
+  const uint32_t mainBase = kind == 1 ? vstride : 0u;           // A1 of the main phase: variant N
 
   auto issue = [&](int st, unsigned char *buf) __attribute__((always_inline)) {
-    int c0, gu = 0, gd = 0;
-    const bool main_stage = st < KM;
-    if (main_stage) {
-      c0 = st * KT;
-    } else {
-      const int r = 1 + (st - KM) / SPR;
-      c0 = ((st - KM) % SPR) * KT;
-      gu = s_order[r - 1];
-      gd = s_order[k - r];
-    }
     unsigned char *dst = buf + lds_row0 * SBP;
+    if (st < KM) {
+      const int c0 = st * KT;
+      const uint32_t so = __builtin_amdgcn_readfirstlane(mainBase + (uint32_t)(c0 * ESZ));   // uniform
+      if (c0 + KT <= m) {
 #pragma unroll
-    for (int q = 0; q < 8; ++q) {
-      const int row = rbase + 8 * q;                     // tile-local row of this lane
-      const int lrow = lds_row0 + 8 * q + (lane >> 3);   // LDS row it lands in
-      const int sl = (lane & 7) ^ ((lrow >> 1) & 7);     // logical slot to fetch
-      const int cc = c0 + sl * EPP;
-      int col, var_new = 1;
-      if (main_stage) {
-        col = cc;
-      } else {
-        const bool up = cc < g;
-        col = up ? gu * g + cc : gd * g + (cc - g);
-        var_new = up ? 2 : 0;
+        for (int q = 0; q < 8; ++q)
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(rMain, (lds_void_t *)(dst + q * 8 * SBP), 16, (int)voff[q],
+                                                   (int)so, 0, 0);
+      } else {                     // ragged last stage: columns past m read as zeros
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+          const int sl = (lane & 7) ^ (((lds_row0 + 8 * q + (lane >> 3)) >> 1) & 7);
+          const uint32_t off = c0 + sl * EPP < m ? voff[q] : OOB;
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(rMain, (lds_void_t *)(dst + q * 8 * SBP), 16, (int)off, (int)so,
+                                                   0, 0);
+        }
       }
-      uint32_t off = (col < m && row < rows_ok) ? (uint32_t)row * rowb + (uint32_t)col * ESZ : OOB;
-      lds_void_t *d = (lds_void_t *)(dst + q * 8 * SBP);
-      if (kind == 2) {
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rX, d, 16, (int)off, 0, 0, 0);
-      } else if (kind == 0 && main_stage) {
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rW, d, 16, (int)off, 0, 0, 0);
-      } else {
-        if (off != OOB) off += (kind == 1 ? 1u : (uint32_t)var_new) * vstride;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rV, d, 16, (int)off, 0, 0, 0);
+      return;
+    }
+    const int r = 1 + (st - KM) / SPR;
+    const int c0 = ((st - KM) % SPR) * KT;
+    const int gu = s_order[r - 1], gd = s_order[k - r];
+    // variant of the changing group's new width: N+1 (index 2) going up, N-1 (0) going down
+    const uint32_t vup = kind == 0 ? 2u * vstride : (kind == 1 ? vstride : 0u);
+    const uint32_t vdn = kind == 1 ? vstride : 0u;
+    if (g >= KT) {                 // the stage lies inside one of the two groups
+      const bool up = c0 < g;
+      const uint32_t so = __builtin_amdgcn_readfirstlane(up ? vup + (uint32_t)((gu * g + c0) * ESZ)
+                                                            : vdn + (uint32_t)((gd * g + c0 - g) * ESZ));
+#pragma unroll
+      for (int q = 0; q < 8; ++q)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rUpd, (lds_void_t *)(dst + q * 8 * SBP), 16, (int)voff[q], (int)so,
+                                                 0, 0);
+    } else {                       // g < KT: one stage (c0 = 0) holds the up group, then the down group
+      const uint32_t so_up = vup + (uint32_t)(gu * g * ESZ);
+      const uint32_t so_dn = vdn + (uint32_t)((gd - 1) * g * ESZ);   // column gd*g + (cc - g); wraps back below
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        const int sl = (lane & 7) ^ (((lds_row0 + 8 * q + (lane >> 3)) >> 1) & 7);
+        const uint32_t add = sl * EPP < g ? so_up : so_dn;
+        const uint32_t off = voff[q] == OOB ? OOB : voff[q] + add;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rUpd, (lds_void_t *)(dst + q * 8 * SBP), 16, (int)off, 0, 0, 0);
       }
     }
   };
