@@ -12,11 +12,13 @@
 // substitution L Z = I: when panel p is factored, its rows of Z = L^-1 become
 // final (Z_p = L_pp^-1 R_p) and every later row block is updated
 // R_i -= L_ip Z_p.  Since H_d^-1 = Z^T Z, d_j is the squared norm of column j of
-// Z, accumulated panel by panel in a fixed order.  Per panel:
-//   chol_diag   (1 workgroup)  factor the 64x64 diagonal block in LDS, invert it
+// Z, accumulated panel by panel in a fixed order.  Per panel p:
 //   chol_panel  L_ip = A_ip L_pp^-T for the rows below; Z_p = L_pp^-1 R_p and d += col-norms^2
-//   chol_update trailing A_ij -= L_ip L_jp^T (lower tiles) and R_ij -= L_ip Z_pj
-// The two GEMM-shaped kernels use v_mfma_f64_16x16x4_f64 on 64x64 tiles.
+//   chol_trail  (part 1) block column p+1 of A and row block p+1 of Z
+//   chol_trail  (part 2) the rest of A_ij -= L_ip L_jp^T and R_ij -= L_ip Z_pj, with
+//               workgroup 0 factoring and inverting diagonal block p+1 meanwhile
+//               (lookahead: the one-workgroup step no longer waits for the bulk update)
+// The GEMM-shaped work uses v_mfma_f64_16x16x4_f64 on 64x64 tiles.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -78,10 +80,11 @@ __global__ __launch_bounds__(256) void sal_init_kernel(const float *__restrict__
 // (8 contiguous columns) of both arrays in registers; each step only column j
 // of A and row j of R travel through LDS, read unconditionally as 16-byte
 // broadcasts, and the updates are selects rather than branches.
-constexpr int DCOLS = 8;   // columns per thread in chol_diag (512 threads: 64 rows x 8 column strips)
-
-__global__ __launch_bounds__(512) void chol_diag_kernel(double *__restrict__ A, int64_t mp, int p,
-                                                        double *__restrict__ TinvT, int32_t *__restrict__ info) {
+template <int NT>
+__device__ __forceinline__ void chol_diag_body(double *__restrict__ A, int64_t mp, int p, double *__restrict__ TinvT,
+                                               int32_t *__restrict__ info) {
+  constexpr int DC = NBK * NBK / NT;   // columns per thread
+  constexpr int NS = NBK / DC;         // column strips per row
   // Ping-pong broadcast buffers: step j reads set j & 1 and publishes step
   // j + 1's column and row into the other set, so one barrier per step keeps
   // readers and writers apart.
@@ -89,11 +92,11 @@ __global__ __launch_bounds__(512) void chol_diag_kernel(double *__restrict__ A, 
   __shared__ __attribute__((aligned(16))) double rowj[2][NBK];   // row j of the right-hand side
   __shared__ double piv[NBK];
   const int tid = threadIdx.x;
-  const int oi = tid >> 3, c0 = DCOLS * (tid & 7);   // this thread: row oi, columns c0 .. c0 + 7
+  const int oi = tid / NS, c0 = DC * (tid % NS);   // this thread: row oi, columns c0 .. c0 + DC - 1
   const int64_t k0 = (int64_t)p * NBK;
-  double Lr[DCOLS], Rr[DCOLS];
+  double Lr[DC], Rr[DC];
 #pragma unroll
-  for (int q = 0; q < DCOLS; ++q) {
+  for (int q = 0; q < DC; ++q) {
     const int c = c0 + q;
     Lr[q] = (c <= oi) ? A[(k0 + oi) * mp + k0 + c] : 0.0;
     Rr[q] = (c == oi) ? 1.0 : 0.0;
@@ -101,7 +104,7 @@ __global__ __launch_bounds__(512) void chol_diag_kernel(double *__restrict__ A, 
   if (c0 == 0) colj[0][oi] = Lr[0];
   if (oi == 0) {
 #pragma unroll
-    for (int q = 0; q < DCOLS; ++q) rowj[0][c0 + q] = Rr[q];
+    for (int q = 0; q < DC; ++q) rowj[0][c0 + q] = Rr[q];
   }
   __syncthreads();
   for (int j = 0; j < NBK; ++j) {
@@ -115,9 +118,9 @@ __global__ __launch_bounds__(512) void chol_diag_kernel(double *__restrict__ A, 
     inv = __fma_rn(inv, __fma_rn(-a, inv, 1.0), inv);
     inv = __fma_rn(inv, __fma_rn(-a, inv, 1.0), inv);
     // Unconditional broadcast reads (contiguous), then branch-free updates.
-    double cv[DCOLS], rv[DCOLS];
+    double cv[DC], rv[DC];
 #pragma unroll
-    for (int q = 0; q < DCOLS; q += 2) {
+    for (int q = 0; q < DC; q += 2) {
       const double2 x = *(const double2 *)&cj[c0 + q];
       const double2 y = *(const double2 *)&rj[c0 + q];
       cv[q] = x.x; cv[q + 1] = x.y;
@@ -125,7 +128,7 @@ __global__ __launch_bounds__(512) void chol_diag_kernel(double *__restrict__ A, 
     }
     const double f = (oi > j) ? -(cj[oi] * inv) : 0.0;
 #pragma unroll
-    for (int q = 0; q < DCOLS; ++q) {
+    for (int q = 0; q < DC; ++q) {
       const int c = c0 + q;
       const double nl = __fma_rn(f, cv[q], Lr[q]);
       const double nr = __fma_rn(f, rv[q], Rr[q]);
@@ -142,22 +145,27 @@ __global__ __launch_bounds__(512) void chol_diag_kernel(double *__restrict__ A, 
       double *rn = rowj[jn & 1];
       double pv = 0.0;
 #pragma unroll
-      for (int q = 0; q < DCOLS; ++q) pv = (c0 + q == jn) ? Lr[q] : pv;
-      if (jn >= c0 && jn < c0 + DCOLS) cn[oi] = pv;
+      for (int q = 0; q < DC; ++q) pv = (c0 + q == jn) ? Lr[q] : pv;
+      if (jn >= c0 && jn < c0 + DC) cn[oi] = pv;
       if (oi == jn) {
 #pragma unroll
-        for (int q = 0; q < DCOLS; q += 2) *(double2 *)&rn[c0 + q] = make_double2(Rr[q], Rr[q + 1]);
+        for (int q = 0; q < DC; q += 2) *(double2 *)&rn[c0 + q] = make_double2(Rr[q], Rr[q + 1]);
       }
     }
     __syncthreads();
   }
   const double si = sqrt(piv[oi]);
 #pragma unroll
-  for (int q = 0; q < DCOLS; ++q) {
+  for (int q = 0; q < DC; ++q) {
     const int c = c0 + q;
     if (c <= oi) A[(k0 + oi) * mp + k0 + c] = Lr[q] / sqrt(piv[c]);   // L_ij = a_ij / sqrt(a_jj)
     TinvT[c * NBK + oi] = (c <= oi) ? Rr[q] / si : 0.0;               // (L^-1)_ij = R_ij / sqrt(a_ii)
   }
+}
+
+__global__ __launch_bounds__(512) void chol_diag_kernel(double *__restrict__ A, int64_t mp, int p,
+                                                        double *__restrict__ TinvT, int32_t *__restrict__ info) {
+  chol_diag_body<512>(A, mp, p, TinvT, info);
 }
 
 // sX[k][i] = src[(r0 + i) * ld + c0 + k]   (row-major source, k contiguous -> transposed)
@@ -272,43 +280,25 @@ __global__ __launch_bounds__(256) void chol_panel_kernel(double *__restrict__ A,
   }
 }
 
-// Trailing update.  Workgroups [0, nA): lower tile (ib >= jb > p): A_ij -= L_ip L_jp^T.
-// Workgroups [nA, nA + nZ): tile (ib > p, cb <= p): Z_ib,cb -= L_ip Z_p,cb.
-__global__ __launch_bounds__(256) void chol_update_kernel(double *__restrict__ A, double *__restrict__ Z,
-                                                          int64_t mp, int p, int nr, int64_t nA) {
+// One 64 x 64 tile of the trailing update of panel p:
+//   A tile (rows r0, cols c0):  A_ij -= L_ip L_jp^T
+//   Z tile (rows r0, cols c0):  Z_ib,cb -= L_ip Z_p,cb
+__device__ __forceinline__ void trail_tile(double *__restrict__ A, double *__restrict__ Z, int64_t mp, int64_t k0,
+                                           int64_t r0, int64_t c0, bool zt) {
   __shared__ double sA[NBK * SP];
   __shared__ double sB[NBK * SP];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
-  const int64_t k0 = (int64_t)p * NBK;
-  const int64_t w = blockIdx.x;
-  double *C;
-  int64_t r0, c0;
-  if (w < nA) {
-    const int id = (int)w;
-    int ii = (int)((sqrt(8.0 * id + 1.0) - 1.0) * 0.5);
-    while ((ii + 1) * (ii + 2) / 2 <= id) ++ii;
-    while (ii * (ii + 1) / 2 > id) --ii;
-    const int jj = id - ii * (ii + 1) / 2;
-    r0 = k0 + (int64_t)(ii + 1) * NBK;
-    c0 = k0 + (int64_t)(jj + 1) * NBK;
-    load_tile_T(sA, A, mp, r0, k0, tid);
-    load_tile_T(sB, A, mp, c0, k0, tid);
-    C = A;
-  } else {
-    const int64_t id = w - nA;
-    const int ib = (int)(id / (p + 1));
-    const int cb = (int)(id % (p + 1));
-    r0 = k0 + (int64_t)(ib + 1) * NBK;
-    c0 = (int64_t)cb * NBK;
-    load_tile_T(sA, A, mp, r0, k0, tid);
+  load_tile_T(sA, A, mp, r0, k0, tid);
+  if (zt)
     load_tile_N(sB, Z, mp, k0, c0, tid);
-    C = Z;
-  }
+  else
+    load_tile_T(sB, A, mp, c0, k0, tid);
   __syncthreads();
   f64x4_t acc[2][2];
   zero_acc(acc);
   gemm64(sA, sB, acc, lane, wm, wn);
+  double *C = zt ? Z : A;
 #pragma unroll
   for (int i = 0; i < 2; ++i)
 #pragma unroll
@@ -320,7 +310,59 @@ __global__ __launch_bounds__(256) void chol_update_kernel(double *__restrict__ A
         double *dst = C + (r0 + row) * mp + c0 + col;
         *dst = *dst - acc[i][j][v];
       }
-  (void)nr;
+}
+
+// Trailing update of panel p, split for lookahead (NB panels in all):
+//   part 1 (next = 1): block column p+1 of A (row blocks p+1 .. NB-1) and
+//                      row block p+1 of Z (column blocks 0 .. p);
+//   part 2 (next = 0): A tiles with row >= column >= p+2, and Z row blocks
+//                      p+2 .. NB-1 (column blocks 0 .. p).
+// With diag set, workgroup 0 instead factors diagonal block p+1 (its inputs
+// are final once part 1 has run), concurrently with part 2.
+__global__ __launch_bounds__(256) void chol_trail_kernel(double *__restrict__ A, double *__restrict__ Z,
+                                                         double *__restrict__ TinvT, int32_t *__restrict__ info,
+                                                         int64_t mp, int p, int NB, int next, int diag) {
+  int64_t w = blockIdx.x;
+  if (diag) {
+    if (w == 0) {
+      chol_diag_body<256>(A, mp, p + 1, TinvT, info);
+      return;
+    }
+    --w;
+  }
+  const int64_t k0 = (int64_t)p * NBK;
+  int ii, jj;
+  bool zt;
+  if (next) {
+    const int nA = NB - p - 1;
+    if (w < nA) {
+      ii = p + 1 + (int)w;
+      jj = p + 1;
+      zt = false;
+    } else {
+      ii = p + 1;
+      jj = (int)(w - nA);
+      zt = true;
+    }
+  } else {
+    const int n2 = NB - p - 2;
+    const int64_t nA = (int64_t)n2 * (n2 + 1) / 2;
+    if (w < nA) {
+      const int id = (int)w;
+      int a = (int)((sqrt(8.0 * id + 1.0) - 1.0) * 0.5);
+      while ((a + 1) * (a + 2) / 2 <= id) ++a;
+      while (a * (a + 1) / 2 > id) --a;
+      ii = p + 2 + a;
+      jj = p + 2 + (id - a * (a + 1) / 2);
+      zt = false;
+    } else {
+      const int64_t id = w - nA;
+      ii = p + 2 + (int)(id / (p + 1));
+      jj = (int)(id % (p + 1));
+      zt = true;
+    }
+  }
+  trail_tile(A, Z, mp, k0, (int64_t)ii * NBK, (int64_t)jj * NBK, zt);
 }
 
 __global__ __launch_bounds__(256) void sal_hinv_out_kernel(const double *__restrict__ d, int64_t m,
@@ -416,16 +458,20 @@ hipError_t launch_salience(const float *H, int64_t m, double damp, const void *W
     if (blocks > 65536) blocks = 65536;
     sal_init_kernel<<<(unsigned)blocks, 256, 0, st>>>(H, m, mp, alpha, A, Z, d, info);
   }
+  // Lookahead: once the block column after panel p is updated, the next
+  // diagonal block is factored in the same launch as the rest of the trailing
+  // update, so the one-workgroup factorisation overlaps the bulk update.
   const int NB = (int)(mp / NBK);
+  chol_diag_kernel<<<1, 512, 0, st>>>(A, mp, 0, TinvT, info);
   for (int p = 0; p < NB; ++p) {
-    chol_diag_kernel<<<1, 512, 0, st>>>(A, mp, p, TinvT, info);
     const int nrow = NB - p - 1;
     chol_panel_kernel<<<nrow + p + 1, 256, 0, st>>>(A, Z, TinvT, d, mp, p, nrow);
     if (nrow > 0) {
-      const int64_t nA = (int64_t)nrow * (nrow + 1) / 2;
-      const int64_t nZ = (int64_t)nrow * (p + 1);
+      chol_trail_kernel<<<(unsigned)(nrow + p + 1), 256, 0, st>>>(A, Z, TinvT, info, mp, p, NB, 1, 0);
+      const int64_t n2 = nrow - 1;
+      const int64_t rest = n2 * (n2 + 1) / 2 + n2 * (p + 1);
       timer_begin(K_CHOL_UPDATE, st);
-      chol_update_kernel<<<(unsigned)(nA + nZ), 256, 0, st>>>(A, Z, mp, p, nrow, nA);
+      chol_trail_kernel<<<(unsigned)(rest + 1), 256, 0, st>>>(A, Z, TinvT, info, mp, p, NB, 0, 1);
       timer_end(K_CHOL_UPDATE, st);
     }
   }
