@@ -33,7 +33,8 @@ from .decode import as_f64, as_f32, bf16_round
 from .hessian import hessian, hessian_entries
 from .salience import hinv_diag, element_salience, group_salience, salience
 from .quantizer import tau_grid, minmax_params, fake_quant, quant_codes
-from .sba import rank_groups, allocation, trial_weights, kl_divergence, sba_search
+from .sba import (rank_groups, allocation, trial_weights, kl_divergence, output_mse, head_tail_order, random_order,
+                  sba_search)
 from .sqc import mask_3sigma, sqc_calibrate
 from .pack import pack_bitplanes, unpack_bitplanes, packed_words
 from .pipeline import quantize_layer

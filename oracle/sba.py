@@ -26,6 +26,20 @@ Readings taken here:
 * KL objective: for every calibration token t, p_t = softmax over the n
   outputs of x_t W^T and q_t = softmax of x_t W_hat^T; the score is the mean
   over tokens of sum_j p_tj (ln p_tj - ln q_tj), natural log, in float64.
+
+Ablation variants (scime.ai summary, "Measured effects": KL rather than MSE as
+the SBA objective, and random or head-tail group allocation instead of SBA;
+rkmt.cn digest, Fig. 5 discussion of random and head-tail allocation on OPT):
+
+* MSE objective: the mean over tokens of the squared error of the layer
+  output, (1/T) sum_t ||x_t W^T - x_t W_hat^T||^2 (summed over the n outputs),
+  in float64.  The pages name the objective only; this is its plainest form.
+* Other allocation orders: the salience ranking is replaced by a given order
+  of the groups, and the two-pointer scan is otherwise unchanged (step r
+  raises the first r groups of the order and lowers the last r).  Head-tail
+  is the order of the group index (head groups up, tail groups down); random
+  is a seeded permutation.  The scan over r and its objective stay as above,
+  so a variant differs from SBA only in which groups move.
 """
 import numpy as np
 
@@ -80,29 +94,58 @@ def kl_divergence(X, W, W_hat, per_token: bool = False):
     return kl_t if per_token else float(kl_t.mean())
 
 
-def sba_search(X, W, S, avg_bits: int, group: int, storage: str):
-    """(bits int8 [k], kl float64 [floor(k/2)+1], r_star) by scoring every step.
+def output_mse(X, W, W_hat, per_token: bool = False):
+    """Mean over tokens of ||x W^T - x W_hat^T||^2, float64."""
+    x = as_f64(X)
+    d = x @ (as_f64(W) - np.asarray(W_hat, dtype=np.float64)).T
+    e_t = (d * d).sum(axis=1)
+    return e_t if per_token else float(e_t.mean())
+
+
+def head_tail_order(k: int) -> np.ndarray:
+    """Head-tail allocation order: group index order."""
+    return np.arange(k, dtype=np.int64)
+
+
+def random_order(k: int, seed: int) -> np.ndarray:
+    """Random allocation order: a permutation from a seeded generator."""
+    return np.random.default_rng([seed, 0x5BA]).permutation(k)
+
+
+def sba_search(X, W, S, avg_bits: int, group: int, storage: str, objective: str = "kl", order=None):
+    """(bits int8 [k], score float64 [floor(k/2)+1], r_star) by scoring every step.
 
     Each step's trial layer output is recomputed from scratch (no reuse of
-    earlier steps' products)."""
+    earlier steps' products).  ``objective`` is "kl" (the method's) or "mse";
+    ``order`` replaces the salience ranking when given (S is then unused)."""
     w = as_f32(W)
     n, m = w.shape
     k = m // group
-    order = rank_groups(S)
+    order = rank_groups(S) if order is None else np.asarray(order, dtype=np.int64)
+    assert sorted(order.tolist()) == list(range(k)), "order must be a permutation of the groups"
     variants = {b: trial_weights(w, np.full(k, b), group, storage)
                 for b in (avg_bits - 1, avg_bits, avg_bits + 1)}
     x = as_f64(X)
-    lp = _log_softmax(x @ as_f64(w).T)
-    p = np.exp(lp)
+    y = x @ as_f64(w).T
+    if objective == "kl":
+        lp = _log_softmax(y)
+        p = np.exp(lp)
+    elif objective != "mse":
+        raise ValueError(objective)
     R = k // 2 + 1
-    kl = np.empty(R)
+    score = np.empty(R)
     for r in range(R):
         bits = allocation(order, r, avg_bits)
         wh = np.empty((n, m), dtype=np.float32)
         for gi in range(k):
             cols = slice(gi * group, (gi + 1) * group)
             wh[:, cols] = variants[int(bits[gi])][:, cols]
-        lq = _log_softmax(x @ wh.astype(np.float64).T)
-        kl[r] = float((p * (lp - lq)).sum(axis=1).mean())
-    r_star = int(np.argmin(kl))
-    return allocation(order, r_star, avg_bits), kl, r_star
+        yh = x @ wh.astype(np.float64).T
+        if objective == "kl":
+            lq = _log_softmax(yh)
+            score[r] = float((p * (lp - lq)).sum(axis=1).mean())
+        else:
+            d = y - yh
+            score[r] = float((d * d).sum(axis=1).mean())
+    r_star = int(np.argmin(score))
+    return allocation(order, r_star, avg_bits), score, r_star

@@ -219,3 +219,76 @@ def test_pack_all_max_and_single_bit():
     words = oracle.pack_bitplanes(codes, bits, g)
     off = n * 1 * (3 + 1) + (1 * n + 2) * 1
     assert np.count_nonzero(words) == 1 and words[off] == (1 << 5)
+
+
+# ----------------------------------------------------------------- ablation variants
+# scime.ai summary, "Measured effects": the SBA objective is KL rather than MSE,
+# and random or head-tail allocation replaces the salience ranking in the
+# ablations; rkmt.cn digest, Fig. 5 (OPT ablation: random / head-tail fail).
+def test_output_mse_brute_force_and_hessian_form():
+    rng = np.random.default_rng(11)
+    T, n, m = 5, 3, 8
+    X = rng.standard_normal((T, m)).astype(np.float32)
+    W = rng.standard_normal((n, m)).astype(np.float32)
+    Wh = W + (rng.standard_normal((n, m)) * 0.1).astype(np.float32)
+    brute = 0.0
+    for t in range(T):
+        for j in range(n):
+            d = sum(float(X[t, c]) * (float(W[j, c]) - float(Wh[j, c])) for c in range(m))
+            brute += d * d
+    brute /= T
+    assert oracle.output_mse(X, W, Wh) == pytest.approx(brute, rel=1e-12)
+    # (1/T) sum_t ||x_t D^T||^2 = trace(D H D^T) / (2T) with H = 2 X^T X
+    D = W.astype(np.float64) - Wh.astype(np.float64)
+    H = oracle.hessian(X)
+    assert oracle.output_mse(X, W, Wh) == pytest.approx(np.trace(D @ H @ D.T) / (2 * T), rel=1e-12)
+
+
+def test_sba_mse_objective_matches_hessian_quadratic_form():
+    rng = np.random.default_rng(12)
+    T, n, m, g = 40, 24, 256, 32
+    X = rng.standard_normal((T, m)).astype(np.float32)
+    X[:, 100:104] *= 15
+    W = (rng.standard_normal((n, m)) * 0.03).astype(np.float32)
+    _, S, _ = oracle.salience(oracle.hessian(X), W, g)
+    bits, mse, rs = oracle.sba_search(X, W, S, 2, g, "f32", objective="mse")
+    order = oracle.rank_groups(S)
+    H = oracle.hessian(X)
+    for r in range(len(mse)):
+        D = W.astype(np.float64) - oracle.trial_weights(W, oracle.allocation(order, r, 2), g, "f32")
+        assert mse[r] == pytest.approx(np.trace(D @ H @ D.T) / (2 * T), rel=1e-9)
+    assert rs == int(np.argmin(mse)) and np.all(mse > 0)
+    assert bits.tolist() == oracle.allocation(order, rs, 2).tolist()
+
+
+def test_allocation_orders():
+    k = 6
+    assert oracle.allocation(oracle.head_tail_order(k), 2, 2).tolist() == [3, 3, 2, 2, 1, 1]
+    p = oracle.random_order(40, 7)
+    assert sorted(p.tolist()) == list(range(40))
+    assert np.array_equal(p, oracle.random_order(40, 7)) and not np.array_equal(p, oracle.random_order(40, 8))
+    # the salience order is the default
+    rng = np.random.default_rng(13)
+    T, n, m, g = 12, 8, 128, 32
+    X = rng.standard_normal((T, m)).astype(np.float32)
+    W = (rng.standard_normal((n, m)) * 0.05).astype(np.float32)
+    S = rng.random(m // g)
+    a = oracle.sba_search(X, W, S, 2, g, "f32")
+    b = oracle.sba_search(X, W, None, 2, g, "f32", order=oracle.rank_groups(S))
+    assert a[2] == b[2] and np.array_equal(a[1], b[1]) and np.array_equal(a[0], b[0])
+    with pytest.raises(AssertionError):
+        oracle.sba_search(X, W, None, 2, g, "f32", order=[0, 0, 1, 2])
+
+
+def test_salience_order_beats_head_tail_and_random_on_outlier_layer():
+    # The ablation's direction on the tiny layer (outlier bands in groups 2
+    # and 3): the salience-ranked scan reaches a lower KL than head-tail or a
+    # random order (informational: the pages report it on OPT models).
+    wl = synth.WORKLOADS["tiny-512"]
+    X, W = synth.make_x(wl, 512, 0, 1024), synth.make_w(wl, 0)
+    _, S, _ = oracle.salience(oracle.hessian(X), W, 128)
+    _, kl_s, _ = oracle.sba_search(X, W, S, 2, 128, "f32")
+    _, kl_h, _ = oracle.sba_search(X, W, None, 2, 128, "f32", order=oracle.head_tail_order(4))
+    _, kl_r, _ = oracle.sba_search(X, W, None, 2, 128, "f32", order=oracle.random_order(4, 1))
+    assert kl_s.min() <= kl_h.min() and kl_s.min() <= kl_r.min()
+    assert kl_s[0] == kl_h[0] == kl_r[0]          # r = 0 is the same uniform allocation
