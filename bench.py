@@ -81,7 +81,7 @@ def measured_traffic(workload: str, linear: str, group: int):
         return None
 
 
-def run_step(slim, X, W, group, N, ev=None):
+def run_step(slim, X, W, group, N, ev=None, variant=None):
     """One pass of the whole path; optional event list records stage boundaries."""
     def mark(i):
         if ev is not None:
@@ -91,7 +91,12 @@ def run_step(slim, X, W, group, N, ev=None):
     mark(1)
     hinv, gsal, info, _ = slim.salience(H, W, group, 0.01)
     mark(2)
-    bits, kl, rs = slim.sba_search(X, W, gsal, group, N)
+    if variant is None:
+        bits, kl, rs = slim.sba_search(X, W, gsal, group, N)
+    else:   # ablation variant: objective and/or a given group order
+        objective, order = variant
+        bits, kl, rs = slim.sba_search_ex(X, W, group, N, group_sal=None if order is not None else gsal,
+                                          order=order, objective=objective)
     mark(3)
     sq = slim.sqc_calibrate(W, bits, hinv, group, 0.1, 50, want_tau=False)
     mark(4)
@@ -162,6 +167,12 @@ def main():
     ap.add_argument("--linear", type=int, default=0)
     ap.add_argument("--group", type=int, default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--objective", choices=("kl", "mse"), default="kl",
+                    help="SBA objective (the method's is kl; mse is the ablation)")
+    ap.add_argument("--order", choices=("salience", "head_tail", "random"), default="salience",
+                    help="group order of the SBA scan (the method's is salience)")
+    ap.add_argument("--ablation-report", action="store_true",
+                    help="also run the scan once per objective/order and report r* and the best score")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="run one plain device copy of this many MiB before the steps (counter calibration)")
     args = ap.parse_args()
@@ -200,8 +211,19 @@ def main():
         print(f"# copy probe: {nbytes} bytes read and written", file=sys.stderr, flush=True)
         del src, dst
 
+    k = m // group
+    variant = None
+    if args.objective != "kl" or args.order != "salience":
+        if args.order == "salience":
+            order = None
+        else:
+            perm = (np.arange(k) if args.order == "head_tail"
+                    else np.random.default_rng([0, 0x5BA]).permutation(k))   # seeded random order
+            order = torch.from_numpy(perm.astype(np.int32)).to("cuda:0")
+        variant = (args.objective, order)
+
     for i in range(args.warmup):
-        info, pinfo, rs, kl = run_step(slim, X, W, group, N)
+        info, pinfo, rs, kl = run_step(slim, X, W, group, N, variant=variant)
         torch.cuda.synchronize()
         print(f"# warmup {i}: info={int(info.item())} r*={int(rs.item())}", file=sys.stderr, flush=True)
     assert int(info.item()) == 0 and int(pinfo.item()) == 0
@@ -213,7 +235,7 @@ def main():
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for s in range(args.steps):
-        run_step(slim, X, W, group, N, evs[s])
+        run_step(slim, X, W, group, N, evs[s], variant=variant)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     slim.timing_enable(False)
@@ -243,7 +265,8 @@ def main():
         "scaling": "weak", "vs_baseline": None, "dtype": "bf16" if wl.dtype == "bf16" else "f32",
         "data": "synthetic (seeded; stands in for 128x2048 WikiText2 tokens and LLaMA weights)",
         "config": {"workload": args.workload, "linear": lin.name, "n": n, "m": m, "tokens": T,
-                   "group": group, "avg_bits": N, "tau_lambda": wl.tau_lambda, "tau_steps": wl.tau_steps},
+                   "group": group, "avg_bits": N, "tau_lambda": wl.tau_lambda, "tau_steps": wl.tau_steps,
+                   "sba_objective": args.objective, "sba_order": args.order},
         "roofline": {"bound": "mfma", "kernel": "sba_klgemm", "achieved": round(achieved / 1e12, 2),
                      "peak": PEAK_BF16_FLOPS / 1e12, "unit": "TFLOP/s",
                      "frac": round(achieved / PEAK_BF16_FLOPS, 4), "traffic": None,
@@ -274,6 +297,22 @@ def main():
             "pack_planes": {"bound": "hbm", "achieved_gbps": round(n * m * (1 + N / 8) / (pms / pl * 1e-3) / 1e9, 1),
                             "frac": round(n * m * (1 + N / 8) / (pms / pl * 1e-3) / PEAK_HBM_BPS, 4)},
         }
+    if args.ablation_report:
+        # The pages' ablation structure on this layer: the scan under each
+        # objective and group order (untimed; r* and the best score).
+        H = slim.hessian(X)
+        _, gsal, _, _ = slim.salience(H, W, group, 0.01)
+        rep = {}
+        for obj in ("kl", "mse"):
+            for ordk in ("salience", "head_tail", "random"):
+                o = None if ordk == "salience" else torch.from_numpy(
+                    (np.arange(k) if ordk == "head_tail" else np.random.default_rng([0, 0x5BA]).permutation(k))
+                    .astype(np.int32)).to("cuda:0")
+                b, sc, r = slim.sba_search_ex(X, W, group, N, group_sal=gsal if o is None else None, order=o,
+                                              objective=obj)
+                scn = sc.cpu().numpy()
+                rep[f"{obj}/{ordk}"] = {"r_star": int(r.item()), "best": float(scn.min()), "r0": float(scn[0])}
+        out["ablation"] = rep
     if not args.no_cpu_baseline:
         print("# timing the CPU oracle on a bounded sample", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(wl, args.linear, group, N, Xh, Wh)

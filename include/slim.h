@@ -10,6 +10,7 @@
  *   slim_hessian        H = 2 X^T X                         (component one, Hessian from calibration)
  *   slim_salience       d = diag((H + a I)^-1), delta = w^2 / d^2, group means   (component one)
  *   slim_sba_search     balanced bit allocation scored by output KL           (component one)
+ *   slim_sba_search_ex  the same with an output-MSE objective or a given group order (ablations)
  *   slim_sqc_calibrate  3-sigma mask + tau-grid search of scale and zero       (component two)
  *   slim_pack           group-structured bit-planes, no bitmap                (FAQ: storage)
  *
@@ -137,6 +138,31 @@ size_t slim_sba_workspace(int64_t t, int64_t n, int64_t m, int group, int dtype)
 int slim_sba_search(const void *X, int xdt, int64_t t, const void *W, int wdt, int64_t n, int64_t m,
                     int group, const double *group_sal, int avg_bits, int8_t *bits, double *kl,
                     int32_t *r_star, void *ws, size_t ws_bytes, void *stream);
+
+/* ------------------------------------------------------------------------
+ * SBA search variants for the ablations (scime.ai summary, "Measured
+ * effects": KL rather than MSE as the objective; random or head-tail group
+ * allocation instead of the salience ranking; rkmt.cn digest, Fig. 5).
+ *
+ * As slim_sba_search, with two changes:
+ *  - order (device int32 [k], or null): when given, it replaces the salience
+ *    ranking: step r raises order[0 .. r-1] and lowers order[k-r .. k-1]
+ *    (group_sal is then ignored and may be null).  It must be a permutation
+ *    of 0 .. k-1; entries outside that range are read as group 0 (the scan
+ *    stays in bounds, its result is meaningless).  Head-tail is the identity
+ *    order, random a permutation the caller draws.
+ *  - objective: SLIM_OBJ_KL (0) scores steps as slim_sba_search does;
+ *    SLIM_OBJ_MSE (1) scores them by the squared output error
+ *        score[r] = mean_t || x_t W^T - x_t W_r^T ||^2   (sum over the n outputs).
+ * score float64 [floor(k/2)+1]; r_star is its first argmin.  Errors as for
+ * slim_sba_search, plus SLIM_E_PARAM for an unknown objective and SLIM_E_NULL
+ * when both group_sal and order are null.
+ * ---------------------------------------------------------------------- */
+#define SLIM_OBJ_KL 0
+#define SLIM_OBJ_MSE 1
+int slim_sba_search_ex(const void *X, int xdt, int64_t t, const void *W, int wdt, int64_t n, int64_t m,
+                       int group, const double *group_sal, const int32_t *order, int avg_bits, int objective,
+                       int8_t *bits, double *score, int32_t *r_star, void *ws, size_t ws_bytes, void *stream);
 
 /* ------------------------------------------------------------------------
  * SQC calibration (component two: salient weights outside mu +- 3 sigma and

@@ -6,16 +6,17 @@ hand-written HIP kernels:
     hessian        H = 2 X^T X                                  (MFMA bf16/f32)
     salience       d = diag((H + a I)^-1), group-mean w^2/d^2   (fp64 MFMA Cholesky)
     sba_search     balanced N-1/N/N+1 allocation scored by output KL (fused MFMA + softmax)
+                   (sba_search_ex: output-MSE objective or a given group order, for the ablations)
     sqc_calibrate  3-sigma mask + tau grid over scale and zero  (wave-level, VALU)
     pack           group-structured bit-planes                  (HBM)
 
 ``quantize_layer`` chains them on the current stream.  PyTorch only provides
 device memory and the stream.
 """
-from ._lib import (SlimError, load_library, hessian, salience, sba_search, sqc_calibrate, pack, tau_table,
+from ._lib import (SlimError, load_library, hessian, salience, sba_search, sba_search_ex, sqc_calibrate, pack, tau_table,
                    timing_enable, timing_reset, timing_read, SLIM_F32, SLIM_BF16)
 from .layer import quantize_layer
 
-__all__ = ["SlimError", "load_library", "hessian", "salience", "sba_search", "sqc_calibrate", "pack",
+__all__ = ["SlimError", "load_library", "hessian", "salience", "sba_search", "sba_search_ex", "sqc_calibrate", "pack",
            "tau_table", "timing_enable", "timing_reset", "timing_read", "quantize_layer", "SLIM_F32",
            "SLIM_BF16"]

@@ -33,6 +33,8 @@ _SIGS = {
     "slim_sba_workspace": (_c_sz, [_c_i64, _c_i64, _c_i64, _c_int, _c_int]),
     "slim_sba_search": (_c_int, [_c_vp, _c_int, _c_i64, _c_vp, _c_int, _c_i64, _c_i64, _c_int, _c_vp, _c_int,
                                  _c_vp, _c_vp, _c_vp, _c_vp, _c_sz, _c_vp]),
+    "slim_sba_search_ex": (_c_int, [_c_vp, _c_int, _c_i64, _c_vp, _c_int, _c_i64, _c_i64, _c_int, _c_vp, _c_vp,
+                                    _c_int, _c_int, _c_vp, _c_vp, _c_vp, _c_vp, _c_sz, _c_vp]),
     "slim_sqc_calibrate": (_c_int, [_c_vp, _c_int, _c_i64, _c_i64, _c_int, _c_vp, _c_vp, _c_dbl, _c_int, _c_vp,
                                     _c_vp, _c_vp, _c_vp, _c_vp, _c_vp]),
     "slim_tau_table": (_c_int, [_c_dbl, _c_int, _c_vp]),
@@ -181,6 +183,36 @@ def sba_search(X, W, group_sal, group: int, avg_bits: int):
                               int(avg_bits), _ptr(bits), _ptr(kl), _ptr(rs), _ptr(ws), ws.numel(),
                               _stream(W.device)), "slim_sba_search")
     return bits, kl, rs
+
+
+OBJECTIVES = {"kl": 0, "mse": 1}
+
+
+def sba_search_ex(X, W, group: int, avg_bits: int, group_sal=None, order=None, objective: str = "kl"):
+    """Ablation variants: objective "kl" or "mse"; order (int32 [k] on the GPU)
+    replaces the salience ranking.  -> (bits int8 [k], score f64 [k//2+1], r_star int32 [1])."""
+    torch = _torch()
+    lib = load_library()
+    X, W = _dev(X), _dev(W)
+    if group_sal is not None:
+        group_sal = _dev(group_sal)
+    if order is not None:
+        order = _dev(order)
+        if order.dtype != torch.int32:
+            raise SlimError("order must be int32")
+    if objective not in OBJECTIVES:
+        raise SlimError(f"unknown objective {objective!r}")
+    T, m = X.shape
+    n = W.shape[0]
+    k = m // group
+    bits = torch.empty(k, dtype=torch.int8, device=W.device)
+    score = torch.empty(k // 2 + 1, dtype=torch.float64, device=W.device)
+    rs = torch.empty(1, dtype=torch.int32, device=W.device)
+    ws = _ws(lib.slim_sba_workspace(T, n, m, group, _dtype_code(W)), W.device)
+    check(lib.slim_sba_search_ex(_ptr(X), _dtype_code(X), T, _ptr(W), _dtype_code(W), n, m, group, _ptr(group_sal),
+                                 _ptr(order), int(avg_bits), OBJECTIVES[objective], _ptr(bits), _ptr(score), _ptr(rs),
+                                 _ptr(ws), ws.numel(), _stream(W.device)), "slim_sba_search_ex")
+    return bits, score, rs
 
 
 def sqc_calibrate(W, bits, hinv, group: int, lam: float = 0.1, n_tau: int = 50, want_tau: bool = True):

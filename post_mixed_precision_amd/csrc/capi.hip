@@ -151,23 +151,32 @@ size_t slim_sba_workspace(int64_t t, int64_t n, int64_t m, int group, int dtype)
   return slim::sba_plan(t, n, m, group, dtype == SLIM_BF16).ws_bytes;
 }
 
-int slim_sba_search(const void *X, int xdt, int64_t t, const void *W, int wdt, int64_t n, int64_t m, int group,
-                    const double *group_sal, int avg_bits, int8_t *bits, double *kl, int32_t *r_star, void *ws,
-                    size_t ws_bytes, void *stream) {
-  if (!X || !W || !group_sal || !bits || !kl || !r_star) return SLIM_E_NULL;
+int slim_sba_search_ex(const void *X, int xdt, int64_t t, const void *W, int wdt, int64_t n, int64_t m, int group,
+                       const double *group_sal, const int32_t *order, int avg_bits, int objective, int8_t *bits,
+                       double *score, int32_t *r_star, void *ws, size_t ws_bytes, void *stream) {
+  if (!X || !W || (!group_sal && !order) || !bits || !score || !r_star) return SLIM_E_NULL;
   if (!valid_dtype(xdt) || xdt != wdt) return SLIM_E_DTYPE;
   if (t < 1 || n < 1 || m < 1 || m > SLIM_MAX_WIDTH) return SLIM_E_SHAPE;
   if (!valid_group(group) || m % group || m / group > SLIM_MAX_GROUPS) return SLIM_E_SHAPE;
   if (avg_bits < 2 || avg_bits > 7) return SLIM_E_PARAM;
+  if (objective != SLIM_OBJ_KL && objective != SLIM_OBJ_MSE) return SLIM_E_PARAM;
   // the three trial-weight variants are addressed with 32-bit buffer offsets
   if ((double)n * (double)m * (xdt == SLIM_BF16 ? 2.0 : 4.0) * 3.0 > 2147483647.0) return SLIM_E_SHAPE;
   if (!aligned16(X) || !aligned16(W)) return SLIM_E_ALIGN;
   const slim::SbaPlan p = slim::sba_plan(t, n, m, group, xdt == SLIM_BF16);
   if (!ws || ws_bytes < p.ws_bytes) return SLIM_E_WORKSPACE;
   if (!aligned16(ws)) return SLIM_E_ALIGN;
-  hipError_t e = slim::launch_sba(X, W, xdt == SLIM_BF16, t, n, m, group, group_sal, avg_bits, bits, kl, r_star, ws, p,
-                                  (hipStream_t)stream);
+  hipError_t e = slim::launch_sba(X, W, xdt == SLIM_BF16, t, n, m, group, group_sal, order, avg_bits, objective,
+                                  bits, score, r_star, ws, p, (hipStream_t)stream);
   return e == hipSuccess ? SLIM_OK : hip_fail(e);
+}
+
+int slim_sba_search(const void *X, int xdt, int64_t t, const void *W, int wdt, int64_t n, int64_t m, int group,
+                    const double *group_sal, int avg_bits, int8_t *bits, double *kl, int32_t *r_star, void *ws,
+                    size_t ws_bytes, void *stream) {
+  if (!group_sal) return SLIM_E_NULL;
+  return slim_sba_search_ex(X, xdt, t, W, wdt, n, m, group, group_sal, nullptr, avg_bits, SLIM_OBJ_KL, bits, kl,
+                            r_star, ws, ws_bytes, stream);
 }
 
 // ---------------------------------------------------------------- SQC

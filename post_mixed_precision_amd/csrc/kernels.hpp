@@ -40,9 +40,11 @@ struct SbaPlan {
   size_t off_wv, off_order, off_sp, off_sq, off_part, ws_bytes;
 };
 SbaPlan sba_plan(int64_t t, int64_t n, int64_t m, int group, bool bf16);
+// ext_order: a caller-given group order (replaces the salience ranking) or null;
+// objective: 0 = output KL, 1 = output MSE.
 hipError_t launch_sba(const void *X, const void *W, bool bf16, int64_t t, int64_t n, int64_t m,
-                      int group, const double *gsal, int avg_bits, int8_t *bits, double *kl,
-                      int32_t *r_star, void *ws, const SbaPlan &p, hipStream_t st);
+                      int group, const double *gsal, const int32_t *ext_order, int avg_bits, int objective,
+                      int8_t *bits, double *kl, int32_t *r_star, void *ws, const SbaPlan &p, hipStream_t st);
 
 // ---- SQC ----
 struct TauTable {

@@ -149,7 +149,7 @@ template <bool BF16, bool PARTIAL>
 __global__ __launch_bounds__(512, 1) void sba_klgemm_kernel(
     const void *__restrict__ X, const void *__restrict__ W, const void *__restrict__ Wv,
     const int *__restrict__ order, int64_t tok_base, int64_t tb_len, int64_t n, int64_t m, int g, int k, int R,
-    int NC, int NCX, int TT, int c_last, float4 *__restrict__ sq, float2 *__restrict__ sp) {
+    int NC, int NCX, int TT, int c_last, float4 *__restrict__ sq, float2 *__restrict__ sp, int mse) {
   constexpr int ESZ = BF16 ? 2 : 4;
   constexpr int KT = BF16 ? 64 : 32;  // K elements per stage (128 bytes per row)
   constexpr int EPP = 16 / ESZ;       // elements per 16-byte piece
@@ -392,6 +392,33 @@ __global__ __launch_bounds__(512, 1) void sba_klgemm_kernel(
   auto epilogue = [&](int r) __attribute__((always_inline)) {
     // output row inside the half of accumulator element (ob, v): ob*32 + acc32_row(v, lane)
     const int lim = PARTIAL ? s_rows_ok - wo * 64 - 4 * (lane >> 5) : 64;
+    if (mse) {
+      // Output-MSE objective: per token, the sum of (y - yhat)^2 over the chunk's outputs.
+#pragma unroll
+      for (int tb = 0; tb < 2; ++tb) {
+        float se = 0.0f;
+#pragma unroll
+        for (int ob = 0; ob < 2; ++ob)
+#pragma unroll
+          for (int v = 0; v < 16; ++v) {
+            const float d = accY[ob * 2 + tb][v] - accQ[ob * 2 + tb][v];
+            if (!PARTIAL || ob * 32 + 8 * (v >> 2) + (v & 3) < lim) se = __builtin_fmaf(d, d, se);
+          }
+        se += __shfl_xor(se, 32, 64);
+        if (lane < 32) xq[wo][wt * 64 + tb * 32 + lane] = make_float4(0.0f, 0.0f, se, 0.0f);
+      }
+      __syncthreads();
+      if (wo == 0 && lane < 32) {
+#pragma unroll
+        for (int tb = 0; tb < 2; ++tb) {
+          const int tok = wt * 64 + tb * 32 + lane;
+          const int64_t tg = tok0 + tok;
+          if (tg < tb_len)
+            sq[((int64_t)r * NC + c) * tb_len + tg] = make_float4(0.0f, 0.0f, xq[0][tok].z + xq[1][tok].z, 0.0f);
+        }
+      }
+      return;
+    }
     float pz[2] = {0.0f, 0.0f}, qm[2], qz[2], qs[2];
 #pragma unroll
     for (int tb = 0; tb < 2; ++tb) {
@@ -514,14 +541,14 @@ __global__ __launch_bounds__(512, 1) void sba_klgemm_kernel(
 // Merge chunk statistics per token, KL_t in float64, per-block sums per step.
 __global__ __launch_bounds__(256) void sba_combine_kernel(const float2 *__restrict__ sp, const float4 *__restrict__ sq,
                                                           int64_t tb, int NC, int R, double *__restrict__ part,
-                                                          int64_t blk_off) {
+                                                          int64_t blk_off, int mse) {
   __shared__ double red[4][1032];
   const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
   const bool valid = t < tb;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   float M = -INFINITY;
   double Z = 0.0;
-  if (valid) {
+  if (valid && !mse) {
     for (int c = 0; c < NC; ++c) {
       const float2 v = sp[(int64_t)c * tb + t];
       if (v.x > M) {
@@ -535,7 +562,9 @@ __global__ __launch_bounds__(256) void sba_combine_kernel(const float2 *__restri
   const double lse_p = (double)M + log(Z);
   for (int r = 0; r < R; ++r) {
     double kl = 0.0;
-    if (valid) {
+    if (valid && mse) {            // squared output error: the chunks' partial sums add up
+      for (int c = 0; c < NC; ++c) kl += (double)sq[((int64_t)r * NC + c) * tb + t].z;
+    } else if (valid) {
       float Mq = -INFINITY;
       double Zq = 0.0, S = 0.0;
       for (int c = 0; c < NC; ++c) {
@@ -632,11 +661,12 @@ SbaPlan sba_plan(int64_t t, int64_t n, int64_t m, int group, bool bf16) {
 }
 
 hipError_t launch_sba(const void *X, const void *W, bool bf16, int64_t t, int64_t n, int64_t m, int group,
-                      const double *gsal, int avg_bits, int8_t *bits, double *kl, int32_t *r_star, void *ws,
-                      const SbaPlan &p, hipStream_t st) {
+                      const double *gsal, const int32_t *ext_order, int avg_bits, int objective, int8_t *bits,
+                      double *kl, int32_t *r_star, void *ws, const SbaPlan &p, hipStream_t st) {
   char *base = (char *)ws;
   void *Wv = base + p.off_wv;
-  int *order = (int *)(base + p.off_order);
+  int *order = ext_order ? (int *)ext_order : (int *)(base + p.off_order);
+  const int mse = objective == 1;
   float2 *sp = (float2 *)(base + p.off_sp);
   float4 *sq = (float4 *)(base + p.off_sq);
   double *part = (double *)(base + p.off_part);
@@ -654,7 +684,7 @@ hipError_t launch_sba(const void *X, const void *W, bool bf16, int64_t t, int64_
     else { SLIM_TRIAL(4) }
 #undef SLIM_TRIAL
   }
-  sba_rank_kernel<<<1, 256, 0, st>>>(gsal, p.k, order);
+  if (!ext_order) sba_rank_kernel<<<1, 256, 0, st>>>(gsal, p.k, order);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
 
@@ -671,22 +701,22 @@ hipError_t launch_sba(const void *X, const void *W, bool bf16, int64_t t, int64_
       const unsigned grid = (unsigned)(8 * NCX * TT);
       if (bf16)
         sba_klgemm_kernel<true, false><<<grid, 512, 0, st>>>(X, W, Wv, order, t0, len, n, m, group, p.k, p.R, NC, NCX,
-                                                             TT, NCF, sq, sp);
+                                                             TT, NCF, sq, sp, mse);
       else
         sba_klgemm_kernel<false, false><<<grid, 512, 0, st>>>(X, W, Wv, order, t0, len, n, m, group, p.k, p.R, NC,
-                                                              NCX, TT, NCF, sq, sp);
+                                                              NCX, TT, NCF, sq, sp, mse);
     }
     if (NC > NCF) {
       if (bf16)
         sba_klgemm_kernel<true, true><<<TT, 512, 0, st>>>(X, W, Wv, order, t0, len, n, m, group, p.k, p.R, NC, NCX, TT,
-                                                          NCF, sq, sp);
+                                                          NCF, sq, sp, mse);
       else
         sba_klgemm_kernel<false, true><<<TT, 512, 0, st>>>(X, W, Wv, order, t0, len, n, m, group, p.k, p.R, NC, NCX,
-                                                           TT, NCF, sq, sp);
+                                                           TT, NCF, sq, sp, mse);
     }
     timer_end(K_SBA_KLGEMM, st);
     const unsigned cb = (unsigned)((len + 255) / 256);
-    sba_combine_kernel<<<cb, 256, 0, st>>>(sp, sq, len, NC, p.R, part, blk_off);
+    sba_combine_kernel<<<cb, 256, 0, st>>>(sp, sq, len, NC, p.R, part, blk_off, mse);
     blk_off += cb;
     e = hipGetLastError();
     if (e != hipSuccess) return e;

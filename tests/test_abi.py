@@ -126,3 +126,13 @@ def test_timing_interface(lib):
     assert _lib.timing_read("sba_klgemm") == (0.0, 0)
     ms, cnt = ctypes.c_double(), ctypes.c_int64()
     assert lib.slim_timing_read(b"nope", ctypes.byref(ms), ctypes.byref(cnt)) == -4
+
+
+def test_sba_variant_validation(lib):
+    def call(**kw):
+        return lib.slim_sba_search_ex(FAKE, 1, 100, FAKE, 1, 64, 256, 128, kw.get("S", FAKE), kw.get("order", None),
+                                      2, kw.get("obj", 0), FAKE, FAKE, FAKE, FAKE, 1 << 40, None)
+    assert call(S=None, order=None) == -1
+    assert call(obj=2) == -4 and call(obj=-1) == -4
+    assert lib.slim_sba_search_ex(FAKE, 1, 100, FAKE, 1, 64, 96, 128, FAKE, None, 2, 0, FAKE, FAKE, FAKE, FAKE,
+                                  1 << 40, None) == -2

@@ -158,6 +158,34 @@ def test_attn_sba_token_slice_vs_oracle(slim, attn, attn_oracle, t0, t1):
     _sba_slice_vs_oracle(slim, X[t0:t1], W, S, 128, 2)
 
 
+def test_attn_sba_mse_objective_full_tokens(slim, attn, attn_oracle):
+    """Output-MSE variant of the scan: all tokens on properties and the token
+    split (the per-token squared error is additive), a slice against the oracle."""
+    wl, X, W = attn
+    _, _, S = attn_oracle
+    T = X.shape[0]
+    _say(f"sba (output MSE) T={T} n=4096 m=4096 g=128 (full layer), halves, slice vs oracle")
+    Xd, Wd = dev(X, torch, True), dev(W, torch, True)
+    Sd = torch.from_numpy(np.asarray(S, dtype=np.float64)).to("cuda:0")
+
+    def run(x):
+        b, sc, rs = slim.sba_search_ex(x, Wd, 128, 2, group_sal=Sd, objective="mse")
+        _sync()
+        return host(b).astype(int), host(sc), int(host(rs)[0])
+    bits, mse, rs = run(Xd)
+    _check_sba_properties(bits, mse, rs, S, 2)
+    h = T // 2
+    _, a, _ = run(Xd[:h])
+    _, b, _ = run(Xd[h:])
+    np.testing.assert_allclose(mse, 0.5 * (a + b), rtol=1e-9, atol=0)
+    bits_s, mse_s, rs_s = run(Xd[:512])
+    bits_o, mse_o, rs_o = oracle.sba_search(X[:512], W, S, 2, 128, "bf16", objective="mse")
+    assert float(np.max(np.abs(mse_s - mse_o) / mse_o)) <= 1e-3
+    if not kl_near_tie(mse_o):
+        assert rs_s == rs_o
+        np.testing.assert_array_equal(bits_s, bits_o)
+
+
 def _sample_rows(n, rng, count):
     rows = {0, 1, 63, 64, 127, 128, n // 2, n - 129, n - 128, n - 2, n - 1}
     rows |= set(rng.choice(n, count, replace=False).tolist())

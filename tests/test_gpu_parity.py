@@ -270,3 +270,53 @@ def test_end_to_end_tiny_layer(slim):
         compare_sqc(g_out, ref["sqc"], 128)
         if (g_out["codes"] == ref["sqc"]["codes"]).all():
             np.testing.assert_array_equal(host(res["packed"]).view(np.uint32), ref["packed"])
+
+
+# ----------------------------------------------------------------- SBA ablation variants
+def _sba_ex_check(slim, X, W, S, g, N, storage, objective, order):
+    o_dev = None if order is None else torch.from_numpy(np.asarray(order, dtype=np.int32)).to("cuda:0")
+    s_dev = None if S is None else torch.from_numpy(np.asarray(S, dtype=np.float64)).to("cuda:0")
+    bits, score, rs = slim.sba_search_ex(dev(X, torch, storage == "bf16"), dev(W, torch, storage == "bf16"), g, N,
+                                         group_sal=s_dev, order=o_dev, objective=objective)
+    _sync()
+    bits_o, score_o, rs_o = oracle.sba_search(X, W, S, N, g, storage, objective=objective, order=order)
+    sg = host(score)
+    err = float(np.max(np.abs(sg - score_o) / np.maximum(np.abs(score_o), 1e-12)))
+    assert err <= 1e-3, (err, sg, score_o)
+    rs_g = int(host(rs)[0])
+    if not kl_near_tie(score_o):
+        assert rs_g == rs_o
+        np.testing.assert_array_equal(host(bits), bits_o)
+    b = host(bits).astype(int)
+    assert (b == N + 1).sum() == (b == N - 1).sum() == rs_g and b.sum() == len(b) * N
+
+
+@pytest.mark.parametrize("T,n,m,g,N,dtype,objective,order_kind", [
+    (700, 256, 512, 128, 2, "bf16", "mse", "salience"),
+    (513, 200, 256, 64, 2, "bf16", "mse", "salience"),     # partial output chunk
+    (300, 130, 160, 32, 2, "bf16", "mse", "random"),       # both groups in one stage, odd k
+    (400, 128, 384, 128, 3, "bf16", "kl", "head_tail"),
+    (256, 96, 256, 128, 2, "f32", "mse", "head_tail"),     # f32 MFMA path
+    (700, 256, 512, 64, 2, "bf16", "kl", "random"),
+])
+def test_sba_variant_parity(slim, T, n, m, g, N, dtype, objective, order_kind):
+    print(f"sba variant T={T} n={n} m={m} g={g} N={N} {dtype} {objective} {order_kind}", flush=True)
+    wl, X, W = _case_inputs(T, n, m, dtype, dist="t5", wid=57, avg_bits=N)
+    k = m // g
+    if order_kind == "salience":
+        _, S, _ = oracle.salience(oracle.hessian(X), W, g)
+        order = None
+    else:
+        S = None
+        order = oracle.head_tail_order(k) if order_kind == "head_tail" else oracle.random_order(k, T)
+    _sba_ex_check(slim, X, W, S, g, N, dtype, objective, order)
+
+
+def test_sba_variant_rejects_bad_arguments(slim):
+    X = torch.zeros((8, 256), dtype=torch.bfloat16, device="cuda:0")
+    W = torch.zeros((16, 256), dtype=torch.bfloat16, device="cuda:0")
+    with pytest.raises(slim.SlimError):
+        slim.sba_search_ex(X, W, 128, 2)                                   # neither salience nor order
+    with pytest.raises(slim.SlimError):
+        slim.sba_search_ex(X, W, 128, 2, order=torch.arange(2, dtype=torch.int32, device="cuda:0"),
+                           objective="l1")
