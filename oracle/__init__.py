@@ -37,6 +37,7 @@ from .sba import (rank_groups, allocation, trial_weights, kl_divergence, output_
                   sba_search)
 from .sqc import mask_3sigma, sqc_calibrate
 from .pack import pack_bitplanes, unpack_bitplanes, packed_words
+from .qlinear import dequant_weights, qlinear
 from .pipeline import quantize_layer
 
 __all__ = [
