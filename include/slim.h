@@ -13,6 +13,7 @@
  *   slim_sba_search_ex  the same with an output-MSE objective or a given group order (ablations)
  *   slim_sqc_calibrate  3-sigma mask + tau-grid search of scale and zero       (component two)
  *   slim_pack           group-structured bit-planes, no bitmap                (FAQ: storage)
+ *   slim_qlinear        Y = X W_hat^T read from the planes (decode batches)    (FAQ: deployment)
  *
  * Conventions shared by every call:
  *  - Pointers are DEVICE pointers unless the parameter says "host".  Arrays
@@ -209,10 +210,36 @@ int slim_pack(const uint8_t *codes, int64_t n, int64_t m, int group, const int8_
               int avg_bits, uint32_t *packed, int32_t *info, void *stream);
 
 /* ------------------------------------------------------------------------
+ * Mixed-precision linear layer on the packed planes (rkmt.cn digest, FAQ on
+ * storage and deployment: no bitmap or codebook, dequantization with the
+ * structure of uniform quantization; scime.ai summary, "Limitations": the
+ * speed of mixed-precision dequantization at inference).
+ *
+ *   Y[a, i] = sum_c X[a, c] * (q[i, c] - zero[i, c/g]) * scale[i, c/g]
+ *
+ * q is decoded from packed (the slim_pack layout, widths bits[k]); scale and
+ * zero are the float32 [n, k] outputs of slim_sqc_calibrate.  X: [t, m] in
+ * dtype xdt (bfloat16 or float32), t <= SLIM_QLINEAR_MAX_T (decode-sized
+ * batches); Y: float32 [t, n].  Accumulation is float32; for a given t the
+ * sum over groups runs in a fixed order (bitwise reproducible).  bits must
+ * hold widths in 1 .. 8 adding up to k * avg_bits, as slim_pack requires;
+ * otherwise every output is NaN (checked before any plane is read).  Workspace:
+ * slim_qlinear_workspace(t, n, m, g) bytes (partial sums over runs of
+ * groups when the layer is split along its input; its contents on entry do
+ * not matter).
+ * ---------------------------------------------------------------------- */
+#define SLIM_QLINEAR_MAX_T 8
+size_t slim_qlinear_workspace(int64_t t, int64_t n, int64_t m, int group);
+int slim_qlinear(const void *X, int xdt, int64_t t, int64_t m, const uint32_t *packed, const int8_t *bits,
+                 int avg_bits, const float *scale, const float *zero, int64_t n, int group, float *Y, void *ws,
+                 size_t ws_bytes, void *stream);
+
+/* ------------------------------------------------------------------------
  * Kernel timing (instrumentation, not part of the method).  When enabled,
  * the library records a pair of HIP events on the launch stream around every
  * launch of the named kernels: "hessian_gram", "chol_update", "sba_klgemm",
- * "sqc_calibrate", "pack_planes".  slim_timing_read synchronises those events
+ * "sqc_calibrate", "pack_planes", "qlinear" (its one or two kernels).
+ * slim_timing_read synchronises those events
  * and returns the summed milliseconds and the launch count since the last
  * reset.  Returns SLIM_E_PARAM for an unknown name.
  * ---------------------------------------------------------------------- */

@@ -40,6 +40,9 @@ _SIGS = {
     "slim_tau_table": (_c_int, [_c_dbl, _c_int, _c_vp]),
     "slim_pack_words": (_c_i64, [_c_i64, _c_i64, _c_int]),
     "slim_pack": (_c_int, [_c_vp, _c_i64, _c_i64, _c_int, _c_vp, _c_int, _c_vp, _c_vp, _c_vp]),
+    "slim_qlinear_workspace": (_c_sz, [_c_i64, _c_i64, _c_i64, _c_int]),
+    "slim_qlinear": (_c_int, [_c_vp, _c_int, _c_i64, _c_i64, _c_vp, _c_vp, _c_int, _c_vp, _c_vp, _c_i64, _c_int,
+                              _c_vp, _c_vp, _c_sz, _c_vp]),
     "slim_timing_enable": (_c_int, [_c_int]),
     "slim_timing_reset": (_c_int, []),
     "slim_timing_read": (_c_int, [ctypes.c_char_p, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(_c_i64)]),
@@ -250,6 +253,20 @@ def pack(codes, bits, group: int, avg_bits: int):
     check(lib.slim_pack(_ptr(codes), n, m, group, _ptr(bits), int(avg_bits), _ptr(packed), _ptr(info),
                         _stream(codes.device)), "slim_pack")
     return packed[:words], info
+
+
+def qlinear(X, packed, bits, scale, zero, group: int, avg_bits: int):
+    """Y = X W_hat^T from the packed planes: X [t, m] bf16/f32 (t <= 8) -> Y float32 [t, n]."""
+    torch = _torch()
+    lib = load_library()
+    X, packed, bits, scale, zero = _dev(X), _dev(packed), _dev(bits), _dev(scale), _dev(zero)
+    T, m = X.shape
+    n = scale.shape[0]
+    Y = torch.empty((T, n), dtype=torch.float32, device=X.device)
+    ws = _ws(lib.slim_qlinear_workspace(T, n, m, group), X.device)
+    check(lib.slim_qlinear(_ptr(X), _dtype_code(X), T, m, _ptr(packed), _ptr(bits), int(avg_bits), _ptr(scale),
+                           _ptr(zero), n, group, _ptr(Y), _ptr(ws), ws.numel(), _stream(X.device)), "slim_qlinear")
+    return Y
 
 
 def tau_table(lam: float = 0.1, n_tau: int = 50) -> np.ndarray:

@@ -34,7 +34,7 @@ std::mutex g_timer_mu;
 bool g_timer_on = false;
 TimerSlot g_slots[slim::K_NUM_TIMED];
 const char *g_timer_names[slim::K_NUM_TIMED] = {"hessian_gram", "chol_update", "sba_klgemm", "sqc_calibrate",
-                                                "pack_planes"};
+                                                "pack_planes", "qlinear"};
 
 void drain(TimerSlot &s) {
   for (auto &pr : s.pending) {
@@ -219,6 +219,31 @@ int slim_pack(const uint8_t *codes, int64_t n, int64_t m, int group, const int8_
   if (!codes || !bits || !packed) return SLIM_E_NULL;
   if (!aligned16(codes) || !aligned16(packed)) return SLIM_E_ALIGN;
   hipError_t e = slim::launch_pack(codes, n, m, group, bits, avg_bits, packed, info, (hipStream_t)stream);
+  return e == hipSuccess ? SLIM_OK : hip_fail(e);
+}
+
+// ---------------------------------------------------------------- packed linear layer
+size_t slim_qlinear_workspace(int64_t t, int64_t n, int64_t m, int group) {
+  if (t < 1 || t > SLIM_QLINEAR_MAX_T || n < 1 || m < 1 || m > SLIM_MAX_WIDTH || !valid_group(group) || m % group)
+    return 0;
+  return slim::qlinear_plan((int)t, n, m, group).ws_bytes;
+}
+
+int slim_qlinear(const void *X, int xdt, int64_t t, int64_t m, const uint32_t *packed, const int8_t *bits,
+                 int avg_bits, const float *scale, const float *zero, int64_t n, int group, float *Y, void *ws,
+                 size_t ws_bytes, void *stream) {
+  if (!X || !packed || !bits || !scale || !zero || !Y) return SLIM_E_NULL;
+  if (!valid_dtype(xdt)) return SLIM_E_DTYPE;
+  if (t < 1 || t > SLIM_QLINEAR_MAX_T || n < 1 || m < 1 || m > SLIM_MAX_WIDTH) return SLIM_E_SHAPE;
+  if (!valid_group(group) || m % group) return SLIM_E_SHAPE;
+  if (avg_bits < 1 || avg_bits > 8) return SLIM_E_PARAM;
+  if (!aligned16(packed) || !aligned16(X)) return SLIM_E_ALIGN;
+  const slim::QlinearPlan p = slim::qlinear_plan((int)t, n, m, group);
+  if (!ws || ws_bytes < p.ws_bytes) return SLIM_E_WORKSPACE;
+  if (!aligned16(ws)) return SLIM_E_ALIGN;
+  hipError_t e = slim::launch_qlinear(X, xdt == SLIM_BF16, (int)t, m, packed, bits, avg_bits, scale, zero, n, group, Y,
+                                      ws, p,
+                                      (hipStream_t)stream);
   return e == hipSuccess ? SLIM_OK : hip_fail(e);
 }
 

@@ -10,7 +10,7 @@ namespace slim {
 // timing is enabled; no-ops otherwise.
 void timer_begin(int kernel_id, hipStream_t st);
 void timer_end(int kernel_id, hipStream_t st);
-enum TimedKernel { K_HESSIAN = 0, K_CHOL_UPDATE, K_SBA_KLGEMM, K_SQC, K_PACK, K_NUM_TIMED };
+enum TimedKernel { K_HESSIAN = 0, K_CHOL_UPDATE, K_SBA_KLGEMM, K_SQC, K_PACK, K_QLINEAR, K_NUM_TIMED };
 
 inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
@@ -58,5 +58,17 @@ hipError_t launch_sqc(const void *W, bool bf16, int64_t n, int64_t m, int group,
 // ---- Pack ----
 hipError_t launch_pack(const uint8_t *codes, int64_t n, int64_t m, int group, const int8_t *bits,
                        int avg_bits, uint32_t *packed, int32_t *info, hipStream_t st);
+
+// ---- Mixed-precision linear layer on the packed planes ----
+struct QlinearPlan {
+  int k, gpw, nrun;          // groups, groups per workgroup, runs of groups
+  int64_t nrb;               // row blocks of 256
+  size_t lds_bytes;          // group tables per workgroup
+  size_t ws_bytes;           // partial sums [nrun, t, n] f32 when nrun > 1
+};
+QlinearPlan qlinear_plan(int t, int64_t n, int64_t m, int group);
+hipError_t launch_qlinear(const void *X, bool bf16, int t, int64_t m, const uint32_t *packed, const int8_t *bits,
+                          int N, const float *scale, const float *zero, int64_t n, int group, float *Y, void *ws,
+                          const QlinearPlan &p, hipStream_t st);
 
 }  // namespace slim

@@ -136,3 +136,18 @@ def test_sba_variant_validation(lib):
     assert call(obj=2) == -4 and call(obj=-1) == -4
     assert lib.slim_sba_search_ex(FAKE, 1, 100, FAKE, 1, 64, 96, 128, FAKE, None, 2, 0, FAKE, FAKE, FAKE, FAKE,
                                   1 << 40, None) == -2
+
+
+def test_qlinear_validation(lib):
+    def call(**kw):
+        return lib.slim_qlinear(kw.get("X", FAKE), kw.get("xdt", 1), kw.get("t", 1), kw.get("m", 256), FAKE, FAKE,
+                                kw.get("N", 2), FAKE, FAKE, kw.get("n", 64), kw.get("g", 128), FAKE, FAKE,
+                                kw.get("ws", 1 << 40), None)
+    assert call(X=None) == -1
+    assert call(xdt=3) == -3
+    assert call(t=0) == -2 and call(t=9) == -2
+    assert call(m=96) == -2
+    assert call(N=9) == -4
+    assert call(ws=0) == -5
+    assert lib.slim_qlinear_workspace(1, 4096, 4096, 128) > 0
+    assert lib.slim_qlinear_workspace(9, 4096, 4096, 128) == 0
