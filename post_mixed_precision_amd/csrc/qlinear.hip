@@ -17,16 +17,18 @@
 // masked X values (16 entries per position), so each 32-bit plane word costs
 // eight table reads, each giving the value for every token of the batch.
 //
-// Work: one output row per thread, 256 rows and a run of consecutive groups
-// per workgroup.  The workgroup tables all the groups of its run once (the
-// first group's plane words are already in flight), then each thread walks
-// the run, loading the next group's plane words, scale and zero while it sums
-// the current one; a thread's words of one plane are adjacent (g/32 words),
-// so a wave reads 64 g/8 contiguous bytes per plane.  The width prefix and
-// check are taken by every wave from the k widths (at most 2048 bytes,
-// cached).  When one run covers all groups the workgroup writes Y; otherwise
-// the runs' partial sums are added in run order by a second kernel, so for a
-// given t results are reproducible.
+// Work: one output row per thread, 256 rows and a run of at most eight
+// consecutive groups per workgroup.  The run's scale and zero (16-byte loads
+// of four groups when aligned: a row's values sit k floats apart) and the X
+// values for the tables go out before the width scan, which every wave takes
+// from the k widths (at most 2048 bytes, cached).  The workgroup tables all
+// the groups of its run once, behind one barrier.  A run's planes are
+// consecutive plane slots of the layout, so each thread then walks them in
+// one loop, its g/32 words of the next plane in flight while it sums the
+// current one (a wave reads 64 g/8 contiguous bytes per plane).  When one run
+// covers all groups the workgroup writes Y; otherwise the runs' partial sums
+// are added in run order by a second kernel, so for a given t results are
+// reproducible.
 #include <algorithm>
 
 #include "common.hpp"
@@ -38,25 +40,29 @@ typedef __attribute__((address_space(3))) float lds_f32;
 typedef unsigned int ql_u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int ql_u32x2 __attribute__((ext_vector_type(2)));
 
-// Table layout.  One table per (group of the run, token chunk); entry
-// (pos, mask, token a) holds the sum of the X values of token a at the
-// 4-column position pos selected by mask.  Tokens are kept in chunks of
-// VW = min(QT, 4) adjacent floats so one ds_read fetches a chunk, and the 16
-// masks of a chunk are contiguous, so the lanes' reads of one position fall
-// in distinct banks.  A position's block is padded to 256 bytes, so the LDS
-// address of an entry is the block address with its low byte replaced by
-// mask * 4 VW: one byte permute per lookup.
+// Table layout.  One table per group of the run; entry (pos, mask, token a)
+// holds the sum of the X values of token a at the 4-column position pos
+// selected by mask.  Tokens are kept in chunks of VW = min(QT, 4) adjacent
+// floats so one ds_read fetches a chunk, and the 16 masks of a chunk are
+// contiguous (64 VW bytes), so the lanes' reads of one position fall in
+// distinct banks.  Blocks are packed 4 / VW to a 256-byte page, so the LDS
+// address of an entry is its page address with the low byte replaced by
+// (block within the page, mask): one byte permute per lookup.
 template <int QT, int G>
 struct QlTab {
-  static constexpr int VW = QT < 4 ? QT : 4;        // tokens per chunk
-  static constexpr int CH = QT / VW;                // chunks
+  static constexpr int VW = QT < 4 ? QT : 4;                   // tokens per chunk
+  static constexpr int CH = QT / VW;                           // chunks
   static constexpr int SH = VW == 1 ? 2 : (VW == 2 ? 3 : 4);   // log2 of a mask's stride in bytes
+  static constexpr int SUB = 4 / VW;                           // blocks per 256-byte page
   static constexpr int NPOS = G / 4;
-  static constexpr int BLK = 64;                    // floats per (position, chunk) block: 256 bytes
-  static constexpr int GROUP = NPOS * CH * BLK;     // floats per group
+  static constexpr int GROUP = NPOS * 16 * QT;                 // floats per group (a multiple of 64)
   __device__ static constexpr int at(int pos, int mask, int a) {
-    return (pos * CH + a / VW) * BLK + mask * VW + a % VW;
+    return ((pos * CH + a / VW) * 16 + mask) * VW + a % VW;
   }
+  // low-byte bits naming the block within its page, for the even (lo) and
+  // odd (hi) nibbles of a word: nibble h is position 8 w + h, block h % SUB
+  static constexpr uint32_t LO_OR = VW == 1 ? 0x80008000u : 0u;
+  static constexpr uint32_t HI_OR = VW == 1 ? 0xC040C040u : (VW == 2 ? 0x80808080u : 0u);
 };
 
 template <int VW>
@@ -80,7 +86,7 @@ __device__ __forceinline__ void ql_x4(const void *Xv, int64_t idx, float &x0, fl
   }
 }
 
-constexpr int QL_TABS = 16;    // group tables per workgroup (groups of a run x token chunks of 4)
+constexpr int QL_RUN = 8;      // most groups per run (scale and zero of the run are held in registers)
 
 template <bool BF16, int QT, int G>
 __global__ __launch_bounds__(256) void qlinear_kernel(const void *__restrict__ Xv, int t, int64_t m,
@@ -97,82 +103,97 @@ __global__ __launch_bounds__(256) void qlinear_kernel(const void *__restrict__ X
   constexpr int MPL = 16 / LPP;        // masks per lane while tabling
   constexpr int LB = MPL == 8 ? 3 : (MPL == 4 ? 2 : 1);
   extern __shared__ __align__(256) float lut[];      // [gpw][GROUP]
-  __shared__ float xsum[QL_TABS * 4];                // [gpw][QT]
+  __shared__ float xsum[QL_RUN * QT];                // [gpw][QT]
+  __shared__ int wrun[QL_RUN];                       // widths of the run's groups
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int64_t i = (int64_t)blockIdx.x * 256 + tid;
   const bool live = i < n;
+  const int64_t il = live ? i : n - 1;   // rows past the end load row n - 1 and store nothing
   const int gc = blockIdx.y;
-  const int j0 = gc * gpw, j1 = min(k, j0 + gpw);
+  const int j0 = gc * gpw, j1 = min(k, j0 + gpw), nq = j1 - j0;
 
-  // widths: the check, and the plane count before the run (every wave alike)
-  int before = 0, total = 0, bad = 0;
+  // loads that need no width go out first: this wave's first table unit of
+  // X, and the run's scale and zero
+  const int tpos = lane / LPP, m0 = (lane % LPP) * MPL;
+  float xf[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+  if (wave < nq * QT && wave % QT < t)
+    ql_x4<BF16>(Xv, (int64_t)(wave % QT) * m + (int64_t)(j0 + wave / QT) * G + 4 * tpos, xf[0], xf[1], xf[2], xf[3]);
+  // scale and zero of the run, four groups per 16-byte load when szv says the
+  // rows allow it (a row's values sit k floats apart: a load per group would
+  // touch a cache line per lane)
+  float sreg[QL_RUN], zreg[QL_RUN];
+  if (szv) {
+#pragma unroll
+    for (int r = 0; r < QL_RUN; r += 4) {
+      float4 sv = make_float4(0.0f, 0.0f, 0.0f, 0.0f), zv = sv;
+      if (r < nq) {
+        sv = *(const float4 *)(scale + il * k + j0 + r);
+        zv = *(const float4 *)(zero + il * k + j0 + r);
+      }
+      sreg[r] = sv.x; sreg[r + 1] = sv.y; sreg[r + 2] = sv.z; sreg[r + 3] = sv.w;
+      zreg[r] = zv.x; zreg[r + 1] = zv.y; zreg[r + 2] = zv.z; zreg[r + 3] = zv.w;
+    }
+  } else {
+#pragma unroll
+    for (int r = 0; r < QL_RUN; ++r) {
+      sreg[r] = r < nq ? scale[il * k + j0 + r] : 0.0f;
+      zreg[r] = r < nq ? zero[il * k + j0 + r] : 0.0f;
+    }
+  }
+
+  // widths: the check, the planes before the run and in it (every wave alike)
+  int before = 0, inrun = 0, total = 0, bad = 0;
   for (int j = lane; j < k; j += 64) {
     const int b = bits[j];
     bad |= (b < 1 || b > 8);
     total += b;
     if (j < j0) before += b;
+    if (j >= j0 && j < j1) {
+      inrun += b;
+      if (wave == 0) wrun[j - j0] = b;
+    }
   }
 #pragma unroll
   for (int s = 32; s > 0; s >>= 1) {
     before += __shfl_xor(before, s, 64);
+    inrun += __shfl_xor(inrun, s, 64);
     total += __shfl_xor(total, s, 64);
     bad |= __shfl_xor(bad, s, 64);
   }
   const bool ok = !bad && total == k * N;
+  const int P0 = __builtin_amdgcn_readfirstlane(before);
+  const int P1 = P0 + __builtin_amdgcn_readfirstlane(inrun);   // the run's planes are P0 .. P1 - 1
 
-  // plane words of the current group, loaded at the top of its step (the
-  // first group's while the tables are built); scale and zero come four
-  // groups per 16-byte load when szv says the rows allow it (a row's values
-  // sit k floats apart, so a load per group would touch a line per lane)
-  uint32_t cur[8][WPS];
-  float4 s4 = make_float4(0.0f, 0.0f, 0.0f, 0.0f), z4 = s4;
-  float sc = 0.0f, zr = 0.0f;
-  auto load = [&](int j, int pre) __attribute__((always_inline)) {
-    const int bq = bits[j];
-    const int64_t off = (int64_t)pre * n * WPS;
-#pragma unroll
-    for (int p = 0; p < 8; ++p) {
-      if (live && p < bq) {
-        const uint32_t *src = packed + off + ((int64_t)p * n + i) * WPS;
-        if constexpr (WPS == 4) {
-          const ql_u32x4 v = __builtin_nontemporal_load((const ql_u32x4 *)src);
-          cur[p][0] = v.x; cur[p][1] = v.y; cur[p][2] = v.z; cur[p][3] = v.w;
-        } else if constexpr (WPS == 2) {
-          const ql_u32x2 v = __builtin_nontemporal_load((const ql_u32x2 *)src);
-          cur[p][0] = v.x; cur[p][1] = v.y;
-        } else {
-          cur[p][0] = __builtin_nontemporal_load(src);
-        }
-      } else {
-#pragma unroll
-        for (int w = 0; w < WPS; ++w) cur[p][w] = 0u;
-      }
-    }
-    if (szv) {
-      const int r = (j - j0) & 3;
-      if (r == 0 && live) {
-        s4 = *(const float4 *)(scale + i * k + j);
-        z4 = *(const float4 *)(zero + i * k + j);
-      }
-      sc = r == 0 ? s4.x : (r == 1 ? s4.y : (r == 2 ? s4.z : s4.w));
-      zr = r == 0 ? z4.x : (r == 1 ? z4.y : (r == 2 ? z4.z : z4.w));
+  // The run's planes are consecutive plane slots of the layout, so the walk
+  // is one loop over them: a thread's words of plane P (g/32 adjacent words,
+  // a wave reads 64 g/8 contiguous bytes) are loaded one plane ahead of use.
+  const uint32_t *prow = packed + il * WPS;
+  const int64_t pstride = n * WPS;
+  auto ldp = [&](int P, uint32_t (&d)[WPS]) __attribute__((always_inline)) {
+    const uint32_t *src = prow + (int64_t)P * pstride;
+    if constexpr (WPS == 4) {
+      const ql_u32x4 v = __builtin_nontemporal_load((const ql_u32x4 *)src);
+      d[0] = v.x; d[1] = v.y; d[2] = v.z; d[3] = v.w;
+    } else if constexpr (WPS == 2) {
+      const ql_u32x2 v = __builtin_nontemporal_load((const ql_u32x2 *)src);
+      d[0] = v.x; d[1] = v.y;
     } else {
-      sc = live ? scale[i * k + j] : 0.0f;
-      zr = live ? zero[i * k + j] : 0.0f;
+      d[0] = __builtin_nontemporal_load(src);
     }
   };
-  int pre = before;
-  if (ok) load(j0, pre);   // in flight while the tables are built
-
+  uint32_t b0[WPS], b1[WPS];
+  if (ok && P0 < P1) ldp(P0, b0);   // in flight while the tables are built
   // tables: wave w builds (group q, token a) units w, w + 4, ...; a lane covers
   // position tpos and masks m0 .. m0 + MPL - 1
   {
-    const int tpos = lane / LPP, m0 = (lane % LPP) * MPL;
-    for (int u = wave; u < (j1 - j0) * QT; u += 4) {
+    for (int u = wave; u < nq * QT; u += 4) {
       const int q = u / QT, a = u % QT;
-      float x0 = 0.0f, x1 = 0.0f, x2 = 0.0f, x3 = 0.0f;
-      if (a < t) ql_x4<BF16>(Xv, (int64_t)a * m + (int64_t)(j0 + q) * G + 4 * tpos, x0, x1, x2, x3);
+      float x0 = xf[0], x1 = xf[1], x2 = xf[2], x3 = xf[3];
+      if (u != wave) {
+        x0 = x1 = x2 = x3 = 0.0f;
+        if (a < t) ql_x4<BF16>(Xv, (int64_t)a * m + (int64_t)(j0 + q) * G + 4 * tpos, x0, x1, x2, x3);
+      }
       const float xv[4] = {x0, x1, x2, x3};
       float base = 0.0f;
 #pragma unroll
@@ -203,108 +224,107 @@ __global__ __launch_bounds__(256) void qlinear_kernel(const void *__restrict__ X
   for (int a = 0; a < QT; ++a) y[a] = ok ? 0.0f : __builtin_nanf("");
   if (ok) {
     const uint32_t lbase = (uint32_t)(uintptr_t)(lds_f32 *)lut;
-    for (int j = j0; j < j1; ++j) {
-      const int bq = bits[j];
-      if (j > j0) load(j, pre);
-      pre += bq;
-      const int q = j - j0;
+    int q = 0, p = 0, bq = __builtin_amdgcn_readfirstlane(wrun[0]);
+    float acc[QT];
+#pragma unroll
+    for (int a = 0; a < QT; ++a) acc[a] = 0.0f;
+    // one plane: sum the table entries its nibbles select, weight 2^p; at the
+    // group's last plane apply scale and zero
+    auto plane = [&](const uint32_t (&cw)[WPS]) __attribute__((always_inline)) {
       const uint32_t gbase = lbase + (uint32_t)(q * TB::GROUP * 4);
-      float acc[QT];
+      float pa[QT];
 #pragma unroll
-      for (int a = 0; a < QT; ++a) acc[a] = 0.0f;
+      for (int a = 0; a < QT; ++a) pa[a] = 0.0f;
+      auto addr_of = [&](uint32_t lo, uint32_t hi, int w, int h, int c) __attribute__((always_inline)) {
+        const int blk = (8 * w + h) * TB::CH + c;                       // block of (position, chunk)
+        const uint32_t page = gbase + (uint32_t)((blk / TB::SUB) * 256);
+        // page bytes 3..1, then byte h / 2 of lo or hi: (block in page, mask)
+        return __builtin_amdgcn_perm(page, (h & 1) ? hi : lo, 0x07060500u | (uint32_t)(h >> 1));
+      };
+      auto add = [&](vec_t x, int c) __attribute__((always_inline)) {
+        if constexpr (TB::VW == 1) {
+          pa[c] += x;
+        } else {
 #pragma unroll
-      for (int p = 0; p < 8; ++p) {
-        if (p < bq) {
-          float pa[QT];
+          for (int e = 0; e < TB::VW; ++e) pa[c * TB::VW + e] += x[e];
+        }
+      };
+      // (lo, hi): bytes holding the even / odd nibbles of a word, scaled to the
+      // mask stride, with the block-in-page bits
+      auto split = [&](uint32_t wd, uint32_t &lo, uint32_t &hi) __attribute__((always_inline)) {
+        lo = ((wd << TB::SH) & (0x0f0f0f0fu << TB::SH)) | TB::LO_OR;
+        hi = (TB::SH == 4 ? (wd & 0xf0f0f0f0u) : ((wd >> (4 - TB::SH)) & (0x0f0f0f0fu << TB::SH))) | TB::HI_OR;
+      };
+      if constexpr (QT <= 2) {
+        // reads of the next word pair are issued before the adds of this one
+        constexpr int WPC = QT == 1 ? (WPS < 2 ? WPS : 2) : 1;   // words per chunk
+        constexpr int NCK = WPS / WPC;
+        constexpr int RPC = WPC * 8 * TB::CH;
+        vec_t v[2][RPC];
+        auto issue = [&](int ck, vec_t (&dst)[RPC]) __attribute__((always_inline)) {
 #pragma unroll
-          for (int a = 0; a < QT; ++a) pa[a] = 0.0f;
-          // table reads for one chunk of words are issued before the adds of
-          // the previous chunk, so each wave keeps two chunks of reads in
-          // flight (chunks of 2 words for one token, 1 word for two; larger
-          // batches have enough adds per read and are left to the scheduler)
-          constexpr int WPC = QT == 1 ? (WPS < 2 ? WPS : 2) : 1;    // words per chunk
-          constexpr int NCK = WPS / WPC;
-          constexpr int RPC = WPC * 8 * TB::CH;                      // reads per chunk
-          constexpr bool PIPE = QT <= 2;
-          vec_t v[PIPE ? 2 : 1][PIPE ? RPC : 1];
-          auto issue = [&](int ck, vec_t (&dst)[RPC]) __attribute__((always_inline)) {
+          for (int ww = 0; ww < WPC; ++ww) {
+            const int w = ck * WPC + ww;
+            uint32_t lo, hi;
+            split(cw[w], lo, hi);
 #pragma unroll
-            for (int ww = 0; ww < WPC; ++ww) {
-              const int w = ck * WPC + ww;
-              // bytes of lo / hi: the even / odd nibbles of the word, times the mask stride
-              const uint32_t wd = cur[p][w];
-              const uint32_t lo = (wd << TB::SH) & (0x0f0f0f0fu << TB::SH);
-              const uint32_t hi =
-                  TB::SH == 4 ? (wd & 0xf0f0f0f0u) : ((wd >> (4 - TB::SH)) & (0x0f0f0f0fu << TB::SH));
+            for (int h = 0; h < 8; ++h)
 #pragma unroll
-              for (int h = 0; h < 8; ++h) {
-                const int pos = 8 * w + h;
-#pragma unroll
-                for (int c = 0; c < TB::CH; ++c) {
-                  const uint32_t blk = gbase + (uint32_t)((pos * TB::CH + c) * TB::BLK * 4);
-                  // address = block bytes 3..1, nibble byte (h / 2) of lo or hi
-                  const uint32_t addr =
-                      __builtin_amdgcn_perm(blk, (h & 1) ? hi : lo, 0x07060500u | (uint32_t)(h >> 1));
-                  dst[(ww * 8 + h) * TB::CH + c] = *(const __attribute__((address_space(3))) vec_t *)(uintptr_t)addr;
-                }
-              }
-            }
-          };
-          auto consume = [&](const vec_t (&src)[RPC]) __attribute__((always_inline)) {
-#pragma unroll
-            for (int r = 0; r < WPC * 8; ++r) {
-#pragma unroll
-              for (int c = 0; c < TB::CH; ++c) {
-                const vec_t x = src[r * TB::CH + c];
-                if constexpr (TB::VW == 1) {
-                  pa[c] += x;
-                } else {
-#pragma unroll
-                  for (int e = 0; e < TB::VW; ++e) pa[c * TB::VW + e] += x[e];
-                }
-              }
-            }
-          };
-          if constexpr (PIPE) {
-            issue(0, v[0]);
-#pragma unroll
-            for (int ck = 0; ck < NCK; ++ck) {
-              if (ck + 1 < NCK) issue(ck + 1, v[(ck + 1) & 1]);
-              __builtin_amdgcn_sched_barrier(0);
-              consume(v[ck & 1]);
-            }
-          } else {
-#pragma unroll
-            for (int w = 0; w < WPS; ++w) {
-              const uint32_t wd = cur[p][w];
-              const uint32_t lo = (wd << TB::SH) & (0x0f0f0f0fu << TB::SH);
-              const uint32_t hi =
-                  TB::SH == 4 ? (wd & 0xf0f0f0f0u) : ((wd >> (4 - TB::SH)) & (0x0f0f0f0fu << TB::SH));
-#pragma unroll
-              for (int h = 0; h < 8; ++h) {
-#pragma unroll
-                for (int c = 0; c < TB::CH; ++c) {
-                  const uint32_t blk = gbase + (uint32_t)(((8 * w + h) * TB::CH + c) * TB::BLK * 4);
-                  const uint32_t addr =
-                      __builtin_amdgcn_perm(blk, (h & 1) ? hi : lo, 0x07060500u | (uint32_t)(h >> 1));
-                  const vec_t x = *(const __attribute__((address_space(3))) vec_t *)(uintptr_t)addr;
-                  if constexpr (TB::VW == 1) {
-                    pa[c] += x;
-                  } else {
-#pragma unroll
-                    for (int e = 0; e < TB::VW; ++e) pa[c * TB::VW + e] += x[e];
-                  }
-                }
-              }
-            }
+              for (int c = 0; c < TB::CH; ++c)
+                dst[(ww * 8 + h) * TB::CH + c] =
+                    *(const __attribute__((address_space(3))) vec_t *)(uintptr_t)addr_of(lo, hi, w, h, c);
           }
-          const float pw2 = (float)(1 << p);
+        };
+        issue(0, v[0]);
 #pragma unroll
-          for (int a = 0; a < QT; ++a) acc[a] = __builtin_fmaf(pw2, pa[a], acc[a]);
+        for (int ck = 0; ck < NCK; ++ck) {
+          if (ck + 1 < NCK) issue(ck + 1, v[(ck + 1) & 1]);
+          __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+          for (int r = 0; r < WPC * 8; ++r)
+#pragma unroll
+            for (int c = 0; c < TB::CH; ++c) add(v[ck & 1][r * TB::CH + c], c);
+        }
+      } else {
+#pragma unroll
+        for (int w = 0; w < WPS; ++w) {
+          uint32_t lo, hi;
+          split(cw[w], lo, hi);
+#pragma unroll
+          for (int h = 0; h < 8; ++h)
+#pragma unroll
+            for (int c = 0; c < TB::CH; ++c)
+              add(*(const __attribute__((address_space(3))) vec_t *)(uintptr_t)addr_of(lo, hi, w, h, c), c);
         }
       }
+      const float pw2 = (float)(1 << p);
 #pragma unroll
-      for (int a = 0; a < QT; ++a) y[a] = __builtin_fmaf(sc, __builtin_fmaf(-zr, xsum[q * QT + a], acc[a]), y[a]);
+      for (int a = 0; a < QT; ++a) acc[a] = __builtin_fmaf(pw2, pa[a], acc[a]);
+      if (++p == bq) {
+        // the current group's scale and zero are at the front of the run's
+        // registers; shift them down for the next group
+#pragma unroll
+        for (int a = 0; a < QT; ++a) {
+          y[a] = __builtin_fmaf(sreg[0], __builtin_fmaf(-zreg[0], xsum[q * QT + a], acc[a]), y[a]);
+          acc[a] = 0.0f;
+        }
+#pragma unroll
+        for (int r = 0; r + 1 < QL_RUN; ++r) {
+          sreg[r] = sreg[r + 1];
+          zreg[r] = zreg[r + 1];
+        }
+        p = 0;
+        ++q;
+        if (q < nq) bq = __builtin_amdgcn_readfirstlane(wrun[q]);
+      }
+    };
+    for (int P = P0; P < P1; P += 2) {
+      if (P + 1 < P1) ldp(P + 1, b1);
+      plane(b0);
+      if (P + 1 < P1) {
+        if (P + 2 < P1) ldp(P + 2, b0);
+        plane(b1);
+      }
     }
   }
   if (live) {
@@ -314,41 +334,37 @@ __global__ __launch_bounds__(256) void qlinear_kernel(const void *__restrict__ X
   }
 }
 
-// Y[a, i] = sum over the runs of groups of the partial sums, in run order.
+// Y[a, i] = sum over the runs of groups of the partial sums, in run order;
+// sixteen runs' loads are in flight at a time.
 __global__ __launch_bounds__(256) void qlinear_reduce_kernel(const float *__restrict__ part, int nrun, int t,
                                                              int64_t n, float *__restrict__ Y) {
   const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (e >= (int64_t)t * n) return;
   const int64_t stride = (int64_t)t * n;
   float s = 0.0f;
-  int r = 0;
-  for (; r + 4 <= nrun; r += 4) {
-    const float a0 = part[(r + 0) * stride + e], a1 = part[(r + 1) * stride + e];
-    const float a2 = part[(r + 2) * stride + e], a3 = part[(r + 3) * stride + e];
-    s += a0;
-    s += a1;
-    s += a2;
-    s += a3;
+  for (int r0 = 0; r0 < nrun; r0 += 16) {
+    float v[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) v[r] = r0 + r < nrun ? part[(int64_t)(r0 + r) * stride + e] : 0.0f;
+#pragma unroll
+    for (int r = 0; r < 16; ++r)
+      if (r0 + r < nrun) s += v[r];
   }
-  for (; r < nrun; ++r) s += part[r * stride + e];
   Y[e] = s;
 }
 
 static int ql_qt(int t) { return t <= 1 ? 1 : (t <= 2 ? 2 : (t <= 4 ? 4 : 8)); }
 
-static size_t ql_group_bytes(int qt, int group) {
-  const int vw = qt < 4 ? qt : 4;
-  return (size_t)(group / 4) * (qt / vw) * 64 * sizeof(float);
-}
+static size_t ql_group_bytes(int qt, int group) { return (size_t)(group / 4) * 16 * qt * sizeof(float); }
 
 QlinearPlan qlinear_plan(int t, int64_t n, int64_t m, int group) {
   QlinearPlan p;
   const int qt = ql_qt(t);
   p.k = (int)(m / group);
   p.nrb = (n + 255) / 256;
-  // groups per workgroup: the tables must fit (QL_TABS tables of 4 tokens,
-  // at most 64 KiB), and the launch keeps a few workgroups per CU
-  const int gmax = (int)std::min<size_t>((size_t)QL_TABS * 4 / qt, (64u << 10) / ql_group_bytes(qt, group));
+  // groups per workgroup: at most QL_RUN, tables within 64 KiB, and enough
+  // workgroups to keep a few per CU
+  const int gmax = (int)std::min<size_t>((size_t)QL_RUN, (64u << 10) / ql_group_bytes(qt, group));
   int gpw = std::min(p.k, std::max(1, gmax));
   while (gpw > 1 && p.nrb * ((p.k + gpw - 1) / gpw) < 1024) gpw = (gpw + 1) / 2;
   p.gpw = gpw;
