@@ -102,6 +102,7 @@ def run_step(slim, X, W, group, N, ev=None, variant=None):
     mark(4)
     packed, pinfo = slim.pack(sq["codes"], bits, group, N)
     mark(5)
+    run_step.last = (bits, packed, sq["scale"], sq["zero"])   # for the serving measurement
     return info, pinfo, rs, kl
 
 
@@ -158,6 +159,54 @@ def cpu_baseline(wl, lin_idx, group, N, Xh, Wh):
     }
 
 
+def qlinear_time(slim, torch, xq, packed, bits, scale, zero, group, N, reps=50):
+    """Seconds per slim.qlinear call, from the library's HIP events around its kernels."""
+    for _ in range(5):
+        slim.qlinear(xq, packed, bits, scale, zero, group, N)
+    torch.cuda.synchronize()
+    slim.timing_enable(True)
+    slim.timing_reset()
+    for _ in range(reps):
+        slim.qlinear(xq, packed, bits, scale, zero, group, N)
+    torch.cuda.synchronize()
+    ms, calls = slim.timing_read("qlinear")
+    slim.timing_enable(False)
+    return ms / max(calls, 1) * 1e-3
+
+
+def qlinear_bench(slim, torch, args):
+    """The packed-plane linear layer alone on a synthetic N x M layer: random
+    plane words (every bit pattern is a valid code), widths avg_bits + 1 on the
+    first third of the groups and avg_bits - 1 on the last third, positive
+    scales, zeros in [0, 2^bits)."""
+    n, m = (int(v) for v in args.qlinear_shape.lower().split("x"))
+    group = args.group or 128
+    N = 2
+    k = m // group
+    bits = np.full(k, N, dtype=np.int8)
+    bits[: k // 3] = N + 1
+    bits[k - k // 3:] = N - 1
+    rng = np.random.default_rng(7)
+    words = n * m * N // 32
+    packed = torch.from_numpy(rng.integers(0, 2 ** 32, size=words, dtype=np.uint64).astype(np.uint32)
+                              .view(np.int32)).to("cuda:0")
+    bits_d = torch.from_numpy(bits).to("cuda:0")
+    scale = torch.from_numpy(rng.uniform(1e-3, 2e-2, size=(n, k)).astype(np.float32)).to("cuda:0")
+    zero = torch.from_numpy((rng.uniform(0, 1, size=(n, k)) * (2.0 ** bits[None, :] - 1)).astype(np.float32)).to("cuda:0")
+    rep = {}
+    for tq in (1, 8):
+        xq = torch.from_numpy(rng.standard_normal((tq, m)).astype(np.float32)).to("cuda:0").to(torch.bfloat16)
+        sec = qlinear_time(slim, torch, xq, packed, bits_d, scale, zero, group, N)
+        qbytes = words * 4 + 2 * n * k * 4 + tq * m * 2 + tq * n * 4
+        rep[f"t{tq}"] = {"us_per_call": round(sec * 1e6, 2), "algorithmic_bytes": qbytes,
+                         "achieved_gbps": round(qbytes / sec / 1e9, 1), "frac": round(qbytes / sec / PEAK_HBM_BPS, 4)}
+    out = {"metric": "packed-plane linear layer, GB/s of algorithmic bytes", "value": rep["t1"]["achieved_gbps"],
+           "unit": "GB/s", "n_gpus": 1, "higher_is_better": True, "dtype": "bf16", "data": "synthetic",
+           "config": {"workload": f"qlinear {n}x{m}", "n": n, "m": m, "group": group, "avg_bits": N},
+           "roofline": {"bound": "hbm", "kernel": "qlinear", "peak": PEAK_HBM_BPS / 1e9, "unit": "GB/s", **rep}}
+    print(json.dumps(out), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -173,6 +222,9 @@ def main():
                     help="group order of the SBA scan (the method's is salience)")
     ap.add_argument("--ablation-report", action="store_true",
                     help="also run the scan once per objective/order and report r* and the best score")
+    ap.add_argument("--qlinear-shape", default=None,
+                    help="NxM: time only the packed-plane linear layer on a synthetic N x M layer "
+                         "(random planes, widths avg_bits +- 1) and print its own JSON line")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="run one plain device copy of this many MiB before the steps (counter calibration)")
     args = ap.parse_args()
@@ -188,6 +240,10 @@ def main():
         from post_mixed_precision_amd import build as _b
         _b.build()
     slim.load_library()
+
+    if args.qlinear_shape:
+        qlinear_bench(slim, torch, args)
+        return
 
     wl = synth.WORKLOADS[args.workload]
     lin = wl.linears[args.linear]
@@ -297,6 +353,19 @@ def main():
             "pack_planes": {"bound": "hbm", "achieved_gbps": round(n * m * (1 + N / 8) / (pms / pl * 1e-3) / 1e9, 1),
                             "frac": round(n * m * (1 + N / 8) / (pms / pl * 1e-3) / PEAK_HBM_BPS, 4)},
         }
+    # The quantized layer served from its own planes (the deployment side):
+    # Y = X W_hat^T for decode batches, timed per call with HIP events around
+    # its kernels; outside the step's timed region.
+    bits_l, packed_l, scale_l, zero_l = run_step.last
+    qrep = {}
+    for tq in (1, 8):
+        xq = X[:tq].contiguous()
+        sec_q = qlinear_time(slim, torch, xq, packed_l, bits_l, scale_l, zero_l, group, N)
+        qbytes = packed_l.numel() * 4 + 2 * n * k * 4 + tq * m * xq.element_size() + tq * n * 4
+        qrep[f"t{tq}"] = {"us_per_call": round(sec_q * 1e6, 2), "algorithmic_bytes": qbytes,
+                          "achieved_gbps": round(qbytes / sec_q / 1e9, 1),
+                          "frac": round(qbytes / sec_q / PEAK_HBM_BPS, 4)}
+    out.setdefault("roofline_other", {})["qlinear"] = {"bound": "hbm", **qrep}
     if args.ablation_report:
         # The pages' ablation structure on this layer: the scan under each
         # objective and group order (untimed; r* and the best score).
