@@ -95,8 +95,8 @@ def test_qlinear_on_calibrated_layer(slim):
 
 
 def test_qlinear_full_size_and_batch_consistency(slim):
-    # 4096 x 4096 at 2 bits against the oracle; the 70B-shaped MLP on
-    # properties: every row of an 8-token batch agrees with the single-token
+    # 4096 x 4096 at 2 bits against the oracle; the 70B-shaped MLP on sampled
+    # rows and on properties: every row of an 8-token batch agrees with the single-token
     # result (the batch size sets how many groups one workgroup sums, so only
     # the float32 order of the group sums differs), and the product is
     # linear in X.
@@ -107,9 +107,20 @@ def test_qlinear_full_size_and_batch_consistency(slim):
     _check(Yg, X, codes, bits, scale, zero, packed, 4096, 4096, 128)
     print("qlinear 28672 x 8192 (70B MLP shape), t = 1 and 8", flush=True)
     bits, codes, scale, zero, packed = _layer(3, 28672, 8192, 128, 2)
-    del codes
     X = np.random.default_rng(4).standard_normal((8, 8192)).astype(np.float32)
     Y8 = _run(slim, X, packed, bits, scale, zero, 128, 2, "f32")
+    # sampled rows (the last row block's tail included) against the float64
+    # product of the dequantized weights, as the oracle forms it
+    rows = np.concatenate([np.random.default_rng(5).choice(28672, 61, replace=False), [0, 28670, 28671]])
+    q = codes[rows].astype(np.float32)
+    z = np.repeat(zero[rows], 128, axis=1)
+    sc = np.repeat(scale[rows], 128, axis=1)
+    Wh = ((q - z).astype(np.float32) * sc).astype(np.float32).astype(np.float64)
+    Yo = X.astype(np.float64) @ Wh.T
+    mag = np.abs(X.astype(np.float64)) @ ((q + np.abs(z)) * sc).astype(np.float64).T
+    err = np.abs(Y8[:, rows].astype(np.float64) - Yo)
+    assert np.all(err <= 3e-5 * mag + 1e-30), float(np.max(err / (3e-5 * mag + 1e-30)))
+    del codes
     for a in (0, 5, 7):
         Y1 = _run(slim, X[a:a + 1], packed, bits, scale, zero, 128, 2, "f32")
         np.testing.assert_allclose(Y1[0], Y8[a], rtol=1e-5, atol=1e-5 * float(np.abs(Y8[a]).max()))
