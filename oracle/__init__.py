@@ -38,6 +38,7 @@ from .sba import (rank_groups, allocation, trial_weights, kl_divergence, output_
 from .sqc import mask_3sigma, sqc_calibrate
 from .pack import pack_bitplanes, unpack_bitplanes, packed_words
 from .qlinear import dequant_weights, qlinear
+from .gptq import upper_chol_inverse, gptq_quantize
 from .pipeline import quantize_layer
 
 __all__ = [
@@ -45,5 +46,6 @@ __all__ = [
     "element_salience", "group_salience", "salience", "tau_grid", "minmax_params",
     "fake_quant", "quant_codes", "rank_groups", "allocation", "trial_weights",
     "kl_divergence", "sba_search", "mask_3sigma", "sqc_calibrate", "pack_bitplanes",
-    "unpack_bitplanes", "packed_words", "quantize_layer",
+    "unpack_bitplanes", "packed_words", "quantize_layer", "dequant_weights", "qlinear",
+    "upper_chol_inverse", "gptq_quantize",
 ]
