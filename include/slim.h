@@ -12,6 +12,7 @@
  *   slim_sba_search     balanced bit allocation scored by output KL           (component one)
  *   slim_sba_search_ex  the same with an output-MSE objective or a given group order (ablations)
  *   slim_sqc_calibrate  3-sigma mask + tau-grid search of scale and zero       (component two)
+ *   slim_gptq_quantize  the same quantizer inside GPTQ's error-compensating sweep  (core design: GPTQ backbone)
  *   slim_pack           group-structured bit-planes, no bitmap                (FAQ: storage)
  *   slim_qlinear        Y = X W_hat^T read from the planes (decode batches)    (FAQ: deployment)
  *
@@ -194,6 +195,37 @@ int slim_sqc_calibrate(const void *W, int wdt, int64_t n, int64_t m, int group, 
 int slim_tau_table(double lambda, int n_tau, float *out_host);
 
 /* ------------------------------------------------------------------------
+ * GPTQ sweep with the SliM-LLM group quantizer (rkmt.cn digest, core design
+ * and the FAQ on GPTQ / AWQ / OmniQuant: SliM-LLM plugs SBA and SQC into
+ * GPTQ's layer-wise backbone; GPTQ, Frantar et al., ICLR 2023).
+ *
+ * Columns are quantized in order.  With H_d = H + damp_frac * mean(diag H) * I
+ * and U the upper Cholesky factor of H_d^-1 (H_d^-1 = U^T U), after column c
+ *     e_c = (w_c - w_hat_c) / U_cc,   w_c' -= e_c U[c, c']  for every c' > c,
+ * in float64.  Group q's quantizer is fixed when the sweep reaches its first
+ * column: the slim_sqc_calibrate calibration (same lambda, n_tau, hinv_diag)
+ * of the group's current weights rounded to float32, at width bits[q].
+ * Each column's code is that quantizer's float32 decision on its current
+ * weight rounded to float32; w_hat = (q - zero) * scale.
+ *
+ * H: float32 [m, m] (slim_hessian's output, undamped); W: [n, m] (dtype
+ * wdt); bits int8 [k] (widths in [1, 8], e.g. from slim_sba_search);
+ * hinv_diag float32 [m] (slim_salience's, same damp_frac).  Outputs: scale,
+ * zero float32 [n, k]; codes uint8 [n, m]; mask uint32 [n, m/32] (the
+ * 3-sigma mask of each group's calibration); tau_idx uint8 [n, k] or NULL;
+ * info int32 [1] (LAPACK convention for H_d; -1 for non-finite H or W;
+ * outputs unspecified when info != 0).  Workspace:
+ * slim_gptq_workspace(n, m, g) bytes (8 (2 m_p^2 + m^2 + n m) + 4 n m bytes
+ * and change, m_p = m rounded up to 64).  Requires n >= 1, m % group == 0,
+ * damp_frac >= 0, the lambda / n_tau ranges of slim_sqc_calibrate.
+ * ---------------------------------------------------------------------- */
+size_t slim_gptq_workspace(int64_t n, int64_t m, int group);
+int slim_gptq_quantize(const float *H, int64_t m, double damp_frac, const void *W, int wdt, int64_t n, int group,
+                       const int8_t *bits, const float *hinv_diag, double lambda, int n_tau, float *scale,
+                       float *zero, uint8_t *codes, uint32_t *mask, uint8_t *tau_idx, int32_t *info, void *ws,
+                       size_t ws_bytes, void *stream);
+
+/* ------------------------------------------------------------------------
  * Packing (FAQ on storage: group-wise bit-widths need no bitmap or codebook
  * and no extra storage; dequantization keeps the uniform-quantizer form).
  *
@@ -238,7 +270,8 @@ int slim_qlinear(const void *X, int xdt, int64_t t, int64_t m, const uint32_t *p
  * Kernel timing (instrumentation, not part of the method).  When enabled,
  * the library records a pair of HIP events on the launch stream around every
  * launch of the named kernels: "hessian_gram", "chol_update", "sba_klgemm",
- * "sqc_calibrate", "pack_planes", "qlinear" (its one or two kernels).
+ * "sqc_calibrate", "pack_planes", "qlinear" (its one or two kernels),
+ * "gptq_sweep", "gptq_trail" (per group).
  * slim_timing_read synchronises those events
  * and returns the summed milliseconds and the launch count since the last
  * reset.  Returns SLIM_E_PARAM for an unknown name.

@@ -79,7 +79,9 @@ def gptq_quantize(W, H, bits, d32, group: int, damp_frac: float = 0.01, lam: flo
     diag(H_d^-1).  Returns a dict with codes [n, m] uint8, scale / zero
     [n, k] float32, tau_idx [n, k] uint8, mask [n, m] bool, what [n, m]
     float32, err [n, m] float64, gap [n, k] (SQC's relative gap between its
-    two best candidates at each calibration), U and info."""
+    two best candidates at each calibration), margin [n, m] (each weight's
+    distance to the 3-sigma thresholds of its calibration, in sigmas), U and
+    info."""
     Wc = as_f64(W).copy()
     n, m = Wc.shape
     k = m // group
@@ -97,6 +99,7 @@ def gptq_quantize(W, H, bits, d32, group: int, damp_frac: float = 0.01, lam: flo
     zero = np.zeros((n, k), dtype=np.float32)
     tau_idx = np.zeros((n, k), dtype=np.uint8)
     gap = np.zeros((n, k))
+    margin = np.zeros((n, m))
     for j in range(k):
         c0, c1 = j * group, (j + 1) * group
         # the group's quantizer, on its current weights
@@ -105,6 +108,7 @@ def gptq_quantize(W, H, bits, d32, group: int, damp_frac: float = 0.01, lam: flo
         z = sq["zero"][:, 0]
         scale[:, j], zero[:, j], tau_idx[:, j], gap[:, j] = s, z, sq["tau_idx"][:, 0], sq["gap"][:, 0]
         mask[:, c0:c1] = sq["mask_bool"]
+        margin[:, c0:c1] = sq["margin"]
         maxq = np.full((n, 1), (1 << int(b[j])) - 1, dtype=np.float32)
         E = np.zeros((n, group))
         for c in range(group):
@@ -120,7 +124,7 @@ def gptq_quantize(W, H, bits, d32, group: int, damp_frac: float = 0.01, lam: flo
             Wc[:, c1:] -= E @ U[c0:c1, c1:]
         err[:, c0:c1] = E
     out.update({"codes": codes, "scale": scale, "zero": zero, "tau_idx": tau_idx, "mask": mask,
-                "what": what, "err": err, "gap": gap})
+                "what": what, "err": err, "gap": gap, "margin": margin})
     return out
 
 

@@ -8,16 +8,18 @@ hand-written HIP kernels:
     sba_search     balanced N-1/N/N+1 allocation scored by output KL (fused MFMA + softmax)
                    (sba_search_ex: output-MSE objective or a given group order, for the ablations)
     sqc_calibrate  3-sigma mask + tau grid over scale and zero  (wave-level, VALU)
+                   (gptq_quantize: the same quantizer inside GPTQ's error-compensating sweep)
     pack           group-structured bit-planes                  (HBM)
     qlinear        Y = X W_hat^T read from the planes (decode-sized batches)
 
 ``quantize_layer`` chains them on the current stream.  PyTorch only provides
 device memory and the stream.
 """
-from ._lib import (SlimError, load_library, hessian, salience, sba_search, sba_search_ex, sqc_calibrate, pack, qlinear, tau_table,
+from ._lib import (SlimError, load_library, hessian, salience, sba_search, sba_search_ex, sqc_calibrate, gptq_quantize, pack, qlinear,
+                   tau_table,
                    timing_enable, timing_reset, timing_read, SLIM_F32, SLIM_BF16)
 from .layer import quantize_layer
 
-__all__ = ["SlimError", "load_library", "hessian", "salience", "sba_search", "sba_search_ex", "sqc_calibrate", "pack", "qlinear",
+__all__ = ["SlimError", "load_library", "hessian", "salience", "sba_search", "sba_search_ex", "sqc_calibrate", "gptq_quantize", "pack", "qlinear",
            "tau_table", "timing_enable", "timing_reset", "timing_read", "quantize_layer", "SLIM_F32",
            "SLIM_BF16"]

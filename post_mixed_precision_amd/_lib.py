@@ -37,6 +37,9 @@ _SIGS = {
                                     _c_int, _c_int, _c_vp, _c_vp, _c_vp, _c_vp, _c_sz, _c_vp]),
     "slim_sqc_calibrate": (_c_int, [_c_vp, _c_int, _c_i64, _c_i64, _c_int, _c_vp, _c_vp, _c_dbl, _c_int, _c_vp,
                                     _c_vp, _c_vp, _c_vp, _c_vp, _c_vp]),
+    "slim_gptq_workspace": (_c_sz, [_c_i64, _c_i64, _c_int]),
+    "slim_gptq_quantize": (_c_int, [_c_vp, _c_i64, _c_dbl, _c_vp, _c_int, _c_i64, _c_int, _c_vp, _c_vp, _c_dbl,
+                                    _c_int, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_sz, _c_vp]),
     "slim_tau_table": (_c_int, [_c_dbl, _c_int, _c_vp]),
     "slim_pack_words": (_c_i64, [_c_i64, _c_i64, _c_int]),
     "slim_pack": (_c_int, [_c_vp, _c_i64, _c_i64, _c_int, _c_vp, _c_int, _c_vp, _c_vp, _c_vp]),
@@ -236,6 +239,32 @@ def sqc_calibrate(W, bits, hinv, group: int, lam: float = 0.1, n_tau: int = 50, 
     check(lib.slim_sqc_calibrate(_ptr(W), _dtype_code(W), n, m, group, _ptr(bits), _ptr(hinv), float(lam),
                                  int(n_tau), _ptr(out["scale"]), _ptr(out["zero"]), _ptr(out["codes"]),
                                  _ptr(out["mask"]), _ptr(out["tau_idx"]), _stream(dev)), "slim_sqc_calibrate")
+    return out
+
+
+def gptq_quantize(H, W, bits, hinv, group: int, damp_frac: float = 0.01, lam: float = 0.1, n_tau: int = 50,
+                  want_tau: bool = True):
+    """GPTQ sweep with the group quantizer -> dict(scale, zero [n, k] f32; codes [n, m] u8;
+    mask [n, m/32] i32 bits; tau_idx [n, k] u8; info i32 [1])."""
+    torch = _torch()
+    lib = load_library()
+    H, W, bits, hinv = _dev(H), _dev(W), _dev(bits), _dev(hinv)
+    n, m = W.shape
+    k = m // group
+    dev = W.device
+    out = {
+        "scale": torch.empty((n, k), dtype=torch.float32, device=dev),
+        "zero": torch.empty((n, k), dtype=torch.float32, device=dev),
+        "codes": torch.empty((n, m), dtype=torch.uint8, device=dev),
+        "mask": torch.empty((n, max(m // 32, 1)), dtype=torch.int32, device=dev),
+        "tau_idx": torch.empty((n, k), dtype=torch.uint8, device=dev) if want_tau else None,
+        "info": torch.zeros(1, dtype=torch.int32, device=dev),
+    }
+    ws = _ws(lib.slim_gptq_workspace(n, m, group), dev)
+    check(lib.slim_gptq_quantize(_ptr(H), m, float(damp_frac), _ptr(W), _dtype_code(W), n, group, _ptr(bits),
+                                 _ptr(hinv), float(lam), int(n_tau), _ptr(out["scale"]), _ptr(out["zero"]),
+                                 _ptr(out["codes"]), _ptr(out["mask"]), _ptr(out["tau_idx"]), _ptr(out["info"]),
+                                 _ptr(ws), ws.numel(), _stream(dev)), "slim_gptq_quantize")
     return out
 
 

@@ -34,7 +34,7 @@ std::mutex g_timer_mu;
 bool g_timer_on = false;
 TimerSlot g_slots[slim::K_NUM_TIMED];
 const char *g_timer_names[slim::K_NUM_TIMED] = {"hessian_gram", "chol_update", "sba_klgemm", "sqc_calibrate",
-                                                "pack_planes", "qlinear"};
+                                                "pack_planes", "qlinear", "gptq_sweep", "gptq_trail"};
 
 void drain(TimerSlot &s) {
   for (auto &pr : s.pending) {
@@ -202,6 +202,30 @@ int slim_sqc_calibrate(const void *W, int wdt, int64_t n, int64_t m, int group, 
   slim::make_tau_table(lambda, n_tau, tt);
   hipError_t e = slim::launch_sqc(W, wdt == SLIM_BF16, n, m, group, bits, hinv_diag, tt, n_tau, scale, zero, codes,
                                   mask, tau_idx, (hipStream_t)stream);
+  return e == hipSuccess ? SLIM_OK : hip_fail(e);
+}
+
+// ---------------------------------------------------------------- GPTQ sweep
+size_t slim_gptq_workspace(int64_t n, int64_t m, int group) {
+  if (n < 1 || m < 1 || m > SLIM_MAX_WIDTH || !valid_group(group) || m % group) return 0;
+  return slim::gptq_ws_bytes(n, m, group);
+}
+
+int slim_gptq_quantize(const float *H, int64_t m, double damp_frac, const void *W, int wdt, int64_t n, int group,
+                       const int8_t *bits, const float *hinv_diag, double lambda, int n_tau, float *scale,
+                       float *zero, uint8_t *codes, uint32_t *mask, uint8_t *tau_idx, int32_t *info, void *ws,
+                       size_t ws_bytes, void *stream) {
+  if (!valid_dtype(wdt)) return SLIM_E_DTYPE;
+  if (n < 1 || m < 1 || m > SLIM_MAX_WIDTH || !valid_group(group) || m % group) return SLIM_E_SHAPE;
+  if (!(damp_frac >= 0.0) || n_tau < 1 || n_tau > 255 || !(lambda >= 0.0 && lambda < 1.0)) return SLIM_E_PARAM;
+  if (!H || !W || !bits || !hinv_diag || !scale || !zero || !codes || !mask || !info) return SLIM_E_NULL;
+  if (!aligned16(H) || !aligned16(W) || !aligned16(hinv_diag) || !aligned16(codes)) return SLIM_E_ALIGN;
+  if (!ws || ws_bytes < slim::gptq_ws_bytes(n, m, group)) return SLIM_E_WORKSPACE;
+  if (!aligned16(ws)) return SLIM_E_ALIGN;
+  slim::TauTable tt;
+  slim::make_tau_table(lambda, n_tau, tt);
+  hipError_t e = slim::launch_gptq(H, m, damp_frac, W, wdt == SLIM_BF16, n, group, bits, hinv_diag, tt, n_tau, scale,
+                                   zero, codes, mask, tau_idx, info, ws, (hipStream_t)stream);
   return e == hipSuccess ? SLIM_OK : hip_fail(e);
 }
 

@@ -1,0 +1,270 @@
+// GPTQ error compensation around the SliM-LLM group quantizer on gfx950.
+//
+// "SliM-LLM" blog digest (rkmt.cn), core design and the FAQ entry on GPTQ /
+// AWQ / OmniQuant: SliM-LLM is a plug-in PTQ framework on GPTQ's layer-wise
+// backbone, inserting SBA (group widths) and SQC (each group's quantizer).
+// GPTQ (Frantar et al., ICLR 2023) quantizes the input columns in order and
+// moves each column's error onto the columns not yet quantized along the
+// inverse Hessian of those columns; all of those inverses are rows of U, the
+// upper Cholesky factor of H_d^-1 = U^T U:
+//     e_c = (w_c - w_hat_c) / U_cc,    w_c' -= e_c U[c, c']   (c' > c).
+//
+// U without forming H_d^-1: with J the index reversal, J H_d J = Lr Lr^T
+// gives H_d = R R^T for the upper R = J Lr J, so H_d^-1 = (R^-1)^T R^-1 and
+// U = R^-1 = J Lr^-1 J.  The salience stage's float64 Cholesky sweep, which
+// forms the factor's inverse in the same pass, runs on the reversed matrix;
+// U[r][c] = Lr^-1[m-1-r][m-1-c].
+//
+// Per group j (the sweep's blocks are the quantization groups), in order:
+//   1. SQC calibrates the group on its current, already compensated weights
+//      (a float32 copy kept up to date for the next group), fixing scale and
+//      zero for the group's columns;
+//   2. gptq_sweep: one thread per row walks the group's columns in 16-column
+//      sub-blocks.  Inside a sub-block the weights sit in registers and every
+//      quantized column updates the rest of the sub-block at once; after a
+//      sub-block its 16 errors update the group's later columns (held in LDS)
+//      as one rank-16 step.  Codes are the quantizer's float32 decision on
+//      the current weight rounded to float32; errors and updates are float64.
+//   3. gptq_trail: W[:, after the group] -= E U[group, after the group], a
+//      float64 MFMA product over 64 x 64 tiles, which also refreshes the
+//      float32 copy of the next group.
+#include "common.hpp"
+#include "f64tile.hpp"
+#include "kernels.hpp"
+
+namespace slim {
+
+constexpr int GQ_SB = 16;   // columns per sub-block of the sweep
+
+// U (m x m, upper, zeros below) and its transpose Ut from the inverse factor
+// Z (mp x mp) of the reversed matrix.
+__global__ __launch_bounds__(256) void gptq_u_kernel(const double *__restrict__ Z, int64_t mp, int64_t m,
+                                                     double *__restrict__ U, double *__restrict__ Ut) {
+  const int64_t total = m * m;
+  for (int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x; idx < total; idx += (int64_t)gridDim.x * 256) {
+    const int64_t r = idx / m, c = idx % m;
+    const double v = c >= r ? Z[(m - 1 - r) * mp + (m - 1 - c)] : 0.0;
+    U[idx] = v;
+    Ut[c * m + r] = v;
+  }
+}
+
+// W64 = W, W32 = W (the float32 copy the group calibration reads); a
+// non-finite weight sets info = -1.
+template <bool BF16>
+__global__ __launch_bounds__(256) void gptq_prep_kernel(const void *__restrict__ W, int64_t total,
+                                                        double *__restrict__ W64, float *__restrict__ W32,
+                                                        int32_t *__restrict__ info) {
+  bool bad = false;
+  for (int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x; idx < total; idx += (int64_t)gridDim.x * 256) {
+    const float w = BF16 ? bf16_bits_to_f32(((const uint16_t *)W)[idx]) : ((const float *)W)[idx];
+    if (!isfinite(w)) bad = true;
+    W64[idx] = (double)w;
+    W32[idx] = w;
+  }
+  if (bad) atomicExch(info, -1);
+}
+
+// The column sweep of group j for 64 rows (one wave).  slab[c][lane] holds
+// the row's current weight of group column c.
+template <int G>
+__global__ __launch_bounds__(64) void gptq_sweep_kernel(const double *__restrict__ W64, int64_t n, int64_t m,
+                                                        int j, const double *__restrict__ U,
+                                                        const double *__restrict__ Ut,
+                                                        const float *__restrict__ scale,
+                                                        const float *__restrict__ zero,
+                                                        const int8_t *__restrict__ bits, uint8_t *__restrict__ codes,
+                                                        double *__restrict__ Err) {
+  __shared__ double slab[G * 64];
+  const int t = threadIdx.x;
+  const int64_t i = (int64_t)blockIdx.x * 64 + t;
+  const bool live = i < n;
+  const int64_t il = live ? i : n - 1;
+  const int64_t k = m / G;
+  const int64_t c0 = (int64_t)j * G;
+  {
+    const double2 *src = (const double2 *)(W64 + il * m + c0);
+#pragma unroll 4
+    for (int c = 0; c < G / 2; ++c) {
+      const double2 v = src[c];
+      slab[(2 * c) * 64 + t] = v.x;
+      slab[(2 * c + 1) * 64 + t] = v.y;
+    }
+  }
+  const float s = scale[il * k + j], z = zero[il * k + j];
+  const float maxq = (float)((1 << bits[j]) - 1);
+  const float r = 1.0f / s;
+  for (int sb = 0; sb < G / GQ_SB; ++sb) {
+    const int64_t cb = c0 + sb * GQ_SB;   // first column of the sub-block
+    double w[GQ_SB], e[GQ_SB];
+#pragma unroll
+    for (int c = 0; c < GQ_SB; ++c) w[c] = slab[(sb * GQ_SB + c) * 64 + t];
+    uint32_t cw[GQ_SB / 4] = {0, 0, 0, 0};
+#pragma unroll
+    for (int c = 0; c < GQ_SB; ++c) {
+      // the quantizer's float32 sequence on the current weight
+      const float w32 = (float)w[c];
+      float tq = w32 * r;
+      tq = tq + z;
+      float q = rintf(tq);
+      q = fminf(fmaxf(q, 0.0f), maxq);
+      const float dq = q - z;
+      const float wh = dq * s;
+      const double *urow = U + (cb + c) * m + cb;
+      e[c] = (w[c] - (double)wh) / urow[c];
+#pragma unroll
+      for (int c2 = c + 1; c2 < GQ_SB; ++c2) w[c2] = w[c2] - e[c] * urow[c2];
+      cw[c >> 2] |= ((uint32_t)q & 0xffu) << (8 * (c & 3));
+    }
+    if (live) {
+      *(uint4 *)(codes + i * m + cb) = make_uint4(cw[0], cw[1], cw[2], cw[3]);
+      double2 *ed = (double2 *)(Err + i * G + sb * GQ_SB);
+#pragma unroll
+      for (int c = 0; c < GQ_SB / 2; ++c) ed[c] = make_double2(e[2 * c], e[2 * c + 1]);
+    }
+    // the sub-block's errors onto the group's later columns, one column at a
+    // time and in column order within the update, as the sweep defines it
+    for (int c2 = (sb + 1) * GQ_SB; c2 < G; ++c2) {
+      const double *ucol = Ut + (c0 + c2) * m + cb;   // U[cb .. cb+15][c0 + c2]
+      double v = slab[c2 * 64 + t];
+#pragma unroll
+      for (int c = 0; c < GQ_SB; ++c) v = v - e[c] * ucol[c];
+      slab[c2 * 64 + t] = v;
+    }
+  }
+}
+
+// W64[:, c1:] -= Err (n x G) . U[c1-G .. c1-1][c1:], 64 x 64 output tiles;
+// columns of the next group also go to the float32 copy.
+template <int G>
+__global__ __launch_bounds__(256) void gptq_trail_kernel(double *__restrict__ W64, float *__restrict__ W32,
+                                                         int64_t n, int64_t m, int64_t c1,
+                                                         const double *__restrict__ Err,
+                                                         const double *__restrict__ U) {
+  __shared__ double sA[NBK * SP];
+  __shared__ double sB[NBK * SP];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int64_t r0 = (int64_t)blockIdx.x * NBK;
+  const int64_t col0 = c1 + (int64_t)blockIdx.y * NBK;
+  const int64_t u0 = c1 - G;   // first U row of the group
+  f64x4_t acc[2][2];
+  zero_acc(acc);
+  for (int kc = 0; kc < G; kc += NBK) {
+    // sA[kk][ii] = Err[r0+ii][kc+kk], sB[kk][cc] = U[u0+kc+kk][col0+cc]; zero outside
+#pragma unroll 4
+    for (int e = 0; e < 16; ++e) {
+      const int idx = tid + e * 256;
+      const int ii = idx >> 6, kk = idx & 63;
+      sA[kk * SP + ii] = (r0 + ii < n && kc + kk < G) ? Err[(r0 + ii) * G + kc + kk] : 0.0;
+      const int k2 = idx >> 6, cc = idx & 63;
+      sB[k2 * SP + cc] = (kc + k2 < G && col0 + cc < m) ? U[(u0 + kc + k2) * m + col0 + cc] : 0.0;
+    }
+    __syncthreads();
+    gemm64(sA, sB, acc, lane, wm, wn);
+    __syncthreads();
+  }
+#pragma unroll
+  for (int a = 0; a < 2; ++a)
+#pragma unroll
+    for (int b = 0; b < 2; ++b)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int64_t row = r0 + wm * 32 + a * 16 + 4 * v + (lane >> 4);
+        const int64_t col = col0 + wn * 32 + b * 16 + (lane & 15);
+        if (row < n && col < m) {
+          const double nv = W64[row * m + col] - acc[a][b][v];
+          W64[row * m + col] = nv;
+          if (col < c1 + G) W32[row * m + col] = (float)nv;
+        }
+      }
+}
+
+static int64_t gq_pad64(int64_t m) { return (m + NBK - 1) / NBK * NBK; }
+
+size_t gptq_ws_bytes(int64_t n, int64_t m, int group) {
+  const int64_t mp = gq_pad64(m);
+  size_t off = 0;
+  off += align_up((size_t)mp * mp * 8, 256);      // A, then U
+  off += align_up((size_t)mp * mp * 8, 256);      // Z
+  off += align_up((size_t)NBK * NBK * 8, 256);    // TinvT
+  off += align_up((size_t)mp * 8, 256);           // d
+  off += 256;                                     // alpha
+  off += align_up((size_t)m * m * 8, 256);        // Ut
+  off += align_up((size_t)n * m * 8, 256);        // W64
+  off += align_up((size_t)n * m * 4, 256);        // W32
+  off += align_up((size_t)n * group * 8, 256);    // Err
+  return off;
+}
+
+template <int G>
+static void gq_group(double *W64, float *W32, int64_t n, int64_t m, int j, const double *U, const double *Ut,
+                     const float *scale, const float *zero, const int8_t *bits, uint8_t *codes, double *Err,
+                     hipStream_t st) {
+  const unsigned nrb = (unsigned)((n + 63) / 64);
+  timer_begin(K_GPTQ_SWEEP, st);
+  gptq_sweep_kernel<G><<<nrb, 64, 0, st>>>(W64, n, m, j, U, Ut, scale, zero, bits, codes, Err);
+  timer_end(K_GPTQ_SWEEP, st);
+  const int64_t c1 = (int64_t)(j + 1) * G;
+  if (c1 < m) {
+    dim3 grid(nrb, (unsigned)((m - c1 + NBK - 1) / NBK));
+    timer_begin(K_GPTQ_TRAIL, st);
+    gptq_trail_kernel<G><<<grid, 256, 0, st>>>(W64, W32, n, m, c1, Err, U);
+    timer_end(K_GPTQ_TRAIL, st);
+  }
+}
+
+hipError_t launch_gptq(const float *H, int64_t m, double damp, const void *W, bool bf16, int64_t n, int group,
+                       const int8_t *bits, const float *hinv, const TauTable &tt, int n_tau, float *scale,
+                       float *zero, uint8_t *codes, uint32_t *mask, uint8_t *tau_idx, int32_t *info, void *ws,
+                       hipStream_t st) {
+  const int64_t mp = gq_pad64(m);
+  char *base = (char *)ws;
+  size_t off = 0;
+  double *A = (double *)(base + off);
+  off += align_up((size_t)mp * mp * 8, 256);
+  double *Z = (double *)(base + off);
+  off += align_up((size_t)mp * mp * 8, 256);
+  double *TinvT = (double *)(base + off);
+  off += align_up((size_t)NBK * NBK * 8, 256);
+  double *d = (double *)(base + off);
+  off += align_up((size_t)mp * 8, 256);
+  double *alpha = (double *)(base + off);
+  off += 256;
+  double *Ut = (double *)(base + off);
+  off += align_up((size_t)m * m * 8, 256);
+  double *W64 = (double *)(base + off);
+  off += align_up((size_t)n * m * 8, 256);
+  float *W32 = (float *)(base + off);
+  off += align_up((size_t)n * m * 4, 256);
+  double *Err = (double *)(base + off);
+
+  hipError_t e = launch_chol_inverse(H, m, damp, true, A, Z, TinvT, d, alpha, info, st);
+  if (e != hipSuccess) return e;
+  double *U = A;   // the factor is no longer needed once its inverse is formed
+  {
+    int64_t blocks = (m * m + 255) / 256;
+    if (blocks > 65536) blocks = 65536;
+    gptq_u_kernel<<<(unsigned)blocks, 256, 0, st>>>(Z, mp, m, U, Ut);
+    blocks = (n * m + 255) / 256;
+    if (blocks > 65536) blocks = 65536;
+    if (bf16)
+      gptq_prep_kernel<true><<<(unsigned)blocks, 256, 0, st>>>(W, n * m, W64, W32, info);
+    else
+      gptq_prep_kernel<false><<<(unsigned)blocks, 256, 0, st>>>(W, n * m, W64, W32, info);
+  }
+  const int k = (int)(m / group);
+  for (int j = 0; j < k; ++j) {
+    e = launch_sqc(W32, false, n, m, group, bits, hinv, tt, n_tau, scale, zero, codes, mask, tau_idx, st, j, 1);
+    if (e != hipSuccess) return e;
+    if (group == 32)
+      gq_group<32>(W64, W32, n, m, j, U, Ut, scale, zero, bits, codes, Err, st);
+    else if (group == 64)
+      gq_group<64>(W64, W32, n, m, j, U, Ut, scale, zero, bits, codes, Err, st);
+    else
+      gq_group<128>(W64, W32, n, m, j, U, Ut, scale, zero, bits, codes, Err, st);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace slim

@@ -10,7 +10,9 @@ namespace slim {
 // timing is enabled; no-ops otherwise.
 void timer_begin(int kernel_id, hipStream_t st);
 void timer_end(int kernel_id, hipStream_t st);
-enum TimedKernel { K_HESSIAN = 0, K_CHOL_UPDATE, K_SBA_KLGEMM, K_SQC, K_PACK, K_QLINEAR, K_NUM_TIMED };
+enum TimedKernel {
+  K_HESSIAN = 0, K_CHOL_UPDATE, K_SBA_KLGEMM, K_SQC, K_PACK, K_QLINEAR, K_GPTQ_SWEEP, K_GPTQ_TRAIL, K_NUM_TIMED
+};
 
 inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
@@ -27,6 +29,11 @@ hipError_t launch_hessian(const void *X, bool bf16, int64_t t, int64_t m, float 
 
 // ---- Salience (damped inverse diagonal + group means) ----
 size_t salience_ws_bytes(int64_t n, int64_t m, int group);
+// Cholesky of the damped Hessian (reversed index order if reverse) with the
+// inverse of its factor: A (mp x mp) ends holding L, Z = L^-1, d = diag of the
+// inverse; mp = m rounded up to 64.
+hipError_t launch_chol_inverse(const float *H, int64_t m, double damp, bool reverse, double *A, double *Z,
+                               double *TinvT, double *d, double *alpha, int32_t *info, hipStream_t st);
 hipError_t launch_salience(const float *H, int64_t m, double damp, const void *W, bool bf16,
                            int64_t n, int group, float *hinv, double *gsal, float *esal,
                            int32_t *info, void *ws, hipStream_t st);
@@ -53,7 +60,15 @@ struct TauTable {
 void make_tau_table(double lambda, int n_tau, TauTable &tt);
 hipError_t launch_sqc(const void *W, bool bf16, int64_t n, int64_t m, int group, const int8_t *bits,
                       const float *hinv, const TauTable &tt, int n_tau, float *scale, float *zero,
-                      uint8_t *codes, uint32_t *mask, uint8_t *tau_idx, hipStream_t st);
+                      uint8_t *codes, uint32_t *mask, uint8_t *tau_idx, hipStream_t st, int64_t j0 = 0,
+                      int64_t nk = -1);
+
+// ---- GPTQ sweep around the group quantizer ----
+size_t gptq_ws_bytes(int64_t n, int64_t m, int group);
+hipError_t launch_gptq(const float *H, int64_t m, double damp, const void *W, bool bf16, int64_t n, int group,
+                       const int8_t *bits, const float *hinv, const TauTable &tt, int n_tau, float *scale,
+                       float *zero, uint8_t *codes, uint32_t *mask, uint8_t *tau_idx, int32_t *info, void *ws,
+                       hipStream_t st);
 
 // ---- Pack ----
 hipError_t launch_pack(const uint8_t *codes, int64_t n, int64_t m, int group, const int8_t *bits,

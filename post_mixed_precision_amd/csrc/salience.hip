@@ -20,12 +20,11 @@
 //               (lookahead: the one-workgroup step no longer waits for the bulk update)
 // The GEMM-shaped work uses v_mfma_f64_16x16x4_f64 on 64x64 tiles.
 #include "common.hpp"
+#include "f64tile.hpp"
 #include "kernels.hpp"
 
 namespace slim {
 
-constexpr int NBK = 64;   // panel width
-constexpr int SP = 65;    // LDS pitch (doubles) of 64x64 operand tiles
 
 __global__ __launch_bounds__(256) void sal_alpha_kernel(const float *__restrict__ H, int64_t m, double damp,
                                                         double *__restrict__ alpha, int32_t *__restrict__ info) {
@@ -45,10 +44,13 @@ __global__ __launch_bounds__(256) void sal_alpha_kernel(const float *__restrict_
 }
 
 // A = lower(H) mirrored + alpha I (identity in the padding), Z = I, d = 0.
+// With reverse set, A holds J H J + alpha I instead (J reverses the index
+// order: A[i][j] = H[m-1-i][m-1-j]); its factor gives the upper Cholesky
+// factor of the inverse that GPTQ uses.
 __global__ __launch_bounds__(256) void sal_init_kernel(const float *__restrict__ H, int64_t m, int64_t mp,
                                                        const double *__restrict__ alpha, double *__restrict__ A,
                                                        double *__restrict__ Z, double *__restrict__ d,
-                                                       int32_t *__restrict__ info) {
+                                                       int32_t *__restrict__ info, int reverse) {
   const int64_t total = mp * mp;
   const double a = alpha[0];
   bool bad = false;
@@ -56,7 +58,8 @@ __global__ __launch_bounds__(256) void sal_init_kernel(const float *__restrict__
     const int64_t i = idx / mp, j = idx % mp;
     double v;
     if (i < m && j < m) {
-      const float h = (j <= i) ? H[i * m + j] : H[j * m + i];
+      const int64_t hi = reverse ? m - 1 - i : i, hj = reverse ? m - 1 - j : j;
+      const float h = (hj <= hi) ? H[hi * m + hj] : H[hj * m + hi];
       if (!isfinite(h)) bad = true;
       v = (double)h + (i == j ? a : 0.0);
     } else {
@@ -166,54 +169,6 @@ __device__ __forceinline__ void chol_diag_body(double *__restrict__ A, int64_t m
 __global__ __launch_bounds__(512) void chol_diag_kernel(double *__restrict__ A, int64_t mp, int p,
                                                         double *__restrict__ TinvT, int32_t *__restrict__ info) {
   chol_diag_body<512>(A, mp, p, TinvT, info);
-}
-
-// sX[k][i] = src[(r0 + i) * ld + c0 + k]   (row-major source, k contiguous -> transposed)
-__device__ __forceinline__ void load_tile_T(double *sX, const double *__restrict__ src, int64_t ld, int64_t r0,
-                                            int64_t c0, int tid) {
-#pragma unroll 4
-  for (int e = 0; e < 16; ++e) {
-    const int idx = tid + e * 256;
-    const int i = idx >> 6, k = idx & 63;
-    sX[k * SP + i] = src[(r0 + i) * ld + c0 + k];
-  }
-}
-// sX[k][c] = src[(r0 + k) * ld + c0 + c]
-__device__ __forceinline__ void load_tile_N(double *sX, const double *__restrict__ src, int64_t ld, int64_t r0,
-                                            int64_t c0, int tid) {
-#pragma unroll 4
-  for (int e = 0; e < 16; ++e) {
-    const int idx = tid + e * 256;
-    const int k = idx >> 6, c = idx & 63;
-    sX[k * SP + c] = src[(r0 + k) * ld + c0 + c];
-  }
-}
-
-// acc (2x2 blocks of 16x16 per wave) = sA^T-layout x sB over K = 64.
-__device__ __forceinline__ void gemm64(const double *sA, const double *sB, f64x4_t acc[2][2], int lane, int wm,
-                                       int wn) {
-#pragma unroll 4
-  for (int ks = 0; ks < 16; ++ks) {
-    const int k = ks * 4 + (lane >> 4);
-    double a[2], b[2];
-#pragma unroll
-    for (int i = 0; i < 2; ++i) a[i] = sA[k * SP + wm * 32 + i * 16 + (lane & 15)];
-#pragma unroll
-    for (int j = 0; j < 2; ++j) b[j] = sB[k * SP + wn * 32 + j * 16 + (lane & 15)];
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-#pragma unroll
-      for (int j = 0; j < 2; ++j) acc[i][j] = mfma_f64(a[i], b[j], acc[i][j]);
-  }
-}
-
-__device__ __forceinline__ void zero_acc(f64x4_t acc[2][2]) {
-#pragma unroll
-  for (int i = 0; i < 2; ++i)
-#pragma unroll
-    for (int j = 0; j < 2; ++j)
-#pragma unroll
-      for (int v = 0; v < 4; ++v) acc[i][j][v] = 0.0;
 }
 
 // Panel kernel.  Workgroups [0, nrow): row block ib = p+1+w: L_ib,p = A_ib,p Tinv^T.
@@ -433,6 +388,35 @@ size_t salience_ws_bytes(int64_t n, int64_t m, int group) {
   return off;
 }
 
+hipError_t launch_chol_inverse(const float *H, int64_t m, double damp, bool reverse, double *A, double *Z,
+                               double *TinvT, double *d, double *alpha, int32_t *info, hipStream_t st) {
+  const int64_t mp = pad64(m);
+  sal_alpha_kernel<<<1, 256, 0, st>>>(H, m, damp, alpha, info);
+  {
+    int64_t blocks = (mp * mp + 255) / 256;
+    if (blocks > 65536) blocks = 65536;
+    sal_init_kernel<<<(unsigned)blocks, 256, 0, st>>>(H, m, mp, alpha, A, Z, d, info, reverse ? 1 : 0);
+  }
+  // Lookahead: once the block column after panel p is updated, the next
+  // diagonal block is factored in the same launch as the rest of the trailing
+  // update, so the one-workgroup factorisation overlaps the bulk update.
+  const int NB = (int)(mp / NBK);
+  chol_diag_kernel<<<1, 512, 0, st>>>(A, mp, 0, TinvT, info);
+  for (int p = 0; p < NB; ++p) {
+    const int nrow = NB - p - 1;
+    chol_panel_kernel<<<nrow + p + 1, 256, 0, st>>>(A, Z, TinvT, d, mp, p, nrow);
+    if (nrow > 0) {
+      chol_trail_kernel<<<(unsigned)(nrow + p + 1), 256, 0, st>>>(A, Z, TinvT, info, mp, p, NB, 1, 0);
+      const int64_t n2 = nrow - 1;
+      const int64_t rest = n2 * (n2 + 1) / 2 + n2 * (p + 1);
+      timer_begin(K_CHOL_UPDATE, st);
+      chol_trail_kernel<<<(unsigned)(rest + 1), 256, 0, st>>>(A, Z, TinvT, info, mp, p, NB, 0, 1);
+      timer_end(K_CHOL_UPDATE, st);
+    }
+  }
+  return hipGetLastError();
+}
+
 hipError_t launch_salience(const float *H, int64_t m, double damp, const void *W, bool bf16, int64_t n, int group,
                            float *hinv, double *gsal, float *esal, int32_t *info, void *ws, hipStream_t st) {
   const int64_t mp = pad64(m);
@@ -452,29 +436,8 @@ hipError_t launch_salience(const float *H, int64_t m, double damp, const void *W
   off += 256;
   double *part = (double *)(base + off);
 
-  sal_alpha_kernel<<<1, 256, 0, st>>>(H, m, damp, alpha, info);
-  {
-    int64_t blocks = (mp * mp + 255) / 256;
-    if (blocks > 65536) blocks = 65536;
-    sal_init_kernel<<<(unsigned)blocks, 256, 0, st>>>(H, m, mp, alpha, A, Z, d, info);
-  }
-  // Lookahead: once the block column after panel p is updated, the next
-  // diagonal block is factored in the same launch as the rest of the trailing
-  // update, so the one-workgroup factorisation overlaps the bulk update.
-  const int NB = (int)(mp / NBK);
-  chol_diag_kernel<<<1, 512, 0, st>>>(A, mp, 0, TinvT, info);
-  for (int p = 0; p < NB; ++p) {
-    const int nrow = NB - p - 1;
-    chol_panel_kernel<<<nrow + p + 1, 256, 0, st>>>(A, Z, TinvT, d, mp, p, nrow);
-    if (nrow > 0) {
-      chol_trail_kernel<<<(unsigned)(nrow + p + 1), 256, 0, st>>>(A, Z, TinvT, info, mp, p, NB, 1, 0);
-      const int64_t n2 = nrow - 1;
-      const int64_t rest = n2 * (n2 + 1) / 2 + n2 * (p + 1);
-      timer_begin(K_CHOL_UPDATE, st);
-      chol_trail_kernel<<<(unsigned)(rest + 1), 256, 0, st>>>(A, Z, TinvT, info, mp, p, NB, 0, 1);
-      timer_end(K_CHOL_UPDATE, st);
-    }
-  }
+  hipError_t e0 = launch_chol_inverse(H, m, damp, false, A, Z, TinvT, d, alpha, info, st);
+  if (e0 != hipSuccess) return e0;
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   sal_hinv_out_kernel<<<(unsigned)((m + 255) / 256), 256, 0, st>>>(d, m, hinv);

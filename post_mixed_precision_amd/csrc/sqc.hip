@@ -23,8 +23,11 @@
 
 namespace slim {
 
+// Segments of groups j0 .. j0 + nk - 1 of every row (the whole layer: j0 = 0,
+// nk = k; the GPTQ sweep calibrates one group at a time).
 template <bool BF16, int LPS>
 __global__ __launch_bounds__(256) void sqc_kernel(const void *__restrict__ W, int64_t n, int64_t m, int g,
+                                                  int64_t j0, int64_t nk,
                                                   const int8_t *__restrict__ bits, const float *__restrict__ hinv,
                                                   const TauTable tt, int n_tau, float *__restrict__ scale,
                                                   float *__restrict__ zero, uint8_t *__restrict__ codes,
@@ -33,8 +36,8 @@ __global__ __launch_bounds__(256) void sqc_kernel(const void *__restrict__ W, in
   const int64_t seg = gl / LPS;
   const int lis = (int)(gl % LPS);
   const int64_t k = m / g;
-  const bool valid = seg < n * k;
-  const int64_t i = valid ? seg / k : 0, j = valid ? seg % k : 0;
+  const bool valid = seg < n * nk;
+  const int64_t i = valid ? seg / nk : 0, j = valid ? j0 + seg % nk : 0;
   const int64_t col0 = j * g + (int64_t)lis * 8;
   const int64_t base = i * m + col0;
 
@@ -176,14 +179,15 @@ void make_tau_table(double lambda, int n_tau, TauTable &tt) {
 
 hipError_t launch_sqc(const void *W, bool bf16, int64_t n, int64_t m, int group, const int8_t *bits,
                       const float *hinv, const TauTable &tt, int n_tau, float *scale, float *zero, uint8_t *codes,
-                      uint32_t *mask, uint8_t *tau_idx, hipStream_t st) {
+                      uint32_t *mask, uint8_t *tau_idx, hipStream_t st, int64_t j0, int64_t nk) {
   const int lps = group / 8;
-  const int64_t lanes = n * (m / group) * lps;
+  if (nk < 0) nk = m / group;
+  const int64_t lanes = n * nk * lps;
   const unsigned blocks = (unsigned)((lanes + 255) / 256);
   timer_begin(K_SQC, st);
 #define SLIM_SQC(L)                                                                                           \
-  if (bf16) sqc_kernel<true, L><<<blocks, 256, 0, st>>>(W, n, m, group, bits, hinv, tt, n_tau, scale, zero, codes, mask, tau_idx); \
-  else sqc_kernel<false, L><<<blocks, 256, 0, st>>>(W, n, m, group, bits, hinv, tt, n_tau, scale, zero, codes, mask, tau_idx);
+  if (bf16) sqc_kernel<true, L><<<blocks, 256, 0, st>>>(W, n, m, group, j0, nk, bits, hinv, tt, n_tau, scale, zero, codes, mask, tau_idx); \
+  else sqc_kernel<false, L><<<blocks, 256, 0, st>>>(W, n, m, group, j0, nk, bits, hinv, tt, n_tau, scale, zero, codes, mask, tau_idx);
   if (lps == 16) { SLIM_SQC(16) }
   else if (lps == 8) { SLIM_SQC(8) }
   else { SLIM_SQC(4) }

@@ -11,14 +11,21 @@ from . import _lib
 
 
 def quantize_layer(X, W, group: int = 128, avg_bits: int = 2, lam: float = 0.1, n_tau: int = 50,
-                   damp_frac: float = 0.01, H=None):
+                   damp_frac: float = 0.01, H=None, gptq: bool = False):
     """X [T, m], W [n, m] (bf16 or f32, GPU).  If H is given the Hessian stage is
-    skipped (a Hessian shared by several linears of one input width)."""
+    skipped (a Hessian shared by several linears of one input width).  With
+    gptq set, the groups are calibrated and quantized inside GPTQ's
+    error-compensating sweep (the backbone the digest names) instead of
+    independently."""
     if H is None:
         H = _lib.hessian(X)
     hinv, gsal, info, _ = _lib.salience(H, W, group, damp_frac)
     bits, kl, r_star = _lib.sba_search(X, W, gsal, group, avg_bits)
-    sq = _lib.sqc_calibrate(W, bits, hinv, group, lam, n_tau)
+    if gptq:
+        sq = _lib.gptq_quantize(H, W, bits, hinv, group, damp_frac, lam, n_tau)
+        sq["gptq_info"] = sq.pop("info")
+    else:
+        sq = _lib.sqc_calibrate(W, bits, hinv, group, lam, n_tau)
     packed, pinfo = _lib.pack(sq["codes"], bits, group, avg_bits)
     return {"H": H, "hinv": hinv, "group_sal": gsal, "info": info, "bits": bits, "kl": kl, "r_star": r_star,
             "pack_info": pinfo, "packed": packed, **sq}

@@ -151,3 +151,19 @@ def test_qlinear_validation(lib):
     assert call(ws=0) == -5
     assert lib.slim_qlinear_workspace(1, 4096, 4096, 128) > 0
     assert lib.slim_qlinear_workspace(9, 4096, 4096, 128) == 0
+
+
+def test_gptq_validation(lib):
+    def call(**kw):
+        return lib.slim_gptq_quantize(kw.get("H", FAKE), kw.get("m", 256), kw.get("damp", 0.01), kw.get("W", FAKE),
+                                      kw.get("wdt", 1), kw.get("n", 64), kw.get("g", 128), FAKE, FAKE,
+                                      kw.get("lam", 0.1), kw.get("n_tau", 50), FAKE, FAKE, FAKE, FAKE, None,
+                                      kw.get("info", FAKE), kw.get("ws", FAKE), kw.get("wsb", 1 << 40), None)
+    assert call(H=None) == -1 and call(W=None) == -1 and call(info=None) == -1
+    assert call(wdt=3) == -3
+    assert call(n=0) == -2 and call(m=200) == -2 and call(g=96) == -2
+    assert call(damp=-1.0) == -4 and call(n_tau=0) == -4 and call(lam=1.0) == -4
+    assert call(ws=None) == -5 and call(wsb=16) == -5
+    assert call(H=ctypes.c_void_p(4100)) == -7
+    assert lib.slim_gptq_workspace(64, 256, 128) > lib.slim_salience_workspace(64, 256, 128)
+    assert lib.slim_gptq_workspace(64, 250, 128) == 0

@@ -1,0 +1,139 @@
+"""Parity of the GPTQ sweep around the group quantizer (slim_gptq_quantize)
+with the oracle, through the C ABI.
+
+Inputs: H, d and the widths are the oracle's (from seeded synthetic X and W),
+handed to both sides.  The bar is the integer one: codes, tau indices and
+masks bit-equal, scale and zero bit-equal.  Both sides take every decision
+in the same arithmetic: the quantizer's float32 sequence on the current
+weight rounded to float32, float64 error feedback with the same order inside
+a group; only the float64 trailing product after each group sums in another
+order (relative differences near 1e-16), so a code could differ only at a
+float64 tie.  At full size the oracle runs on sampled rows, which is exact:
+given U, each row's sweep depends on that row alone.
+"""
+import numpy as np
+import pytest
+
+import oracle
+from gpu_helpers import TIE, dev, host
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(scope="module")
+def slim():
+    import post_mixed_precision_amd as s
+    s.load_library()
+    return s
+
+
+def _inputs(n, m, g, N, dtype, seed, tokens=512):
+    import synth
+    wl = synth.custom(tokens=tokens, dtype=dtype, n=n, m=m, dist="t5", wid=80 + seed)
+    X, W = synth.make_x(wl, m), synth.make_w(wl, 0)
+    H = oracle.hessian(X).astype(np.float32)
+    d32, S, info = oracle.salience(H, W, g)
+    assert info == 0
+    k = m // g
+    bits = oracle.allocation(oracle.rank_groups(S), max(1, k // 4), N)
+    return H, W, d32, bits
+
+
+def _run(slim, H, W, bits, d32, g, dtype):
+    out = slim.gptq_quantize(torch.from_numpy(H).to("cuda:0"), dev(W, torch, dtype == "bf16"),
+                             torch.from_numpy(bits).to("cuda:0"), torch.from_numpy(d32).to("cuda:0"), g)
+    torch.cuda.synchronize()
+    return {k: (host(v) if v is not None else None) for k, v in out.items()}
+
+
+def _compare(r, o, g):
+    """Exact equality, except after a row's first near-tie calibration (the
+    oracle's best two tau candidates within TIE relative, or a weight within
+    TIE sigma of the 3-sigma threshold): a different tau* or mask there gives
+    that row another quantizer and so other errors for the rest of the sweep.
+    Returns the number of rows compared in full."""
+    n, k = o["scale"].shape
+    m = k * g
+    tie = (o["gap"] < TIE) | np.any(o["margin"].reshape(n, k, g) < TIE, axis=2)
+    first = np.where(tie.any(axis=1), np.argmax(tie, axis=1), k)
+    words = (o["mask"].reshape(n, m // 32, 32).astype(np.uint64) << np.arange(32, dtype=np.uint64)).sum(-1)
+    words = words.astype(np.uint32)
+    rmask = r["mask"].view(np.uint32)
+    for i in range(n):
+        jq = int(first[i])
+        cq = jq * g
+        assert np.array_equal(r["codes"][i, :cq], o["codes"][i, :cq]), f"codes of row {i} before group {jq}"
+        assert np.array_equal(r["scale"][i, :jq], o["scale"][i, :jq]), f"scale of row {i}"
+        assert np.array_equal(r["zero"][i, :jq], o["zero"][i, :jq]), f"zero of row {i}"
+        assert np.array_equal(r["tau_idx"][i, :jq], o["tau_idx"][i, :jq]), f"tau of row {i}"
+        assert np.array_equal(rmask[i, :cq // 32], words[i, :cq // 32]), f"mask of row {i}"
+    full = int(np.sum(first == k))
+    print(f"  rows compared in full: {full} of {n}", flush=True)
+    return full
+
+
+@pytest.mark.parametrize("n,m,g,N,dtype", [
+    (130, 256, 64, 2, "bf16"),    # ragged row block
+    (64, 384, 128, 3, "f32"),
+    (200, 96, 32, 2, "f32"),      # m not a multiple of 64: padded factor
+    (1, 128, 32, 4, "bf16"),      # one row
+    (257, 512, 128, 2, "bf16"),   # several trailing tiles, ragged rows
+])
+def test_gptq_parity(slim, n, m, g, N, dtype):
+    print(f"gptq n={n} m={m} g={g} N={N} {dtype}", flush=True)
+    H, W, d32, bits = _inputs(n, m, g, N, dtype, seed=n % 7)
+    r = _run(slim, H, W, bits, d32, g, dtype)
+    assert int(r["info"][0]) == 0
+    o = oracle.gptq_quantize(W, H, bits, d32, g)
+    assert _compare(r, o, g) >= 0.9 * n
+
+
+def test_gptq_diagonal_hessian_equals_sqc(slim):
+    # no column coupling: the sweep must reproduce the plain calibration
+    rng = np.random.default_rng(9)
+    n, m, g = 96, 256, 64
+    H = np.diag(rng.uniform(0.5, 4.0, m)).astype(np.float32)
+    W = rng.standard_normal((n, m)).astype(np.float32)
+    d32, S, _ = oracle.salience(H, W, g)
+    bits = oracle.allocation(oracle.rank_groups(S), 1, 2)
+    r = _run(slim, H, W, bits, d32, g, "f32")
+    sq = slim.sqc_calibrate(torch.from_numpy(W).to("cuda:0"), torch.from_numpy(bits).to("cuda:0"),
+                            torch.from_numpy(d32).to("cuda:0"), g)
+    torch.cuda.synchronize()
+    assert np.array_equal(r["codes"], host(sq["codes"]))
+    assert np.array_equal(r["scale"], host(sq["scale"])) and np.array_equal(r["zero"], host(sq["zero"]))
+
+
+def test_gptq_failure_codes(slim):
+    n, m, g = 8, 64, 32
+    W = np.ones((n, m), np.float32)
+    bits = np.array([2, 2], np.int8)
+    d32 = np.ones(m, np.float32)
+    H = -np.eye(m, dtype=np.float32)                 # not positive definite at order 1
+    r = _run(slim, H, W, bits, d32, g, "f32")
+    assert int(r["info"][0]) == 1
+    H = np.eye(m, dtype=np.float32)
+    W[3, 5] = np.inf
+    r = _run(slim, H, W, bits, d32, g, "f32")
+    assert int(r["info"][0]) == -1
+
+
+def test_gptq_full_size_sampled_rows(slim):
+    # the 4096 x 4096 q_proj layer (bf16), H from 8192 of its calibration tokens
+    import synth
+    wl = synth.WORKLOADS["llama7b-attn-4096"]
+    print("gptq 4096 x 4096, H from 8192 tokens", flush=True)
+    X = synth.make_x(wl, 4096, 0, 8192)
+    W = synth.make_w(wl, 0)
+    H = oracle.hessian(X).astype(np.float32)
+    d32, S, info = oracle.salience(H, W, 128)
+    assert info == 0
+    bits = oracle.allocation(oracle.rank_groups(S), 3, 2)
+    r = _run(slim, H, W, bits, d32, 128, "bf16")
+    assert int(r["info"][0]) == 0
+    rows = np.concatenate([np.random.default_rng(11).choice(4096, 30, replace=False), [0, 4095]])
+    o = oracle.gptq_quantize(W[rows], H, bits, d32, 128)
+    sub = {k: r[k][rows] for k in ("codes", "scale", "zero", "tau_idx", "mask")}
+    assert _compare(sub, o, 128) >= 0.9 * len(rows)
