@@ -81,7 +81,7 @@ def measured_traffic(workload: str, linear: str, group: int):
         return None
 
 
-def run_step(slim, X, W, group, N, ev=None, variant=None):
+def run_step(slim, X, W, group, N, ev=None, variant=None, gptq=False):
     """One pass of the whole path; optional event list records stage boundaries."""
     def mark(i):
         if ev is not None:
@@ -98,7 +98,10 @@ def run_step(slim, X, W, group, N, ev=None, variant=None):
         bits, kl, rs = slim.sba_search_ex(X, W, group, N, group_sal=None if order is not None else gsal,
                                           order=order, objective=objective)
     mark(3)
-    sq = slim.sqc_calibrate(W, bits, hinv, group, 0.1, 50, want_tau=False)
+    if gptq:   # the quantizer inside GPTQ's error-compensating sweep
+        sq = slim.gptq_quantize(H, W, bits, hinv, group, 0.01, 0.1, 50, want_tau=False)
+    else:
+        sq = slim.sqc_calibrate(W, bits, hinv, group, 0.1, 50, want_tau=False)
     mark(4)
     packed, pinfo = slim.pack(sq["codes"], bits, group, N)
     mark(5)
@@ -222,6 +225,8 @@ def main():
                     help="group order of the SBA scan (the method's is salience)")
     ap.add_argument("--ablation-report", action="store_true",
                     help="also run the scan once per objective/order and report r* and the best score")
+    ap.add_argument("--gptq", action="store_true",
+                    help="calibrate and quantize the groups inside GPTQ's error-compensating sweep")
     ap.add_argument("--qlinear-shape", default=None,
                     help="NxM: time only the packed-plane linear layer on a synthetic N x M layer "
                          "(random planes, widths avg_bits +- 1) and print its own JSON line")
@@ -279,7 +284,7 @@ def main():
         variant = (args.objective, order)
 
     for i in range(args.warmup):
-        info, pinfo, rs, kl = run_step(slim, X, W, group, N, variant=variant)
+        info, pinfo, rs, kl = run_step(slim, X, W, group, N, variant=variant, gptq=args.gptq)
         torch.cuda.synchronize()
         print(f"# warmup {i}: info={int(info.item())} r*={int(rs.item())}", file=sys.stderr, flush=True)
     assert int(info.item()) == 0 and int(pinfo.item()) == 0
@@ -291,7 +296,7 @@ def main():
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for s in range(args.steps):
-        run_step(slim, X, W, group, N, evs[s], variant=variant)
+        run_step(slim, X, W, group, N, evs[s], variant=variant, gptq=args.gptq)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     slim.timing_enable(False)
@@ -310,6 +315,8 @@ def main():
     qms, ql = slim.timing_read("sqc_calibrate")
     pms, pl = slim.timing_read("pack_planes")
     cms, cl = slim.timing_read("chol_update")
+    gsms, gsl = slim.timing_read("gptq_sweep")
+    gtms, gtl = slim.timing_read("gptq_trail")
     print(f"# sba_klgemm {ms_per_launch:.3f} ms/launch ({launches_per_step:.0f}/step); "
           f"stages ms {json.dumps({k: round(v, 3) for k, v in stages.items()})}", file=sys.stderr, flush=True)
 
@@ -322,7 +329,8 @@ def main():
         "data": "synthetic (seeded; stands in for 128x2048 WikiText2 tokens and LLaMA weights)",
         "config": {"workload": args.workload, "linear": lin.name, "n": n, "m": m, "tokens": T,
                    "group": group, "avg_bits": N, "tau_lambda": wl.tau_lambda, "tau_steps": wl.tau_steps,
-                   "sba_objective": args.objective, "sba_order": args.order},
+                   "sba_objective": args.objective, "sba_order": args.order,
+                   "backbone": "gptq" if args.gptq else "none"},
         "roofline": {"bound": "mfma", "kernel": "sba_klgemm", "achieved": round(achieved / 1e12, 2),
                      "peak": PEAK_BF16_FLOPS / 1e12, "unit": "TFLOP/s",
                      "frac": round(achieved / PEAK_BF16_FLOPS, 4), "traffic": None,
@@ -366,6 +374,13 @@ def main():
                           "achieved_gbps": round(qbytes / sec_q / 1e9, 1),
                           "frac": round(qbytes / sec_q / PEAK_HBM_BPS, 4)}
     out.setdefault("roofline_other", {})["qlinear"] = {"bound": "hbm", **qrep}
+    if args.gptq:
+        out["kernels_ms_per_step"]["gptq_sweep"] = round(gsms / args.steps, 3)
+        out["kernels_ms_per_step"]["gptq_trail"] = round(gtms / args.steps, 3)
+        # trailing products: sum over groups of 2 n g (m - (j+1) g) = n m (m - g) flops per step
+        tflops = n * m * (m - group) / (gtms / args.steps * 1e-3) / 1e12 if gtl else 0.0
+        out.setdefault("roofline_other", {})["gptq_trail"] = {"bound": "mfma", "achieved_tflops": round(tflops, 2),
+                                                              "peak": 78.6, "frac": round(tflops / 78.6, 4)}
     if args.ablation_report:
         # The pages' ablation structure on this layer: the scan under each
         # objective and group order (untimed; r* and the best score).

@@ -19,12 +19,13 @@
 //   1. SQC calibrates the group on its current, already compensated weights
 //      (a float32 copy kept up to date for the next group), fixing scale and
 //      zero for the group's columns;
-//   2. gptq_sweep: one thread per row walks the group's columns in 16-column
-//      sub-blocks.  Inside a sub-block the weights sit in registers and every
-//      quantized column updates the rest of the sub-block at once; after a
-//      sub-block its 16 errors update the group's later columns (held in LDS)
-//      as one rank-16 step.  Codes are the quantizer's float32 decision on
-//      the current weight rounded to float32; errors and updates are float64.
+//   2. gptq_sweep: a quad of lanes per row walks the group's columns in
+//      16-column sub-blocks.  Inside a sub-block every quantized column
+//      updates the rest of the sub-block at once; after a sub-block its 16
+//      errors update the group's later columns (spread over the quad's
+//      LDS slots) as one rank-16 step.  Codes are the quantizer's float32
+//      decision on the current weight rounded to float32; errors and updates
+//      are float64.
 //   3. gptq_trail: W[:, after the group] -= E U[group, after the group], a
 //      float64 MFMA product over 64 x 64 tiles, which also refreshes the
 //      float32 copy of the next group.
@@ -65,8 +66,15 @@ __global__ __launch_bounds__(256) void gptq_prep_kernel(const void *__restrict__
   if (bad) atomicExch(info, -1);
 }
 
-// The column sweep of group j for 64 rows (one wave).  slab[c][lane] holds
-// the row's current weight of group column c.
+// The column sweep of group j for 16 rows (one wave): a row is held by a quad
+// of lanes; lane q of the quad keeps, of every 16-column sub-block, columns
+// 4q .. 4q+3 (slot 4 sb + t of the lane is column 16 sb + 4q + t; the slots
+// live in LDS, slab[slot][lane]).  For each sub-block the quad first gathers
+// its 16 weights into every lane, each lane runs the sub-block's sequential
+// part (the same arithmetic in all four), then each lane applies the
+// sub-block's 16 errors to its own columns of the later sub-blocks.  Every
+// weight sees the same float64 operations in the same order as in a
+// one-thread-per-row sweep.
 template <int G>
 __global__ __launch_bounds__(64) void gptq_sweep_kernel(const double *__restrict__ W64, int64_t n, int64_t m,
                                                         int j, const double *__restrict__ U,
@@ -75,61 +83,78 @@ __global__ __launch_bounds__(64) void gptq_sweep_kernel(const double *__restrict
                                                         const float *__restrict__ zero,
                                                         const int8_t *__restrict__ bits, uint8_t *__restrict__ codes,
                                                         double *__restrict__ Err) {
-  __shared__ double slab[G * 64];
-  const int t = threadIdx.x;
-  const int64_t i = (int64_t)blockIdx.x * 64 + t;
+  constexpr int NSB = G / GQ_SB;
+  __shared__ double slab[NSB * 4 * 64];
+  const int lane = threadIdx.x;
+  const int q = lane & 3;                 // lane in the quad
+  const int qbase = lane & ~3;
+  const int64_t i = (int64_t)blockIdx.x * 16 + (lane >> 2);
   const bool live = i < n;
   const int64_t il = live ? i : n - 1;
   const int64_t k = m / G;
   const int64_t c0 = (int64_t)j * G;
-  {
-    const double2 *src = (const double2 *)(W64 + il * m + c0);
-#pragma unroll 4
-    for (int c = 0; c < G / 2; ++c) {
-      const double2 v = src[c];
-      slab[(2 * c) * 64 + t] = v.x;
-      slab[(2 * c + 1) * 64 + t] = v.y;
-    }
+  for (int sb = 0; sb < NSB; ++sb) {
+    const double2 *src = (const double2 *)(W64 + il * m + c0 + sb * GQ_SB + 4 * q);
+    const double2 a = src[0], b = src[1];
+    slab[(4 * sb) * 64 + lane] = a.x;
+    slab[(4 * sb + 1) * 64 + lane] = a.y;
+    slab[(4 * sb + 2) * 64 + lane] = b.x;
+    slab[(4 * sb + 3) * 64 + lane] = b.y;
   }
   const float s = scale[il * k + j], z = zero[il * k + j];
   const float maxq = (float)((1 << bits[j]) - 1);
   const float r = 1.0f / s;
-  for (int sb = 0; sb < G / GQ_SB; ++sb) {
+  for (int sb = 0; sb < NSB; ++sb) {
     const int64_t cb = c0 + sb * GQ_SB;   // first column of the sub-block
     double w[GQ_SB], e[GQ_SB];
+    {
+      double mine[4];
 #pragma unroll
-    for (int c = 0; c < GQ_SB; ++c) w[c] = slab[(sb * GQ_SB + c) * 64 + t];
-    uint32_t cw[GQ_SB / 4] = {0, 0, 0, 0};
+      for (int t = 0; t < 4; ++t) mine[t] = slab[(4 * sb + t) * 64 + lane];
+#pragma unroll
+      for (int qq = 0; qq < 4; ++qq)
+#pragma unroll
+        for (int t = 0; t < 4; ++t) w[4 * qq + t] = __shfl(mine[t], qbase + qq, 64);
+    }
+    uint32_t cw = 0;
 #pragma unroll
     for (int c = 0; c < GQ_SB; ++c) {
       // the quantizer's float32 sequence on the current weight
       const float w32 = (float)w[c];
       float tq = w32 * r;
       tq = tq + z;
-      float q = rintf(tq);
-      q = fminf(fmaxf(q, 0.0f), maxq);
-      const float dq = q - z;
+      float qv = rintf(tq);
+      qv = fminf(fmaxf(qv, 0.0f), maxq);
+      const float dq = qv - z;
       const float wh = dq * s;
       const double *urow = U + (cb + c) * m + cb;
       e[c] = (w[c] - (double)wh) / urow[c];
 #pragma unroll
       for (int c2 = c + 1; c2 < GQ_SB; ++c2) w[c2] = w[c2] - e[c] * urow[c2];
-      cw[c >> 2] |= ((uint32_t)q & 0xffu) << (8 * (c & 3));
+      if ((c >> 2) == q) cw |= ((uint32_t)qv & 0xffu) << (8 * (c & 3));
     }
     if (live) {
-      *(uint4 *)(codes + i * m + cb) = make_uint4(cw[0], cw[1], cw[2], cw[3]);
-      double2 *ed = (double2 *)(Err + i * G + sb * GQ_SB);
+      *(uint32_t *)(codes + i * m + cb + 4 * q) = cw;
+      double e4[4];
 #pragma unroll
-      for (int c = 0; c < GQ_SB / 2; ++c) ed[c] = make_double2(e[2 * c], e[2 * c + 1]);
+      for (int t = 0; t < 4; ++t) e4[t] = q == 0 ? e[t] : (q == 1 ? e[4 + t] : (q == 2 ? e[8 + t] : e[12 + t]));
+      double2 *ed = (double2 *)(Err + i * G + sb * GQ_SB + 4 * q);
+      ed[0] = make_double2(e4[0], e4[1]);
+      ed[1] = make_double2(e4[2], e4[3]);
     }
-    // the sub-block's errors onto the group's later columns, one column at a
-    // time and in column order within the update, as the sweep defines it
-    for (int c2 = (sb + 1) * GQ_SB; c2 < G; ++c2) {
-      const double *ucol = Ut + (c0 + c2) * m + cb;   // U[cb .. cb+15][c0 + c2]
-      double v = slab[c2 * 64 + t];
+    // the sub-block's errors onto this lane's columns of the later sub-blocks,
+    // in column order within the update (four independent chains)
+    for (int sb2 = sb + 1; sb2 < NSB; ++sb2) {
+      const double *ucol = Ut + (c0 + sb2 * GQ_SB + 4 * q) * m + cb;   // U[cb .. cb+15][column 4q + t]
+      double v[4];
 #pragma unroll
-      for (int c = 0; c < GQ_SB; ++c) v = v - e[c] * ucol[c];
-      slab[c2 * 64 + t] = v;
+      for (int t = 0; t < 4; ++t) v[t] = slab[(4 * sb2 + t) * 64 + lane];
+#pragma unroll
+      for (int c = 0; c < GQ_SB; ++c)
+#pragma unroll
+        for (int t = 0; t < 4; ++t) v[t] = v[t] - e[c] * ucol[t * m + c];
+#pragma unroll
+      for (int t = 0; t < 4; ++t) slab[(4 * sb2 + t) * 64 + lane] = v[t];
     }
   }
 }
@@ -203,7 +228,7 @@ static void gq_group(double *W64, float *W32, int64_t n, int64_t m, int j, const
                      hipStream_t st) {
   const unsigned nrb = (unsigned)((n + 63) / 64);
   timer_begin(K_GPTQ_SWEEP, st);
-  gptq_sweep_kernel<G><<<nrb, 64, 0, st>>>(W64, n, m, j, U, Ut, scale, zero, bits, codes, Err);
+  gptq_sweep_kernel<G><<<(unsigned)((n + 15) / 16), 64, 0, st>>>(W64, n, m, j, U, Ut, scale, zero, bits, codes, Err);
   timer_end(K_GPTQ_SWEEP, st);
   const int64_t c1 = (int64_t)(j + 1) * G;
   if (c1 < m) {
