@@ -431,16 +431,18 @@ __global__ __launch_bounds__(512, 1) void sba_klgemm_kernel(
             if (!PARTIAL || ob * 32 + 8 * (v >> 2) + (v & 3) < lim) mx = fmaxf(mx, accY[ob * 2 + tb][v]);
         mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
         float z = 0.0f, sy = 0.0f;
+        const float mx2 = mx * 1.44269504088896341f;   // the same exp form as for yhat below
 #pragma unroll
         for (int ob = 0; ob < 2; ++ob)
 #pragma unroll
           for (int v = 0; v < 16; ++v) {
             const float y = accY[ob * 2 + tb][v];
             float e = 0.0f;
-            if (!PARTIAL || ob * 32 + 8 * (v >> 2) + (v & 3) < lim) e = __expf(y - mx);
+            if (!PARTIAL || ob * 32 + 8 * (v >> 2) + (v & 3) < lim)
+              e = __builtin_amdgcn_exp2f(__builtin_fmaf(y, 1.44269504088896341f, -mx2));
             accY[ob * 2 + tb][v] = e;
             z += e;
-            sy += e * y;
+            sy = __builtin_fmaf(e, y, sy);
           }
         z += __shfl_xor(z, 32, 64);
         sy += __shfl_xor(sy, 32, 64);
@@ -456,13 +458,16 @@ __global__ __launch_bounds__(512, 1) void sba_klgemm_kernel(
           if (!PARTIAL || ob * 32 + 8 * (v >> 2) + (v & 3) < lim) mq = fmaxf(mq, accQ[ob * 2 + tb][v]);
       mq = fmaxf(mq, __shfl_xor(mq, 32, 64));
       float zq = 0.0f, se = 0.0f;
+      // e^(yh - mq) as 2^(yh log2 e - mq log2 e): one fused multiply-add before v_exp
+      const float mq2 = mq * 1.44269504088896341f;
 #pragma unroll
       for (int ob = 0; ob < 2; ++ob)
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
           const float yh = accQ[ob * 2 + tb][v];
-          if (!PARTIAL || ob * 32 + 8 * (v >> 2) + (v & 3) < lim) zq += __expf(yh - mq);
-          se += accY[ob * 2 + tb][v] * yh;
+          if (!PARTIAL || ob * 32 + 8 * (v >> 2) + (v & 3) < lim)
+            zq += __builtin_amdgcn_exp2f(__builtin_fmaf(yh, 1.44269504088896341f, -mq2));
+          se = __builtin_fmaf(accY[ob * 2 + tb][v], yh, se);
         }
       zq += __shfl_xor(zq, 32, 64);
       se += __shfl_xor(se, 32, 64);
