@@ -15,10 +15,13 @@
 // Z, accumulated panel by panel in a fixed order.  Per panel p:
 //   chol_panel  L_ip = A_ip L_pp^-T for the rows below; Z_p = L_pp^-1 R_p and d += col-norms^2
 //   chol_trail  (part 1) block column p+1 of A and row block p+1 of Z
-//   chol_trail  (part 2) the rest of A_ij -= L_ip L_jp^T and R_ij -= L_ip Z_pj, with
-//               workgroup 0 factoring and inverting diagonal block p+1 meanwhile
-//               (lookahead: the one-workgroup step no longer waits for the bulk update)
+//   chol_diag   factor and invert diagonal block p+1, on a side stream ...
+//   chol_trail  (part 2) ... while the rest of A_ij -= L_ip L_jp^T and
+//               R_ij -= L_ip Z_pj runs (lookahead: the one-workgroup step does
+//               not wait for the bulk update, nor the bulk for it)
 // The GEMM-shaped work uses v_mfma_f64_16x16x4_f64 on 64x64 tiles.
+#include <mutex>
+
 #include "common.hpp"
 #include "f64tile.hpp"
 #include "kernels.hpp"
@@ -75,24 +78,33 @@ __global__ __launch_bounds__(256) void sal_init_kernel(const float *__restrict__
 // Factor the diagonal block of panel p and invert it; writes L_pp into A and
 // (L_pp^-1)^T into TinvT (64 x 64, row k holds column k of the inverse).
 //
-// One sweep of 64 steps.  Step j eliminates column j from the unscaled block
-// (A <- A - a_j a_j^T / a_jj on the trailing part) and applies the same row
-// operation to a right-hand side R that starts as the identity
-// (R_i <- R_i - (a_ij / a_jj) R_j); afterwards L_ij = a_ij / sqrt(a_jj) and
-// (L^-1)_ij = R_ij / sqrt(a_ii).  Thread t keeps its cells of row t / 8
-// (8 contiguous columns) of both arrays in registers; each step only column j
-// of A and row j of R travel through LDS, read unconditionally as 16-byte
-// broadcasts, and the updates are selects rather than branches.
+// Unscaled elimination on the block (A <- A - a_j a_j^T / a_jj on the trailing
+// part, column by column) with the same row operations applied to a
+// right-hand side R that starts as the identity; afterwards
+// L_ij = a_ij / sqrt(a_jj) and (L^-1)_ij = R_ij / sqrt(a_ii).  The columns are
+// taken four at a time: with P the 4 x 4 pivot block and v the row's four
+// entries in its columns (both as they stand when the block is reached),
+// eliminating the four columns one by one amounts to
+//     a_i,c += h_i . v_c  (c past the block),   R_i += h_i . R_block,
+//     h_i = -P^-1 v_i,
+// and the row's entries in the block's columns become L_P^-1 v_i (P = L_P D
+// L_P^T, unit L_P, D the four pivots).  Every thread factors P itself, so one
+// barrier per four columns publishes the block's columns of A and rows of R.
+// Thread t keeps its cells of row t / NS (DC contiguous columns) of both
+// arrays in registers.
 template <int NT>
 __device__ __forceinline__ void chol_diag_body(double *__restrict__ A, int64_t mp, int p, double *__restrict__ TinvT,
                                                int32_t *__restrict__ info) {
   constexpr int DC = NBK * NBK / NT;   // columns per thread
   constexpr int NS = NBK / DC;         // column strips per row
-  // Ping-pong broadcast buffers: step j reads set j & 1 and publishes step
-  // j + 1's column and row into the other set, so one barrier per step keeps
-  // readers and writers apart.
-  __shared__ __attribute__((aligned(16))) double colj[2][NBK];   // column j of the working block
-  __shared__ __attribute__((aligned(16))) double rowj[2][NBK];   // row j of the right-hand side
+  constexpr int EB = 4;                // columns eliminated per barrier
+  static_assert(DC % EB == 0, "a block of columns lies in one strip");
+  // Ping-pong buffers: the block's columns of A (all rows) and rows of R,
+  // both stored [t][pm(c)] with pm(c) = (c % DC) NS + c / DC, so the NS
+  // strips of a row, reading column c0 + q at once, touch consecutive words.
+  __shared__ __attribute__((aligned(16))) double colJ[2][EB][NBK];
+  __shared__ __attribute__((aligned(16))) double rowJ[2][EB][NBK];
+  auto pm = [](int c) __attribute__((always_inline)) { return (c % DC) * NS + c / DC; };
   __shared__ double piv[NBK];
   const int tid = threadIdx.x;
   const int oi = tid / NS, c0 = DC * (tid % NS);   // this thread: row oi, columns c0 .. c0 + DC - 1
@@ -104,57 +116,119 @@ __device__ __forceinline__ void chol_diag_body(double *__restrict__ A, int64_t m
     Lr[q] = (c <= oi) ? A[(k0 + oi) * mp + k0 + c] : 0.0;
     Rr[q] = (c == oi) ? 1.0 : 0.0;
   }
-  if (c0 == 0) colj[0][oi] = Lr[0];
-  if (oi == 0) {
+  // publish block j1's columns of A and rows of R into buffer b
+  auto publish = [&](int j1, int b) __attribute__((always_inline)) {
+    if (j1 >= c0 && j1 < c0 + DC) {
 #pragma unroll
-    for (int q = 0; q < DC; ++q) rowj[0][c0 + q] = Rr[q];
-  }
-  __syncthreads();
-  for (int j = 0; j < NBK; ++j) {
-    const double *cj = colj[j & 1];
-    const double *rj = rowj[j & 1];
-    double a = cj[j];
-    const bool bad = !(a > 0.0) || !isfinite(a);
-    if (bad) a = 1.0;  // reported below; a harmless pivot keeps the sweep finite
-    // 1/a: hardware reciprocal refined by two Newton steps (full double accuracy)
-    double inv = __builtin_amdgcn_rcp(a);
-    inv = __fma_rn(inv, __fma_rn(-a, inv, 1.0), inv);
-    inv = __fma_rn(inv, __fma_rn(-a, inv, 1.0), inv);
-    // Unconditional broadcast reads (contiguous), then branch-free updates.
-    double cv[DC], rv[DC];
+      for (int q = 0; q < DC; q += EB)
+        if (c0 + q == j1) {
 #pragma unroll
-    for (int q = 0; q < DC; q += 2) {
-      const double2 x = *(const double2 *)&cj[c0 + q];
-      const double2 y = *(const double2 *)&rj[c0 + q];
-      cv[q] = x.x; cv[q + 1] = x.y;
-      rv[q] = y.x; rv[q + 1] = y.y;
+          for (int t = 0; t < EB; ++t) colJ[b][t][pm(oi)] = Lr[q + t];
+        }
     }
-    const double f = (oi > j) ? -(cj[oi] * inv) : 0.0;
+    if (oi >= j1 && oi < j1 + EB) {
+#pragma unroll
+      for (int q = 0; q < DC; ++q) rowJ[b][oi - j1][pm(c0 + q)] = Rr[q];
+    }
+  };
+  publish(0, 0);
+  __syncthreads();
+#pragma unroll 1
+  for (int blk = 0; blk < NBK / EB; ++blk) {
+    const int j0 = blk * EB, b = blk & 1;
+    // LDL^T of the pivot block (every thread alike): L(t, s) below the unit
+    // diagonal, d[s] the pivots; a non-positive or non-finite pivot is
+    // reported and replaced by 1 so the sweep stays finite.
+    // In place: below the diagonal P ends holding L, on it the pivots d.
+    double P[EB][EB], dinv[EB];
+#pragma unroll
+    for (int t = 0; t < EB; ++t)
+#pragma unroll
+      for (int s = 0; s <= t; ++s) P[t][s] = colJ[b][s][pm(j0 + t)];
+    int bad_at = -1;
+#pragma unroll
+    for (int s = 0; s < EB; ++s) {
+      double a = P[s][s];
+      if (!(a > 0.0) || !isfinite(a)) {
+        if (bad_at < 0) bad_at = s;
+        a = 1.0;
+      }
+      P[s][s] = a;
+      double inv = __builtin_amdgcn_rcp(a);
+      inv = __fma_rn(inv, __fma_rn(-a, inv, 1.0), inv);
+      inv = __fma_rn(inv, __fma_rn(-a, inv, 1.0), inv);
+      dinv[s] = inv;
+      // later rows first, so the unscaled P[u][s] (u < t) are still there
+#pragma unroll
+      for (int t = EB - 1; t > s; --t) {
+        const double l = P[t][s] * inv;
+#pragma unroll
+        for (int u = s + 1; u <= t; ++u) P[t][u] = __fma_rn(-l, P[u][s], P[t][u]);
+        P[t][s] = l;
+      }
+    }
+#define L(t, s) P[t][s]
+    double d[EB];
+#pragma unroll
+    for (int s = 0; s < EB; ++s) d[s] = P[s][s];
+    if (tid == 0) {
+#pragma unroll
+      for (int s = 0; s < EB; ++s) piv[j0 + s] = d[s];
+      if (bad_at >= 0) atomicCAS(info, 0, (int)(k0 + j0 + bad_at + 1));
+    }
+    // Coefficients of this row, branch-free, from one solve with P = L D L^T:
+    // u = L^-1 v (v: the row's entries in the block's columns), then
+    // h_s = -u_s / d_s - sum_{r > s} L(r, s) h_r over s < lim.  Rows past the
+    // block (lim = 4): h = -P^-1 v drives both updates and u holds their final
+    // entries in the block's columns.  A row of the block (lim = tt = oi - j0):
+    // its entries v_s vanish past s = tt, u_s = d_s L(tt, s) for s < tt are its
+    // final entries, and h is row tt of L^-1 below the diagonal, the
+    // coefficients of its R row.  Rows above the block (lim = 0) keep
+    // everything.
+    const bool below = oi >= j0 + EB, inblk = oi >= j0 && !below;
+    const int tt = oi - j0;
+    const int lim = below ? EB : (inblk ? tt : 0);
+    double u[EB], h[EB], bv[EB];
+    {
+      double v[EB];
+#pragma unroll
+      for (int t = 0; t < EB; ++t) v[t] = colJ[b][t][pm(oi)];
+#pragma unroll
+      for (int s2 = 0; s2 < EB; ++s2) {
+        double x = v[s2];
+#pragma unroll
+        for (int r = 0; r < s2; ++r) x = __fma_rn(-L(s2, r), u[r], x);
+        u[s2] = x;
+      }
+#pragma unroll
+      for (int s2 = EB - 1; s2 >= 0; --s2) {
+        double x = -u[s2] * dinv[s2];
+#pragma unroll
+        for (int r = s2 + 1; r < EB; ++r) x = __fma_rn(-L(r, s2), h[r], x);
+        h[s2] = s2 < lim ? x : 0.0;
+      }
+#pragma unroll
+      for (int s2 = 0; s2 < EB; ++s2) bv[s2] = (inblk && s2 == tt) ? d[s2] : u[s2];
+    }
+    // A column is either past the block (A's trailing part) or not (R's
+    // columns up to the block): one chain of EB fused multiply-adds on the
+    // matching buffer (both are stored [t][pm(c)]).
 #pragma unroll
     for (int q = 0; q < DC; ++q) {
       const int c = c0 + q;
-      const double nl = __fma_rn(f, cv[q], Lr[q]);
-      const double nr = __fma_rn(f, rv[q], Rr[q]);
-      Lr[q] = (c > j && c <= oi) ? nl : Lr[q];
-      Rr[q] = (c <= j) ? nr : Rr[q];
-    }
-    if (tid == 0) {
-      piv[j] = a;
-      if (bad) atomicCAS(info, 0, (int)(k0 + j + 1));
-    }
-    const int jn = j + 1;
-    if (jn < NBK) {
-      double *cn = colj[jn & 1];
-      double *rn = rowj[jn & 1];
-      double pv = 0.0;
+      const bool isA = c >= j0 + EB;
+      const double *src = (isA ? &colJ[b][0][0] : &rowJ[b][0][0]) + pm(c);
+      double acc = isA ? Lr[q] : Rr[q];
 #pragma unroll
-      for (int q = 0; q < DC; ++q) pv = (c0 + q == jn) ? Lr[q] : pv;
-      if (jn >= c0 && jn < c0 + DC) cn[oi] = pv;
-      if (oi == jn) {
+      for (int t = 0; t < EB; ++t) acc = __fma_rn(h[t], src[t * NBK], acc);
+      double blockv = bv[0];
 #pragma unroll
-        for (int q = 0; q < DC; q += 2) *(double2 *)&rn[c0 + q] = make_double2(Rr[q], Rr[q + 1]);
-      }
+      for (int t = 1; t < EB; ++t) blockv = (c - j0 == t) ? bv[t] : blockv;
+      const bool inJ = c >= j0 && !isA;
+      Lr[q] = isA ? ((below && c <= oi) ? acc : Lr[q]) : ((inJ && c <= oi && (below || inblk)) ? blockv : Lr[q]);
+      Rr[q] = isA ? Rr[q] : acc;
     }
+    if (blk + 1 < NBK / EB) publish(j0 + EB, b ^ 1);
     __syncthreads();
   }
   const double si = sqrt(piv[oi]);
@@ -272,19 +346,12 @@ __device__ __forceinline__ void trail_tile(double *__restrict__ A, double *__res
 //                      row block p+1 of Z (column blocks 0 .. p);
 //   part 2 (next = 0): A tiles with row >= column >= p+2, and Z row blocks
 //                      p+2 .. NB-1 (column blocks 0 .. p).
-// With diag set, workgroup 0 instead factors diagonal block p+1 (its inputs
-// are final once part 1 has run), concurrently with part 2.
+// Diagonal block p+1 is factored by its own launch between the two parts
+// (its inputs are final once part 1 has run).
 __global__ __launch_bounds__(256) void chol_trail_kernel(double *__restrict__ A, double *__restrict__ Z,
                                                          double *__restrict__ TinvT, int32_t *__restrict__ info,
-                                                         int64_t mp, int p, int NB, int next, int diag) {
-  int64_t w = blockIdx.x;
-  if (diag) {
-    if (w == 0) {
-      chol_diag_body<256>(A, mp, p + 1, TinvT, info);
-      return;
-    }
-    --w;
-  }
+                                                         int64_t mp, int p, int NB, int next) {
+  const int64_t w = blockIdx.x;
   const int64_t k0 = (int64_t)p * NBK;
   int ii, jj;
   bool zt;
@@ -388,6 +455,22 @@ size_t salience_ws_bytes(int64_t n, int64_t m, int group) {
   return off;
 }
 
+// One side stream per device (default priority, non-blocking), created on
+// first use and kept for the life of the process; null if it cannot be made.
+static hipStream_t side_stream() {
+  static std::mutex mu;
+  static hipStream_t streams[64] = {};
+  static bool tried[64] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return nullptr;
+  std::lock_guard<std::mutex> lk(mu);
+  if (!tried[dev]) {
+    tried[dev] = true;
+    if (hipStreamCreateWithFlags(&streams[dev], hipStreamNonBlocking) != hipSuccess) streams[dev] = nullptr;
+  }
+  return streams[dev];
+}
+
 hipError_t launch_chol_inverse(const float *H, int64_t m, double damp, bool reverse, double *A, double *Z,
                                double *TinvT, double *d, double *alpha, int32_t *info, hipStream_t st) {
   const int64_t mp = pad64(m);
@@ -397,23 +480,49 @@ hipError_t launch_chol_inverse(const float *H, int64_t m, double damp, bool reve
     if (blocks > 65536) blocks = 65536;
     sal_init_kernel<<<(unsigned)blocks, 256, 0, st>>>(H, m, mp, alpha, A, Z, d, info, reverse ? 1 : 0);
   }
-  // Lookahead: once the block column after panel p is updated, the next
-  // diagonal block is factored in the same launch as the rest of the trailing
-  // update, so the one-workgroup factorisation overlaps the bulk update.
+  // Lookahead: once the block column after panel p is updated (part 1), the
+  // next diagonal block is factored on a side stream while the rest of the
+  // trailing update (part 2) runs; the next panel waits for both.  The two
+  // touch disjoint data: part 2 the tiles with row >= column >= p + 2 and Z's
+  // later row blocks, the diagonal step block (p + 1, p + 1) and TinvT.
+  // Without a side stream the step runs in order between the two parts.
   const int NB = (int)(mp / NBK);
+  hipStream_t side = side_stream();
+  hipEvent_t evA = nullptr, evB = nullptr;
+  if (side && (hipEventCreateWithFlags(&evA, hipEventDisableTiming) != hipSuccess ||
+               hipEventCreateWithFlags(&evB, hipEventDisableTiming) != hipSuccess)) {
+    if (evA) (void)hipEventDestroy(evA);
+    evA = nullptr;
+    side = nullptr;
+  }
   chol_diag_kernel<<<1, 512, 0, st>>>(A, mp, 0, TinvT, info);
-  for (int p = 0; p < NB; ++p) {
+  hipError_t err = hipSuccess;
+  for (int p = 0; p < NB && err == hipSuccess; ++p) {
     const int nrow = NB - p - 1;
     chol_panel_kernel<<<nrow + p + 1, 256, 0, st>>>(A, Z, TinvT, d, mp, p, nrow);
     if (nrow > 0) {
-      chol_trail_kernel<<<(unsigned)(nrow + p + 1), 256, 0, st>>>(A, Z, TinvT, info, mp, p, NB, 1, 0);
+      chol_trail_kernel<<<(unsigned)(nrow + p + 1), 256, 0, st>>>(A, Z, TinvT, info, mp, p, NB, 1);
+      if (side) {
+        err = hipEventRecord(evA, st);
+        if (err == hipSuccess) err = hipStreamWaitEvent(side, evA, 0);
+        chol_diag_kernel<<<1, 512, 0, side>>>(A, mp, p + 1, TinvT, info);
+        if (err == hipSuccess) err = hipEventRecord(evB, side);
+      } else {
+        chol_diag_kernel<<<1, 512, 0, st>>>(A, mp, p + 1, TinvT, info);
+      }
       const int64_t n2 = nrow - 1;
       const int64_t rest = n2 * (n2 + 1) / 2 + n2 * (p + 1);
-      timer_begin(K_CHOL_UPDATE, st);
-      chol_trail_kernel<<<(unsigned)(rest + 1), 256, 0, st>>>(A, Z, TinvT, info, mp, p, NB, 0, 1);
-      timer_end(K_CHOL_UPDATE, st);
+      if (rest > 0) {
+        timer_begin(K_CHOL_UPDATE, st);
+        chol_trail_kernel<<<(unsigned)rest, 256, 0, st>>>(A, Z, TinvT, info, mp, p, NB, 0);
+        timer_end(K_CHOL_UPDATE, st);
+      }
+      if (side && err == hipSuccess) err = hipStreamWaitEvent(st, evB, 0);
     }
   }
+  if (evA) (void)hipEventDestroy(evA);
+  if (evB) (void)hipEventDestroy(evB);
+  if (err != hipSuccess) return err;
   return hipGetLastError();
 }
 
