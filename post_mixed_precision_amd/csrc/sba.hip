@@ -49,6 +49,20 @@ constexpr uint32_t OOB = 0x7ffffff0u;          // offset beyond every range: the
 
 typedef __attribute__((address_space(3))) void lds_void_t;
 
+// Lanes l and l ^ 32 combined in registers.  v_permlane32_swap exchanges the
+// upper 32 lanes of its first operand with the lower 32 lanes of its second;
+// swapping a value with itself leaves every lane holding the lower-half and
+// the upper-half value of its pair, so their sum (or max) is the pair's, in
+// the same order on both lanes.
+__device__ __forceinline__ float pair_sum32(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float pair_max32(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
 // ---------------------------------------------------------------------------
 // Trial weights at tau = 1 for the three widths N-1, N, N+1: Wv[v][n][m].
 // LPS lanes per row segment, 8 weights per lane.
@@ -404,7 +418,7 @@ __global__ __launch_bounds__(512, 1) void sba_klgemm_kernel(
             const float d = accY[ob * 2 + tb][v] - accQ[ob * 2 + tb][v];
             if (!PARTIAL || ob * 32 + 8 * (v >> 2) + (v & 3) < lim) se = __builtin_fmaf(d, d, se);
           }
-        se += __shfl_xor(se, 32, 64);
+        se = pair_sum32(se);
         if (lane < 32) xq[wo][wt * 64 + tb * 32 + lane] = make_float4(0.0f, 0.0f, se, 0.0f);
       }
       __syncthreads();
@@ -429,7 +443,7 @@ __global__ __launch_bounds__(512, 1) void sba_klgemm_kernel(
 #pragma unroll
           for (int v = 0; v < 16; ++v)
             if (!PARTIAL || ob * 32 + 8 * (v >> 2) + (v & 3) < lim) mx = fmaxf(mx, accY[ob * 2 + tb][v]);
-        mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+        mx = pair_max32(mx);
         float z = 0.0f, sy = 0.0f;
         const float mx2 = mx * 1.44269504088896341f;   // the same exp form as for yhat below
 #pragma unroll
@@ -444,8 +458,8 @@ __global__ __launch_bounds__(512, 1) void sba_klgemm_kernel(
             z += e;
             sy = __builtin_fmaf(e, y, sy);
           }
-        z += __shfl_xor(z, 32, 64);
-        sy += __shfl_xor(sy, 32, 64);
+        z = pair_sum32(z);
+        sy = pair_sum32(sy);
         m_own[tb] = mx;
         sy_own[tb] = sy;
         pz[tb] = z;
@@ -456,7 +470,7 @@ __global__ __launch_bounds__(512, 1) void sba_klgemm_kernel(
 #pragma unroll
         for (int v = 0; v < 16; ++v)
           if (!PARTIAL || ob * 32 + 8 * (v >> 2) + (v & 3) < lim) mq = fmaxf(mq, accQ[ob * 2 + tb][v]);
-      mq = fmaxf(mq, __shfl_xor(mq, 32, 64));
+      mq = pair_max32(mq);
       float zq = 0.0f, se = 0.0f;
       // e^(yh - mq) as 2^(yh log2 e - mq log2 e): one fused multiply-add before v_exp
       const float mq2 = mq * 1.44269504088896341f;
@@ -469,8 +483,8 @@ __global__ __launch_bounds__(512, 1) void sba_klgemm_kernel(
             zq += __builtin_amdgcn_exp2f(__builtin_fmaf(yh, 1.44269504088896341f, -mq2));
           se = __builtin_fmaf(accY[ob * 2 + tb][v], yh, se);
         }
-      zq += __shfl_xor(zq, 32, 64);
-      se += __shfl_xor(se, 32, 64);
+      zq = pair_sum32(zq);
+      se = pair_sum32(se);
       qm[tb] = mq;
       qz[tb] = zq;
       qs[tb] = sy_own[tb] - se;
@@ -518,10 +532,82 @@ __global__ __launch_bounds__(512, 1) void sba_klgemm_kernel(
     __syncthreads();
     if ((st - KM) % SPR == SPR - 1) epilogue(1 + (st - KM) / SPR);
   };
+  // bf16 steady state.  Issued back to back at the top of a stage, the eight
+  // DMA loads of the next stage hold up the wave's issue while the texture
+  // path accepts them; here they go out one after each MFMA of the first K
+  // step instead, so the matrix pipe stays fed meanwhile.  The issue is
+  // branch-free so that it shares one scheduling region with the MFMAs: main
+  // stages select the ragged columns per lane; update stages (g >= KT, one
+  // group per stage) count their (step, sub-stage) rather than divide it out.
+  auto pin_first_k_step = [&]() __attribute__((always_inline)) {
+    __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);     // LDS fragment reads of K step 0
+    for (int j = 0; j < 8; ++j) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
+      __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);   // one DMA load of the next stage
+    }
+    for (int j = 0; j < 3; ++j) {
+      __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+    }
+  };
+  auto issue_main_pinned = [&](int st, unsigned char *buf) __attribute__((always_inline)) {
+    unsigned char *dst = buf + lds_row0 * SBP;
+    const int c0 = st * KT;
+    const uint32_t so = __builtin_amdgcn_readfirstlane(mainBase + (uint32_t)(c0 * ESZ));
+    const bool full = c0 + KT <= m;
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      const int sl = (lane & 7) ^ (((lds_row0 + 8 * q + (lane >> 3)) >> 1) & 7);
+      const uint32_t off = (full || c0 + sl * EPP < m) ? voff[q] : OOB;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rMain, (lds_void_t *)(dst + q * 8 * SBP), 16, (int)off, (int)so, 0, 0);
+    }
+  };
+  auto main_stage_pinned = [&](int st, const unsigned char *cur, unsigned char *nxt) __attribute__((always_inline)) {
+    issue_main_pinned(st + 1, nxt);
+    compute_main(cur);
+    pin_first_k_step();
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+  };
+  int cr = 1, csub = 0;   // (step, sub-stage) of the current update stage
+  auto update_stage_pinned = [&](const unsigned char *cur, unsigned char *nxt) __attribute__((always_inline)) {
+    int nr = cr, nsub = csub + 1;
+    if (nsub == SPR) {
+      nsub = 0;
+      ++nr;
+    }
+    {
+      unsigned char *dst = nxt + lds_row0 * SBP;
+      const int c0 = nsub * KT;
+      const int gu = s_order[nr - 1], gd = s_order[k - nr];
+      const uint32_t vup = kind == 0 ? 2u * vstride : (kind == 1 ? vstride : 0u);
+      const uint32_t vdn = kind == 1 ? vstride : 0u;
+      const uint32_t so = __builtin_amdgcn_readfirstlane(c0 < g ? vup + (uint32_t)((gu * g + c0) * ESZ)
+                                                                : vdn + (uint32_t)((gd * g + c0 - g) * ESZ));
+#pragma unroll
+      for (int q = 0; q < 8; ++q)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rUpd, (lds_void_t *)(dst + q * 8 * SBP), 16, (int)voff[q], (int)so,
+                                                 0, 0);
+    }
+    compute_update(cur);
+    pin_first_k_step();
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (csub == SPR - 1) epilogue(cr);
+    cr = nr;
+    csub = nsub;
+  };
+
   issue(0, lds0);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   int st = 0;
+  if (BF16) {
+    for (; st + 2 < KM; st += 2) {
+      main_stage_pinned(st, lds0, lds1);
+      main_stage_pinned(st + 1, lds1, lds0);
+    }
+  }
   for (; st + 1 < KM; st += 2) {
     main_stage(st, lds0, lds1);
     main_stage(st + 1, lds1, lds0);
@@ -534,6 +620,14 @@ __global__ __launch_bounds__(512, 1) void sba_klgemm_kernel(
   if (st < total && (st & 1)) {
     update_stage(st, lds1, lds0);
     ++st;
+  }
+  if (BF16 && g >= KT && st < total) {
+    cr = 1 + (st - KM) / SPR;
+    csub = (st - KM) % SPR;
+    for (; st + 2 < total; st += 2) {
+      update_stage_pinned(lds0, lds1);
+      update_stage_pinned(lds1, lds0);
+    }
   }
   for (; st + 1 < total; st += 2) {
     update_stage(st, lds0, lds1);
