@@ -43,8 +43,11 @@ __global__ __launch_bounds__(256, 2) void hessian_gram_kernel(const void *__rest
   constexpr int NPIECE = BF16 ? 1 : 2;  // 16-byte pieces per loader row (8 columns)
   __shared__ __attribute__((aligned(16))) unsigned char lds[2][2][HT * HPITCH];
 
-  // workgroup id -> (lower tile, token split), tiles varying fastest
-  const int tile = (int)(blockIdx.x % (unsigned)ntiles), split = (int)(blockIdx.x / (unsigned)ntiles);
+  // workgroup (x, y) = (lower tile, token split), tiles varying fastest.  Both
+  // come from the grid rather than from a division of one id: a quotient made
+  // on the vector unit stays in a vector register, and a buffer descriptor
+  // built from it (the token range below) would need a waterfall loop per load.
+  const int tile = (int)blockIdx.x, split = (int)blockIdx.y;
   int bi, bj;
   tri_decode(tile, bi, bj);
   const int64_t tbeg = (int64_t)split * tok_per_split;
@@ -206,8 +209,11 @@ __global__ __launch_bounds__(512, 1) void hessian_gram_tr_kernel(const uint16_t 
                                                                  float *__restrict__ part) {
   __shared__ __attribute__((aligned(16))) unsigned char lds0[2 * HOP2];
   __shared__ __attribute__((aligned(16))) unsigned char lds1[2 * HOP2];
-  // workgroup id -> (lower tile, token split), tiles varying fastest
-  const int tile = (int)(blockIdx.x % (unsigned)ntiles), split = (int)(blockIdx.x / (unsigned)ntiles);
+  // workgroup (x, y) = (lower tile, token split), tiles varying fastest.  Both
+  // come from the grid rather than from a division of one id: a quotient made
+  // on the vector unit stays in a vector register, and a buffer descriptor
+  // built from it (the token range below) would need a waterfall loop per load.
+  const int tile = (int)blockIdx.x, split = (int)blockIdx.y;
   int bi, bj;
   tri_decode(tile, bi, bj);
   const int64_t tbeg = (int64_t)split * tok_per_split;
@@ -285,11 +291,33 @@ __global__ __launch_bounds__(512, 1) void hessian_gram_tr_kernel(const uint16_t 
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
   };
+  // Steady state: the next stage's eight DMA loads go out one after each MFMA
+  // of the first K step rather than back to back ahead of it, so the matrix
+  // pipe stays fed while the texture path accepts them.
+  auto stage_pinned = [&](int64_t t0, const unsigned char *cur, unsigned char *nxt) __attribute__((always_inline)) {
+    issue(t0 + HK2, nxt);
+    compute(cur);
+    __builtin_amdgcn_sched_group_barrier(0x100, 12, 0);     // fragment reads of K step 0
+    for (int j = 0; j < 8; ++j) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
+      __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);   // one DMA load of the next stage
+    }
+    for (int j = 0; j < 3; ++j) {
+      __builtin_amdgcn_sched_group_barrier(0x100, 12, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+    }
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+  };
   if (tbeg < tend) {
     issue(tbeg, lds0);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     int64_t t0 = tbeg;
+    for (; t0 + 2 * HK2 < tend; t0 += 2 * HK2) {
+      stage_pinned(t0, lds0, lds1);
+      stage_pinned(t0 + HK2, lds1, lds0);
+    }
     for (; t0 + HK2 < tend; t0 += 2 * HK2) {
       stage(t0, lds0, lds1);
       stage(t0 + HK2, lds1, lds0);
@@ -400,7 +428,8 @@ hipError_t launch_hessian(const void *X, bool bf16, int64_t t, int64_t m, float 
   const unsigned grid = (unsigned)(p.ntiles * p.nsplit);
   timer_begin(K_HESSIAN, st);
   if (p.tr) {
-    hessian_gram_tr_kernel<<<grid, 512, 0, st>>>((const uint16_t *)X, t, m, p.tok_per_split, p.ntiles, part);
+    hessian_gram_tr_kernel<<<dim3(p.ntiles, p.nsplit), 512, 0, st>>>((const uint16_t *)X, t, m, p.tok_per_split,
+                                                                   p.ntiles, part);
   } else {
     const bool aligned = bf16 ? (m % 8 == 0) : (m % 4 == 0);
     if (bf16)
