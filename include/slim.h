@@ -253,7 +253,11 @@ int slim_pack(const uint8_t *codes, int64_t n, int64_t m, int group, const int8_
  * zero are the float32 [n, k] outputs of slim_sqc_calibrate.  X: [t, m] in
  * dtype xdt (bfloat16 or float32), t <= SLIM_QLINEAR_MAX_T (decode-sized
  * batches); Y: float32 [t, n].  Accumulation is float32; for a given t the
- * sum over groups runs in a fixed order (bitwise reproducible).  bits must
+ * sum over groups runs in a fixed order (bitwise reproducible).  Up to two
+ * tokens the codes are summed through nibble tables; from three on they are
+ * expanded to bfloat16 integers for the matrix cores (float32 X as three
+ * exact bfloat16 terms), so results for different t agree to float32
+ * rounding, not bit for bit.  bits must
  * hold widths in 1 .. 8 adding up to k * avg_bits, as slim_pack requires;
  * otherwise every output is NaN (checked before any plane is read).  Workspace:
  * slim_qlinear_workspace(t, n, m, g) bytes (partial sums over runs of

@@ -76,12 +76,16 @@ hipError_t launch_pack(const uint8_t *codes, int64_t n, int64_t m, int group, co
 
 // ---- Mixed-precision linear layer on the packed planes ----
 struct QlinearPlan {
-  int k, gpw, nrun;          // groups, groups per workgroup, runs of groups
-  int64_t nrb;               // row blocks of 256
-  size_t lds_bytes;          // group tables per workgroup
+  int k, gpw, nrun;          // groups, groups per workgroup (table) or per wave (MFMA), runs of groups
+  int64_t nrb;               // row blocks of 256 (table kernel)
+  size_t lds_bytes;          // group tables per workgroup (table kernel)
   size_t ws_bytes;           // partial sums [nrun, t, n] f32 when nrun > 1
+  bool mma;                  // t >= 2: codes expanded for the matrix cores (qlinear_mma.hip)
 };
 QlinearPlan qlinear_plan(int t, int64_t n, int64_t m, int group);
+void launch_qlinear_mma(const void *X, bool bf16, int t, int64_t m, const uint32_t *packed, const int8_t *bits,
+                        int N, const float *scale, const float *zero, int64_t n, int group, int k, int gpr, int nrun,
+                        float *out, hipStream_t st);
 hipError_t launch_qlinear(const void *X, bool bf16, int t, int64_t m, const uint32_t *packed, const int8_t *bits,
                           int N, const float *scale, const float *zero, int64_t n, int group, float *Y, void *ws,
                           const QlinearPlan &p, hipStream_t st);

@@ -361,6 +361,19 @@ QlinearPlan qlinear_plan(int t, int64_t n, int64_t m, int group) {
   QlinearPlan p;
   const int qt = ql_qt(t);
   p.k = (int)(m / group);
+  p.mma = t >= 3;   // measured: the tables win up to two tokens, the matrix cores from three
+  if (p.mma) {
+    // 16 rows per wave, 64 per workgroup; runs of groups per wave, halved
+    // (down to 4) until about 2048 workgroups are in flight
+    p.nrb = (n + 63) / 64;
+    int gpr = std::min(p.k, 8);   // X of a run in LDS: at most 8 groups
+    while (gpr > 2 && p.nrb * ((p.k + gpr - 1) / gpr) < 2048) gpr = (gpr + 1) / 2;
+    p.gpw = gpr;
+    p.nrun = (p.k + gpr - 1) / gpr;
+    p.lds_bytes = 0;
+    p.ws_bytes = p.nrun > 1 ? align_up((size_t)p.nrun * t * n * sizeof(float), 256) : 256;
+    return p;
+  }
   p.nrb = (n + 255) / 256;
   // groups per workgroup: at most QL_RUN, tables within 64 KiB, and enough
   // workgroups to keep a few per CU
@@ -389,6 +402,16 @@ hipError_t launch_qlinear(const void *X, bool bf16, int t, int64_t m, const uint
                           int N, const float *scale, const float *zero, int64_t n, int group, float *Y, void *ws,
                           const QlinearPlan &p, hipStream_t st) {
   float *out = p.nrun > 1 ? (float *)ws : Y;
+  if (p.mma) {
+    timer_begin(K_QLINEAR, st);
+    launch_qlinear_mma(X, bf16, t, m, packed, bits, N, scale, zero, n, group, p.k, p.gpw, p.nrun, out, st);
+    if (p.nrun > 1) {
+      const int64_t e = (int64_t)t * n;
+      qlinear_reduce_kernel<<<(unsigned)((e + 255) / 256), 256, 0, st>>>((const float *)ws, p.nrun, t, n, Y);
+    }
+    timer_end(K_QLINEAR, st);
+    return hipGetLastError();
+  }
   dim3 grid((unsigned)p.nrb, (unsigned)p.nrun);
   // four groups per scale / zero load: runs start at multiples of 4 groups and
   // both arrays are 16-byte aligned
