@@ -14,13 +14,13 @@
 // R_i -= L_ip Z_p.  Since H_d^-1 = Z^T Z, d_j is the squared norm of column j of
 // Z, accumulated panel by panel in a fixed order.  Per panel p:
 //   chol_panel  L_ip = A_ip L_pp^-T for the rows below; Z_p = L_pp^-1 R_p and d += col-norms^2
-//   chol_trail  (part 1) block column p+1 of A and row block p+1 of Z
-//   chol_diag   factor and invert diagonal block p+1, on a side stream ...
-//   chol_trail  (part 2) ... while the rest of A_ij -= L_ip L_jp^T and
-//               R_ij -= L_ip Z_pj runs (lookahead: the one-workgroup step does
-//               not wait for the bulk update, nor the bulk for it)
+//   chol_trail       (part 1) block column p+1 of A and row block p+1 of Z
+//   chol_trail_diag  (part 2) the rest of A_ij -= L_ip L_jp^T and
+//                    R_ij -= L_ip Z_pj, with diagonal block p+1 factored and
+//                    inverted by workgroup 0 of the same launch (lookahead:
+//                    the one-workgroup step does not wait for the bulk update,
+//                    nor the bulk for it, and no cross-stream wait is needed)
 // The GEMM-shaped work uses v_mfma_f64_16x16x4_f64 on 64x64 tiles.
-#include <mutex>
 
 #include "common.hpp"
 #include "f64tile.hpp"
@@ -348,13 +348,7 @@ __device__ __forceinline__ void trail_tile(double *__restrict__ A, double *__res
 //                      p+2 .. NB-1 (column blocks 0 .. p).
 // Diagonal block p+1 is factored by its own launch between the two parts
 // (its inputs are final once part 1 has run).
-__global__ __launch_bounds__(256) void chol_trail_kernel(double *__restrict__ A, double *__restrict__ Z,
-                                                         double *__restrict__ TinvT, int32_t *__restrict__ info,
-                                                         int64_t mp, int p, int NB, int next) {
-  const int64_t w = blockIdx.x;
-  const int64_t k0 = (int64_t)p * NBK;
-  int ii, jj;
-  bool zt;
+__device__ __forceinline__ void trail_coords(int64_t w, int p, int NB, int next, int &ii, int &jj, bool &zt) {
   if (next) {
     const int nA = NB - p - 1;
     if (w < nA) {
@@ -384,7 +378,34 @@ __global__ __launch_bounds__(256) void chol_trail_kernel(double *__restrict__ A,
       zt = true;
     }
   }
-  trail_tile(A, Z, mp, k0, (int64_t)ii * NBK, (int64_t)jj * NBK, zt);
+}
+
+__global__ __launch_bounds__(256) void chol_trail_kernel(double *__restrict__ A, double *__restrict__ Z,
+                                                         double *__restrict__ TinvT, int32_t *__restrict__ info,
+                                                         int64_t mp, int p, int NB, int next) {
+  int ii, jj;
+  bool zt;
+  trail_coords(blockIdx.x, p, NB, next, ii, jj, zt);
+  trail_tile(A, Z, mp, (int64_t)p * NBK, (int64_t)ii * NBK, (int64_t)jj * NBK, zt);
+}
+
+// Part 2 of panel p's trailing update with diagonal block p+1 factored
+// beside it, in one launch: workgroup 0 factors the block (its inputs are
+// final once part 1 has run; no part-2 tile reads it or TinvT), the others
+// take the part-2 tiles.  The next panel then follows on the same stream
+// with no cross-stream wait.
+__global__ __launch_bounds__(256) void chol_trail_diag_kernel(double *__restrict__ A, double *__restrict__ Z,
+                                                              double *__restrict__ TinvT,
+                                                              int32_t *__restrict__ info, int64_t mp, int p,
+                                                              int NB) {
+  if (blockIdx.x == 0) {
+    chol_diag_body<256>(A, mp, p + 1, TinvT, info);
+    return;
+  }
+  int ii, jj;
+  bool zt;
+  trail_coords((int64_t)blockIdx.x - 1, p, NB, 0, ii, jj, zt);
+  trail_tile(A, Z, mp, (int64_t)p * NBK, (int64_t)ii * NBK, (int64_t)jj * NBK, zt);
 }
 
 __global__ __launch_bounds__(256) void sal_hinv_out_kernel(const double *__restrict__ d, int64_t m,
@@ -455,22 +476,6 @@ size_t salience_ws_bytes(int64_t n, int64_t m, int group) {
   return off;
 }
 
-// One side stream per device (default priority, non-blocking), created on
-// first use and kept for the life of the process; null if it cannot be made.
-static hipStream_t side_stream() {
-  static std::mutex mu;
-  static hipStream_t streams[64] = {};
-  static bool tried[64] = {};
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return nullptr;
-  std::lock_guard<std::mutex> lk(mu);
-  if (!tried[dev]) {
-    tried[dev] = true;
-    if (hipStreamCreateWithFlags(&streams[dev], hipStreamNonBlocking) != hipSuccess) streams[dev] = nullptr;
-  }
-  return streams[dev];
-}
-
 hipError_t launch_chol_inverse(const float *H, int64_t m, double damp, bool reverse, double *A, double *Z,
                                double *TinvT, double *d, double *alpha, int32_t *info, hipStream_t st) {
   const int64_t mp = pad64(m);
@@ -480,49 +485,23 @@ hipError_t launch_chol_inverse(const float *H, int64_t m, double damp, bool reve
     if (blocks > 65536) blocks = 65536;
     sal_init_kernel<<<(unsigned)blocks, 256, 0, st>>>(H, m, mp, alpha, A, Z, d, info, reverse ? 1 : 0);
   }
-  // Lookahead: once the block column after panel p is updated (part 1), the
-  // next diagonal block is factored on a side stream while the rest of the
-  // trailing update (part 2) runs; the next panel waits for both.  The two
-  // touch disjoint data: part 2 the tiles with row >= column >= p + 2 and Z's
-  // later row blocks, the diagonal step block (p + 1, p + 1) and TinvT.
-  // Without a side stream the step runs in order between the two parts.
+  // Per panel: the panel solve, part 1 of the trailing update (the next
+  // block column, whose diagonal block is then final), then part 2 with the
+  // next diagonal block factored beside it in the same launch.
   const int NB = (int)(mp / NBK);
-  hipStream_t side = side_stream();
-  hipEvent_t evA = nullptr, evB = nullptr;
-  if (side && (hipEventCreateWithFlags(&evA, hipEventDisableTiming) != hipSuccess ||
-               hipEventCreateWithFlags(&evB, hipEventDisableTiming) != hipSuccess)) {
-    if (evA) (void)hipEventDestroy(evA);
-    evA = nullptr;
-    side = nullptr;
-  }
   chol_diag_kernel<<<1, 512, 0, st>>>(A, mp, 0, TinvT, info);
-  hipError_t err = hipSuccess;
-  for (int p = 0; p < NB && err == hipSuccess; ++p) {
+  for (int p = 0; p < NB; ++p) {
     const int nrow = NB - p - 1;
     chol_panel_kernel<<<nrow + p + 1, 256, 0, st>>>(A, Z, TinvT, d, mp, p, nrow);
     if (nrow > 0) {
       chol_trail_kernel<<<(unsigned)(nrow + p + 1), 256, 0, st>>>(A, Z, TinvT, info, mp, p, NB, 1);
-      if (side) {
-        err = hipEventRecord(evA, st);
-        if (err == hipSuccess) err = hipStreamWaitEvent(side, evA, 0);
-        chol_diag_kernel<<<1, 512, 0, side>>>(A, mp, p + 1, TinvT, info);
-        if (err == hipSuccess) err = hipEventRecord(evB, side);
-      } else {
-        chol_diag_kernel<<<1, 512, 0, st>>>(A, mp, p + 1, TinvT, info);
-      }
       const int64_t n2 = nrow - 1;
       const int64_t rest = n2 * (n2 + 1) / 2 + n2 * (p + 1);
-      if (rest > 0) {
-        timer_begin(K_CHOL_UPDATE, st);
-        chol_trail_kernel<<<(unsigned)rest, 256, 0, st>>>(A, Z, TinvT, info, mp, p, NB, 0);
-        timer_end(K_CHOL_UPDATE, st);
-      }
-      if (side && err == hipSuccess) err = hipStreamWaitEvent(st, evB, 0);
+      timer_begin(K_CHOL_UPDATE, st);
+      chol_trail_diag_kernel<<<(unsigned)(1 + rest), 256, 0, st>>>(A, Z, TinvT, info, mp, p, NB);
+      timer_end(K_CHOL_UPDATE, st);
     }
   }
-  if (evA) (void)hipEventDestroy(evA);
-  if (evB) (void)hipEventDestroy(evB);
-  if (err != hipSuccess) return err;
   return hipGetLastError();
 }
 
