@@ -89,7 +89,10 @@ def run_step(slim, X, W, group, N, ev=None, variant=None, gptq=False):
     mark(0)
     H = slim.hessian(X)
     mark(1)
-    hinv, gsal, info, _ = slim.salience(H, W, group, 0.01)
+    if gptq:   # the salience sweep also yields the factor GPTQ reads
+        hinv, gsal, info, _, U = slim.salience(H, W, group, 0.01, want_u=True)
+    else:
+        hinv, gsal, info, _ = slim.salience(H, W, group, 0.01)
     mark(2)
     if variant is None:
         bits, kl, rs = slim.sba_search(X, W, gsal, group, N)
@@ -99,7 +102,7 @@ def run_step(slim, X, W, group, N, ev=None, variant=None, gptq=False):
                                           order=order, objective=objective)
     mark(3)
     if gptq:   # the quantizer inside GPTQ's error-compensating sweep
-        sq = slim.gptq_quantize(H, W, bits, hinv, group, 0.01, 0.1, 50, want_tau=False)
+        sq = slim.gptq_quantize(None, W, bits, hinv, group, 0.01, 0.1, 50, want_tau=False, U=U)
     else:
         sq = slim.sqc_calibrate(W, bits, hinv, group, 0.1, 50, want_tau=False)
     mark(4)

@@ -9,10 +9,12 @@
  *
  *   slim_hessian        H = 2 X^T X                         (component one, Hessian from calibration)
  *   slim_salience       d = diag((H + a I)^-1), delta = w^2 / d^2, group means   (component one)
+ *   slim_salience_u     the same, also writing the upper Cholesky factor of (H + a I)^-1
  *   slim_sba_search     balanced bit allocation scored by output KL           (component one)
  *   slim_sba_search_ex  the same with an output-MSE objective or a given group order (ablations)
  *   slim_sqc_calibrate  3-sigma mask + tau-grid search of scale and zero       (component two)
  *   slim_gptq_quantize  the same quantizer inside GPTQ's error-compensating sweep  (core design: GPTQ backbone)
+ *   slim_gptq_quantize_u  the same with that factor given (no second factorisation)
  *   slim_pack           group-structured bit-planes, no bitmap                (FAQ: storage)
  *   slim_qlinear        Y = X W_hat^T read from the planes (decode batches)    (FAQ: deployment)
  *
@@ -115,6 +117,19 @@ size_t slim_salience_workspace(int64_t n, int64_t m, int group);
 int slim_salience(const float *H, int64_t m, double damp_frac, const void *W, int wdt, int64_t n,
                   int group, float *hinv_diag, double *group_sal, float *elem_sal, int32_t *info,
                   void *ws, size_t ws_bytes, void *stream);
+
+/* slim_salience, and also the upper Cholesky factor U of H_d^-1 (H_d^-1 =
+ * U^T U): U float64 [m, m], row-major, zeros below the diagonal, 16-byte
+ * aligned.  This is the factor GPTQ's sweep reads (core design: the GPTQ
+ * backbone), so slim_gptq_quantize_u can take it instead of factoring H
+ * again.  The sweep runs on the index-reversed matrix (its inverse factor,
+ * read backwards, is U); hinv_diag, group_sal and elem_sal are the same
+ * quantities as slim_salience's, with float64 rounding in another order.
+ * U is meaningful only when *info ends 0.  Same workspace as slim_salience.
+ */
+int slim_salience_u(const float *H, int64_t m, double damp_frac, const void *W, int wdt, int64_t n,
+                    int group, float *hinv_diag, double *group_sal, float *elem_sal, double *U,
+                    int32_t *info, void *ws, size_t ws_bytes, void *stream);
 
 /* ------------------------------------------------------------------------
  * SBA search (component one: bit-widths minimise the KL divergence of the
@@ -224,6 +239,16 @@ int slim_gptq_quantize(const float *H, int64_t m, double damp_frac, const void *
                        const int8_t *bits, const float *hinv_diag, double lambda, int n_tau, float *scale,
                        float *zero, uint8_t *codes, uint32_t *mask, uint8_t *tau_idx, int32_t *info, void *ws,
                        size_t ws_bytes, void *stream);
+
+/* slim_gptq_quantize with the factor given: U float64 [m, m] as
+ * slim_salience_u writes it (16-byte aligned; read only).  H and damp_frac
+ * are not needed; *info is set to 0, or -1 for a non-finite W.  Same
+ * workspace and outputs as slim_gptq_quantize, which, given the same H, forms
+ * the same U itself. */
+int slim_gptq_quantize_u(const double *U, int64_t m, const void *W, int wdt, int64_t n, int group,
+                         const int8_t *bits, const float *hinv_diag, double lambda, int n_tau, float *scale,
+                         float *zero, uint8_t *codes, uint32_t *mask, uint8_t *tau_idx, int32_t *info, void *ws,
+                         size_t ws_bytes, void *stream);
 
 /* ------------------------------------------------------------------------
  * Packing (FAQ on storage: group-wise bit-widths need no bitmap or codebook

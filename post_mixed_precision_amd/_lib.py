@@ -30,6 +30,8 @@ _SIGS = {
     "slim_salience_workspace": (_c_sz, [_c_i64, _c_i64, _c_int]),
     "slim_salience": (_c_int, [_c_vp, _c_i64, _c_dbl, _c_vp, _c_int, _c_i64, _c_int, _c_vp, _c_vp, _c_vp,
                                _c_vp, _c_vp, _c_sz, _c_vp]),
+    "slim_salience_u": (_c_int, [_c_vp, _c_i64, _c_dbl, _c_vp, _c_int, _c_i64, _c_int, _c_vp, _c_vp, _c_vp,
+                                 _c_vp, _c_vp, _c_vp, _c_sz, _c_vp]),
     "slim_sba_workspace": (_c_sz, [_c_i64, _c_i64, _c_i64, _c_int, _c_int]),
     "slim_sba_search": (_c_int, [_c_vp, _c_int, _c_i64, _c_vp, _c_int, _c_i64, _c_i64, _c_int, _c_vp, _c_int,
                                  _c_vp, _c_vp, _c_vp, _c_vp, _c_sz, _c_vp]),
@@ -40,6 +42,8 @@ _SIGS = {
     "slim_gptq_workspace": (_c_sz, [_c_i64, _c_i64, _c_int]),
     "slim_gptq_quantize": (_c_int, [_c_vp, _c_i64, _c_dbl, _c_vp, _c_int, _c_i64, _c_int, _c_vp, _c_vp, _c_dbl,
                                     _c_int, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_sz, _c_vp]),
+    "slim_gptq_quantize_u": (_c_int, [_c_vp, _c_i64, _c_vp, _c_int, _c_i64, _c_int, _c_vp, _c_vp, _c_dbl, _c_int,
+                                      _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_sz, _c_vp]),
     "slim_tau_table": (_c_int, [_c_dbl, _c_int, _c_vp]),
     "slim_pack_words": (_c_i64, [_c_i64, _c_i64, _c_int]),
     "slim_pack": (_c_int, [_c_vp, _c_i64, _c_i64, _c_int, _c_vp, _c_int, _c_vp, _c_vp, _c_vp]),
@@ -156,8 +160,9 @@ def hessian(X, H=None, accumulate: bool = False):
     return H
 
 
-def salience(H, W, group: int, damp_frac: float = 0.01, elem: bool = False):
-    """-> (hinv_diag f32 [m], group_sal f64 [k], info i32 [1], elem_sal f32 [n, m] or None)."""
+def salience(H, W, group: int, damp_frac: float = 0.01, elem: bool = False, want_u: bool = False):
+    """-> (hinv_diag f32 [m], group_sal f64 [k], info i32 [1], elem_sal f32 [n, m] or None), and with
+    want_u the upper Cholesky factor U f64 [m, m] of H_d^-1 appended (slim_salience_u)."""
     torch = _torch()
     lib = load_library()
     H, W = _dev(H), _dev(W)
@@ -168,6 +173,12 @@ def salience(H, W, group: int, damp_frac: float = 0.01, elem: bool = False):
     info = torch.zeros(1, dtype=torch.int32, device=W.device)
     esal = torch.empty((n, m), dtype=torch.float32, device=W.device) if elem else None
     ws = _ws(lib.slim_salience_workspace(n, m, group), W.device)
+    if want_u:
+        U = torch.empty((m, m), dtype=torch.float64, device=W.device)
+        check(lib.slim_salience_u(_ptr(H), m, float(damp_frac), _ptr(W), _dtype_code(W), n, group, _ptr(hinv),
+                                  _ptr(gsal), _ptr(esal), _ptr(U), _ptr(info), _ptr(ws), ws.numel(),
+                                  _stream(W.device)), "slim_salience_u")
+        return hinv, gsal, info, esal, U
     check(lib.slim_salience(_ptr(H), m, float(damp_frac), _ptr(W), _dtype_code(W), n, group, _ptr(hinv), _ptr(gsal),
                             _ptr(esal), _ptr(info), _ptr(ws), ws.numel(), _stream(W.device)), "slim_salience")
     return hinv, gsal, info, esal
@@ -243,12 +254,14 @@ def sqc_calibrate(W, bits, hinv, group: int, lam: float = 0.1, n_tau: int = 50, 
 
 
 def gptq_quantize(H, W, bits, hinv, group: int, damp_frac: float = 0.01, lam: float = 0.1, n_tau: int = 50,
-                  want_tau: bool = True):
+                  want_tau: bool = True, U=None):
     """GPTQ sweep with the group quantizer -> dict(scale, zero [n, k] f32; codes [n, m] u8;
-    mask [n, m/32] i32 bits; tau_idx [n, k] u8; info i32 [1])."""
+    mask [n, m/32] i32 bits; tau_idx [n, k] u8; info i32 [1]).  With U (the factor
+    salience(..., want_u=True) returns) H may be None and is not factored again
+    (slim_gptq_quantize_u)."""
     torch = _torch()
     lib = load_library()
-    H, W, bits, hinv = _dev(H), _dev(W), _dev(bits), _dev(hinv)
+    W, bits, hinv = _dev(W), _dev(bits), _dev(hinv)
     n, m = W.shape
     k = m // group
     dev = W.device
@@ -261,6 +274,14 @@ def gptq_quantize(H, W, bits, hinv, group: int, damp_frac: float = 0.01, lam: fl
         "info": torch.zeros(1, dtype=torch.int32, device=dev),
     }
     ws = _ws(lib.slim_gptq_workspace(n, m, group), dev)
+    if U is not None:
+        U = _dev(U)
+        check(lib.slim_gptq_quantize_u(_ptr(U), m, _ptr(W), _dtype_code(W), n, group, _ptr(bits), _ptr(hinv),
+                                       float(lam), int(n_tau), _ptr(out["scale"]), _ptr(out["zero"]),
+                                       _ptr(out["codes"]), _ptr(out["mask"]), _ptr(out["tau_idx"]),
+                                       _ptr(out["info"]), _ptr(ws), ws.numel(), _stream(dev)), "slim_gptq_quantize_u")
+        return out
+    H = _dev(H)
     check(lib.slim_gptq_quantize(_ptr(H), m, float(damp_frac), _ptr(W), _dtype_code(W), n, group, _ptr(bits),
                                  _ptr(hinv), float(lam), int(n_tau), _ptr(out["scale"]), _ptr(out["zero"]),
                                  _ptr(out["codes"]), _ptr(out["mask"]), _ptr(out["tau_idx"]), _ptr(out["info"]),

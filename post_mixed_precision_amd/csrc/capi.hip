@@ -139,7 +139,24 @@ int slim_salience(const float *H, int64_t m, double damp_frac, const void *W, in
   if (!ws || ws_bytes < need) return SLIM_E_WORKSPACE;
   if (!aligned16(ws)) return SLIM_E_ALIGN;
   hipError_t e = slim::launch_salience(H, m, damp_frac, W, wdt == SLIM_BF16, n, group, hinv_diag, group_sal, elem_sal,
-                                       info, ws, (hipStream_t)stream);
+                                       nullptr, info, ws, (hipStream_t)stream);
+  return e == hipSuccess ? SLIM_OK : hip_fail(e);
+}
+
+int slim_salience_u(const float *H, int64_t m, double damp_frac, const void *W, int wdt, int64_t n, int group,
+                    float *hinv_diag, double *group_sal, float *elem_sal, double *U, int32_t *info, void *ws,
+                    size_t ws_bytes, void *stream) {
+  if (!H || !W || !hinv_diag || !group_sal || !U || !info) return SLIM_E_NULL;
+  if (!valid_dtype(wdt)) return SLIM_E_DTYPE;
+  if (n < 1 || m < 1 || m > SLIM_MAX_WIDTH) return SLIM_E_SHAPE;
+  if (!valid_group(group) || m % group) return SLIM_E_SHAPE;
+  if (!(damp_frac >= 0.0) || !isfinite(damp_frac)) return SLIM_E_PARAM;
+  if (!aligned16(H) || !aligned16(W) || !aligned16(hinv_diag) || !aligned16(U)) return SLIM_E_ALIGN;
+  const size_t need = slim::salience_ws_bytes(n, m, group);
+  if (!ws || ws_bytes < need) return SLIM_E_WORKSPACE;
+  if (!aligned16(ws)) return SLIM_E_ALIGN;
+  hipError_t e = slim::launch_salience(H, m, damp_frac, W, wdt == SLIM_BF16, n, group, hinv_diag, group_sal, elem_sal,
+                                       U, info, ws, (hipStream_t)stream);
   return e == hipSuccess ? SLIM_OK : hip_fail(e);
 }
 
@@ -224,8 +241,25 @@ int slim_gptq_quantize(const float *H, int64_t m, double damp_frac, const void *
   if (!aligned16(ws)) return SLIM_E_ALIGN;
   slim::TauTable tt;
   slim::make_tau_table(lambda, n_tau, tt);
-  hipError_t e = slim::launch_gptq(H, m, damp_frac, W, wdt == SLIM_BF16, n, group, bits, hinv_diag, tt, n_tau, scale,
-                                   zero, codes, mask, tau_idx, info, ws, (hipStream_t)stream);
+  hipError_t e = slim::launch_gptq(H, nullptr, m, damp_frac, W, wdt == SLIM_BF16, n, group, bits, hinv_diag, tt, n_tau,
+                                   scale, zero, codes, mask, tau_idx, info, ws, (hipStream_t)stream);
+  return e == hipSuccess ? SLIM_OK : hip_fail(e);
+}
+
+int slim_gptq_quantize_u(const double *U, int64_t m, const void *W, int wdt, int64_t n, int group, const int8_t *bits,
+                         const float *hinv_diag, double lambda, int n_tau, float *scale, float *zero, uint8_t *codes,
+                         uint32_t *mask, uint8_t *tau_idx, int32_t *info, void *ws, size_t ws_bytes, void *stream) {
+  if (!valid_dtype(wdt)) return SLIM_E_DTYPE;
+  if (n < 1 || m < 1 || m > SLIM_MAX_WIDTH || !valid_group(group) || m % group) return SLIM_E_SHAPE;
+  if (n_tau < 1 || n_tau > 255 || !(lambda >= 0.0 && lambda < 1.0)) return SLIM_E_PARAM;
+  if (!U || !W || !bits || !hinv_diag || !scale || !zero || !codes || !mask || !info) return SLIM_E_NULL;
+  if (!aligned16(U) || !aligned16(W) || !aligned16(hinv_diag) || !aligned16(codes)) return SLIM_E_ALIGN;
+  if (!ws || ws_bytes < slim::gptq_ws_bytes(n, m, group)) return SLIM_E_WORKSPACE;
+  if (!aligned16(ws)) return SLIM_E_ALIGN;
+  slim::TauTable tt;
+  slim::make_tau_table(lambda, n_tau, tt);
+  hipError_t e = slim::launch_gptq(nullptr, U, m, 0.0, W, wdt == SLIM_BF16, n, group, bits, hinv_diag, tt, n_tau,
+                                   scale, zero, codes, mask, tau_idx, info, ws, (hipStream_t)stream);
   return e == hipSuccess ? SLIM_OK : hip_fail(e);
 }
 

@@ -50,6 +50,18 @@ __global__ __launch_bounds__(256) void gptq_u_kernel(const double *__restrict__ 
   }
 }
 
+// Ut = U^T for a factor the caller supplies; info starts at 0 (a fill
+// kernel rather than a memset, so the call stays capturable).
+__global__ __launch_bounds__(256) void gptq_ut_kernel(const double *__restrict__ U, int64_t m,
+                                                      double *__restrict__ Ut, int32_t *__restrict__ info) {
+  const int64_t total = m * m;
+  if (blockIdx.x == 0 && threadIdx.x == 0) *info = 0;
+  for (int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x; idx < total; idx += (int64_t)gridDim.x * 256) {
+    const int64_t r = idx / m, c = idx % m;
+    Ut[c * m + r] = U[idx];
+  }
+}
+
 // W64 = W, W32 = W (the float32 copy the group calibration reads); a
 // non-finite weight sets info = -1.
 template <bool BF16>
@@ -239,10 +251,10 @@ static void gq_group(double *W64, float *W32, int64_t n, int64_t m, int j, const
   }
 }
 
-hipError_t launch_gptq(const float *H, int64_t m, double damp, const void *W, bool bf16, int64_t n, int group,
-                       const int8_t *bits, const float *hinv, const TauTable &tt, int n_tau, float *scale,
-                       float *zero, uint8_t *codes, uint32_t *mask, uint8_t *tau_idx, int32_t *info, void *ws,
-                       hipStream_t st) {
+hipError_t launch_gptq(const float *H, const double *Ugiven, int64_t m, double damp, const void *W, bool bf16,
+                       int64_t n, int group, const int8_t *bits, const float *hinv, const TauTable &tt, int n_tau,
+                       float *scale, float *zero, uint8_t *codes, uint32_t *mask, uint8_t *tau_idx, int32_t *info,
+                       void *ws, hipStream_t st) {
   const int64_t mp = gq_pad64(m);
   char *base = (char *)ws;
   size_t off = 0;
@@ -264,13 +276,20 @@ hipError_t launch_gptq(const float *H, int64_t m, double damp, const void *W, bo
   off += align_up((size_t)n * m * 4, 256);
   double *Err = (double *)(base + off);
 
-  hipError_t e = launch_chol_inverse(H, m, damp, true, A, Z, TinvT, d, alpha, info, st);
-  if (e != hipSuccess) return e;
-  double *U = A;   // the factor is no longer needed once its inverse is formed
+  hipError_t e = hipSuccess;
+  const double *U = Ugiven;
   {
     int64_t blocks = (m * m + 255) / 256;
     if (blocks > 65536) blocks = 65536;
-    gptq_u_kernel<<<(unsigned)blocks, 256, 0, st>>>(Z, mp, m, U, Ut);
+    if (Ugiven) {
+      // the factor of a salience call on the same H (slim_salience_u)
+      gptq_ut_kernel<<<(unsigned)blocks, 256, 0, st>>>(Ugiven, m, Ut, info);
+    } else {
+      e = launch_chol_inverse(H, m, damp, true, A, Z, TinvT, d, alpha, info, st);
+      if (e != hipSuccess) return e;
+      U = A;   // the factor is no longer needed once its inverse is formed
+      gptq_u_kernel<<<(unsigned)blocks, 256, 0, st>>>(Z, mp, m, A, Ut);
+    }
     blocks = (n * m + 255) / 256;
     if (blocks > 65536) blocks = 65536;
     if (bf16)

@@ -34,9 +34,11 @@ size_t salience_ws_bytes(int64_t n, int64_t m, int group);
 // inverse; mp = m rounded up to 64.
 hipError_t launch_chol_inverse(const float *H, int64_t m, double damp, bool reverse, double *A, double *Z,
                                double *TinvT, double *d, double *alpha, int32_t *info, hipStream_t st);
+// U (nullable, m x m float64): also write the upper factor of H_d^-1 (the
+// sweep then runs on the reversed matrix).
 hipError_t launch_salience(const float *H, int64_t m, double damp, const void *W, bool bf16,
                            int64_t n, int group, float *hinv, double *gsal, float *esal,
-                           int32_t *info, void *ws, hipStream_t st);
+                           double *U, int32_t *info, void *ws, hipStream_t st);
 
 // ---- SBA ----
 struct SbaPlan {
@@ -65,10 +67,12 @@ hipError_t launch_sqc(const void *W, bool bf16, int64_t n, int64_t m, int group,
 
 // ---- GPTQ sweep around the group quantizer ----
 size_t gptq_ws_bytes(int64_t n, int64_t m, int group);
-hipError_t launch_gptq(const float *H, int64_t m, double damp, const void *W, bool bf16, int64_t n, int group,
-                       const int8_t *bits, const float *hinv, const TauTable &tt, int n_tau, float *scale,
-                       float *zero, uint8_t *codes, uint32_t *mask, uint8_t *tau_idx, int32_t *info, void *ws,
-                       hipStream_t st);
+// Ugiven (nullable): the upper factor of H_d^-1 from slim_salience_u; H and
+// damp are then unused.
+hipError_t launch_gptq(const float *H, const double *Ugiven, int64_t m, double damp, const void *W, bool bf16,
+                       int64_t n, int group, const int8_t *bits, const float *hinv, const TauTable &tt, int n_tau,
+                       float *scale, float *zero, uint8_t *codes, uint32_t *mask, uint8_t *tau_idx, int32_t *info,
+                       void *ws, hipStream_t st);
 
 // ---- Pack ----
 hipError_t launch_pack(const uint8_t *codes, int64_t n, int64_t m, int group, const int8_t *bits,

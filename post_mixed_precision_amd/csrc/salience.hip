@@ -408,10 +408,23 @@ __global__ __launch_bounds__(256) void chol_trail_diag_kernel(double *__restrict
   trail_tile(A, Z, mp, (int64_t)p * NBK, (int64_t)ii * NBK, (int64_t)jj * NBK, zt);
 }
 
+// hinv[j] = d_j; after the reversed sweep d holds the diagonal in reverse order.
 __global__ __launch_bounds__(256) void sal_hinv_out_kernel(const double *__restrict__ d, int64_t m,
-                                                           float *__restrict__ hinv) {
+                                                           float *__restrict__ hinv, int reverse) {
   const int64_t j = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (j < m) hinv[j] = (float)d[j];
+  if (j < m) hinv[j] = (float)d[reverse ? m - 1 - j : j];
+}
+
+// U (m x m, upper, zeros below) from the inverse factor Z (mp x mp) of the
+// reversed matrix: J H_d J = Lr Lr^T gives H_d = R R^T with R = J Lr J upper,
+// so U = R^-1 = J Lr^-1 J and H_d^-1 = U^T U.
+__global__ __launch_bounds__(256) void sal_u_out_kernel(const double *__restrict__ Z, int64_t mp, int64_t m,
+                                                        double *__restrict__ U) {
+  const int64_t total = m * m;
+  for (int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x; idx < total; idx += (int64_t)gridDim.x * 256) {
+    const int64_t r = idx / m, c = idx % m;
+    U[idx] = c >= r ? Z[(m - 1 - r) * mp + (m - 1 - c)] : 0.0;
+  }
 }
 
 // delta = fl(w*w)/fl(d*d) (float32); per (row block, group) float64 partial sums.
@@ -506,7 +519,8 @@ hipError_t launch_chol_inverse(const float *H, int64_t m, double damp, bool reve
 }
 
 hipError_t launch_salience(const float *H, int64_t m, double damp, const void *W, bool bf16, int64_t n, int group,
-                           float *hinv, double *gsal, float *esal, int32_t *info, void *ws, hipStream_t st) {
+                           float *hinv, double *gsal, float *esal, double *U, int32_t *info, void *ws,
+                           hipStream_t st) {
   const int64_t mp = pad64(m);
   const int64_t nrb = (n + 63) / 64;
   const int k = (int)(m / group);
@@ -524,11 +538,19 @@ hipError_t launch_salience(const float *H, int64_t m, double damp, const void *W
   off += 256;
   double *part = (double *)(base + off);
 
-  hipError_t e0 = launch_chol_inverse(H, m, damp, false, A, Z, TinvT, d, alpha, info, st);
+  // With U requested the sweep runs on the reversed matrix, whose inverse
+  // factor is U read backwards; d is then the diagonal in reverse order.
+  const bool rev = U != nullptr;
+  hipError_t e0 = launch_chol_inverse(H, m, damp, rev, A, Z, TinvT, d, alpha, info, st);
   if (e0 != hipSuccess) return e0;
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  sal_hinv_out_kernel<<<(unsigned)((m + 255) / 256), 256, 0, st>>>(d, m, hinv);
+  if (rev) {
+    int64_t blocks = (m * m + 255) / 256;
+    if (blocks > 65536) blocks = 65536;
+    sal_u_out_kernel<<<(unsigned)blocks, 256, 0, st>>>(Z, mp, m, U);
+  }
+  sal_hinv_out_kernel<<<(unsigned)((m + 255) / 256), 256, 0, st>>>(d, m, hinv, rev ? 1 : 0);
   dim3 grid(k, (unsigned)nrb);
   if (bf16)
     sal_group_partial_kernel<true><<<grid, 256, 0, st>>>(W, n, m, group, hinv, esal, part, info);

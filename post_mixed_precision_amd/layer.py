@@ -19,10 +19,13 @@ def quantize_layer(X, W, group: int = 128, avg_bits: int = 2, lam: float = 0.1, 
     independently."""
     if H is None:
         H = _lib.hessian(X)
-    hinv, gsal, info, _ = _lib.salience(H, W, group, damp_frac)
+    if gptq:   # the salience sweep also yields the factor GPTQ reads
+        hinv, gsal, info, _, U = _lib.salience(H, W, group, damp_frac, want_u=True)
+    else:
+        hinv, gsal, info, _ = _lib.salience(H, W, group, damp_frac)
     bits, kl, r_star = _lib.sba_search(X, W, gsal, group, avg_bits)
     if gptq:
-        sq = _lib.gptq_quantize(H, W, bits, hinv, group, damp_frac, lam, n_tau)
+        sq = _lib.gptq_quantize(None, W, bits, hinv, group, damp_frac, lam, n_tau, U=U)
         sq["gptq_info"] = sq.pop("info")
     else:
         sq = _lib.sqc_calibrate(W, bits, hinv, group, lam, n_tau)

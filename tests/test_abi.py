@@ -84,6 +84,19 @@ def test_salience_validation(lib):
     assert lib.slim_salience_workspace(64, 250, 128) == 0
 
 
+def test_salience_u_validation(lib):
+    def call(**kw):
+        return lib.slim_salience_u(kw.get("H", FAKE), kw.get("m", 256), kw.get("damp", 0.01), FAKE, kw.get("wdt", 1),
+                                   kw.get("n", 64), kw.get("g", 128), FAKE, FAKE, None, kw.get("U", FAKE),
+                                   kw.get("info", FAKE), FAKE, kw.get("ws", 1 << 40), None)
+    assert call(H=None) == -1 and call(U=None) == -1 and call(info=None) == -1
+    assert call(wdt=3) == -3
+    assert call(m=200) == -2 and call(g=96) == -2 and call(n=0) == -2
+    assert call(damp=-1.0) == -4
+    assert call(ws=16) == -5
+    assert call(U=ctypes.c_void_p(4100)) == -7
+
+
 def test_sba_validation(lib):
     def call(**kw):
         return lib.slim_sba_search(FAKE, kw.get("xdt", 1), kw.get("t", 100), FAKE, kw.get("wdt", 1),
@@ -166,4 +179,16 @@ def test_gptq_validation(lib):
     assert call(ws=None) == -5 and call(wsb=16) == -5
     assert call(H=ctypes.c_void_p(4100)) == -7
     assert lib.slim_gptq_workspace(64, 256, 128) > lib.slim_salience_workspace(64, 256, 128)
+
+    def call_u(**kw):
+        return lib.slim_gptq_quantize_u(kw.get("U", FAKE), kw.get("m", 256), kw.get("W", FAKE), kw.get("wdt", 1),
+                                        kw.get("n", 64), kw.get("g", 128), FAKE, FAKE, kw.get("lam", 0.1),
+                                        kw.get("n_tau", 50), FAKE, FAKE, FAKE, FAKE, None, kw.get("info", FAKE),
+                                        kw.get("ws", FAKE), kw.get("wsb", 1 << 40), None)
+    assert call_u(U=None) == -1 and call_u(W=None) == -1 and call_u(info=None) == -1
+    assert call_u(wdt=3) == -3
+    assert call_u(n=0) == -2 and call_u(m=200) == -2 and call_u(g=96) == -2
+    assert call_u(n_tau=0) == -4 and call_u(lam=1.0) == -4
+    assert call_u(ws=None) == -5 and call_u(wsb=16) == -5
+    assert call_u(U=ctypes.c_void_p(4100)) == -7
     assert lib.slim_gptq_workspace(64, 250, 128) == 0

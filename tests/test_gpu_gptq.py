@@ -137,3 +137,38 @@ def test_gptq_full_size_sampled_rows(slim):
     o = oracle.gptq_quantize(W[rows], H, bits, d32, 128)
     sub = {k: r[k][rows] for k in ("codes", "scale", "zero", "tau_idx", "mask")}
     assert _compare(sub, o, 128) >= 0.9 * len(rows)
+
+
+def test_salience_u_factor_and_gptq_reuse(slim):
+    # slim_salience_u: the salience of slim_salience (float64 rounding in
+    # another order) plus U with H_d^-1 = U^T U, checked against LAPACK's
+    # factor; slim_gptq_quantize_u on that U must give slim_gptq_quantize's
+    # outputs bit for bit (both come from the same reversed sweep of H).
+    n, m, g, N = 200, 352, 32, 2          # m not a multiple of 64: padded sweep
+    print(f"salience_u / gptq_u n={n} m={m} g={g}", flush=True)
+    H, W, d32, bits = _inputs(n, m, g, N, "bf16", seed=5)
+    Ht, Wt = torch.from_numpy(H).to("cuda:0"), dev(W, torch, True)
+    hinv, gsal, info, _ = slim.salience(Ht, Wt, g)
+    hinv_u, gsal_u, info_u, _, U = slim.salience(Ht, Wt, g, want_u=True)
+    torch.cuda.synchronize()
+    assert int(host(info)[0]) == 0 and int(host(info_u)[0]) == 0
+    np.testing.assert_allclose(host(hinv_u), host(hinv), rtol=1e-6)
+    np.testing.assert_allclose(host(gsal_u), host(gsal), rtol=1e-9)
+    Uh = host(U)
+    Uo, inf = oracle.upper_chol_inverse(H)
+    assert inf == 0
+    assert np.all(np.tril(Uh, -1) == 0.0)
+    np.testing.assert_allclose(Uh, Uo, rtol=1e-8, atol=1e-10 * float(np.abs(Uo).max()))
+    bt, dt = torch.from_numpy(bits).to("cuda:0"), torch.from_numpy(d32).to("cuda:0")
+    r_h = slim.gptq_quantize(Ht, Wt, bt, dt, g)
+    r_u = slim.gptq_quantize(None, Wt, bt, dt, g, U=U)
+    torch.cuda.synchronize()
+    assert int(host(r_u["info"])[0]) == 0
+    for key in ("codes", "scale", "zero", "tau_idx", "mask"):
+        assert np.array_equal(host(r_u[key]), host(r_h[key])), key
+    # a non-finite weight is still reported on this path
+    W2 = np.array(W, copy=True)
+    W2[7, 11] = 0x7f80                      # bfloat16 +inf
+    r2 = slim.gptq_quantize(None, dev(W2, torch, True), bt, dt, g, U=U)
+    torch.cuda.synchronize()
+    assert int(host(r2["info"])[0]) == -1
