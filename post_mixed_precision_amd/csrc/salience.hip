@@ -12,12 +12,11 @@
 // substitution L Z = I: when panel p is factored, its rows of Z = L^-1 become
 // final (Z_p = L_pp^-1 R_p) and every later row block is updated
 // R_i -= L_ip Z_p.  Since H_d^-1 = Z^T Z, d_j is the squared norm of column j of
-// Z, accumulated panel by panel in a fixed order.  Per panel p:
-//   chol_panel  L_ip = A_ip L_pp^-T for the rows below; Z_p = L_pp^-1 R_p and d += col-norms^2
-//   chol_trail       (part 1) block column p+1 of A and row block p+1 of Z
-//   chol_trail_diag  (part 2) the rest of A_ij -= L_ip L_jp^T and
-//                    R_ij -= L_ip Z_pj, with diagonal block p+1 factored and
-//                    inverted by workgroup 0 of the same launch (lookahead:
+// Z, accumulated panel by panel in a fixed order.  Per panel p, two launches:
+//   chol_panel       L_ip = A_ip L_pp^-T for the rows below; Z_p = L_pp^-1 R_p and d += col-norms^2
+//   chol_trail_diag  A_ij -= L_ip L_jp^T and R_ij -= L_ip Z_pj over the
+//                    trailing tiles, with diagonal block p+1 updated, factored
+//                    and inverted by workgroup 0 of the same launch (lookahead:
 //                    the one-workgroup step does not wait for the bulk update,
 //                    nor the bulk for it, and no cross-stream wait is needed)
 // The GEMM-shaped work uses v_mfma_f64_16x16x4_f64 on 64x64 tiles.
@@ -341,26 +340,31 @@ __device__ __forceinline__ void trail_tile(double *__restrict__ A, double *__res
       }
 }
 
-// Trailing update of panel p, split for lookahead (NB panels in all):
-//   part 1 (next = 1): block column p+1 of A (row blocks p+1 .. NB-1) and
-//                      row block p+1 of Z (column blocks 0 .. p);
-//   part 2 (next = 0): A tiles with row >= column >= p+2, and Z row blocks
-//                      p+2 .. NB-1 (column blocks 0 .. p).
-// Diagonal block p+1 is factored by its own launch between the two parts
-// (its inputs are final once part 1 has run).
-__device__ __forceinline__ void trail_coords(int64_t w, int p, int NB, int next, int &ii, int &jj, bool &zt) {
-  if (next) {
-    const int nA = NB - p - 1;
-    if (w < nA) {
-      ii = p + 1 + (int)w;
+// Trailing update of panel p (NB panels in all), one launch with the next
+// diagonal block factored beside it (lookahead).  Workgroup b:
+//   b = 0          tile (p+1, p+1) of A, then factors and inverts that block
+//                  (no other workgroup reads or writes it, nor TinvT);
+//   1 <= b < NB    the rest of block column p+1 of A (row blocks p+2 .. NB-1)
+//                  and row block p+1 of Z (column blocks 0 .. p);
+//   b >= NB        A tiles with row >= column >= p+2, and Z row blocks
+//                  p+2 .. NB-1 (column blocks 0 .. p).
+// The next panel solve needs all of block column p+1, the factored block and
+// row block p+1 of Z, so it follows this launch on the same stream with no
+// cross-stream wait.
+__device__ __forceinline__ void trail_coords(int64_t b, int p, int NB, int &ii, int &jj, bool &zt) {
+  if (b < NB) {
+    const int nA = NB - p - 1;   // block column p+1, the diagonal tile (b = 0) included
+    if (b < nA) {
+      ii = p + 1 + (int)b;
       jj = p + 1;
       zt = false;
     } else {
       ii = p + 1;
-      jj = (int)(w - nA);
+      jj = (int)(b - nA);
       zt = true;
     }
   } else {
+    const int64_t w = b - NB;
     const int n2 = NB - p - 2;
     const int64_t nA = (int64_t)n2 * (n2 + 1) / 2;
     if (w < nA) {
@@ -380,32 +384,20 @@ __device__ __forceinline__ void trail_coords(int64_t w, int p, int NB, int next,
   }
 }
 
-__global__ __launch_bounds__(256) void chol_trail_kernel(double *__restrict__ A, double *__restrict__ Z,
-                                                         double *__restrict__ TinvT, int32_t *__restrict__ info,
-                                                         int64_t mp, int p, int NB, int next) {
-  int ii, jj;
-  bool zt;
-  trail_coords(blockIdx.x, p, NB, next, ii, jj, zt);
-  trail_tile(A, Z, mp, (int64_t)p * NBK, (int64_t)ii * NBK, (int64_t)jj * NBK, zt);
-}
-
-// Part 2 of panel p's trailing update with diagonal block p+1 factored
-// beside it, in one launch: workgroup 0 factors the block (its inputs are
-// final once part 1 has run; no part-2 tile reads it or TinvT), the others
-// take the part-2 tiles.  The next panel then follows on the same stream
-// with no cross-stream wait.
 __global__ __launch_bounds__(256) void chol_trail_diag_kernel(double *__restrict__ A, double *__restrict__ Z,
                                                               double *__restrict__ TinvT,
                                                               int32_t *__restrict__ info, int64_t mp, int p,
                                                               int NB) {
-  if (blockIdx.x == 0) {
-    chol_diag_body<256>(A, mp, p + 1, TinvT, info);
-    return;
-  }
   int ii, jj;
   bool zt;
-  trail_coords((int64_t)blockIdx.x - 1, p, NB, 0, ii, jj, zt);
+  trail_coords((int64_t)blockIdx.x, p, NB, ii, jj, zt);
   trail_tile(A, Z, mp, (int64_t)p * NBK, (int64_t)ii * NBK, (int64_t)jj * NBK, zt);
+  if (blockIdx.x == 0) {
+    // the block's updated entries were stored by other threads of this workgroup
+    __threadfence();
+    __syncthreads();
+    chol_diag_body<256>(A, mp, p + 1, TinvT, info);
+  }
 }
 
 // hinv[j] = d_j; after the reversed sweep d holds the diagonal in reverse order.
@@ -498,20 +490,18 @@ hipError_t launch_chol_inverse(const float *H, int64_t m, double damp, bool reve
     if (blocks > 65536) blocks = 65536;
     sal_init_kernel<<<(unsigned)blocks, 256, 0, st>>>(H, m, mp, alpha, A, Z, d, info, reverse ? 1 : 0);
   }
-  // Per panel: the panel solve, part 1 of the trailing update (the next
-  // block column, whose diagonal block is then final), then part 2 with the
-  // next diagonal block factored beside it in the same launch.
+  // Per panel: the panel solve, then the trailing update with the next
+  // diagonal block factored beside it in the same launch.
   const int NB = (int)(mp / NBK);
   chol_diag_kernel<<<1, 512, 0, st>>>(A, mp, 0, TinvT, info);
   for (int p = 0; p < NB; ++p) {
     const int nrow = NB - p - 1;
     chol_panel_kernel<<<nrow + p + 1, 256, 0, st>>>(A, Z, TinvT, d, mp, p, nrow);
     if (nrow > 0) {
-      chol_trail_kernel<<<(unsigned)(nrow + p + 1), 256, 0, st>>>(A, Z, TinvT, info, mp, p, NB, 1);
       const int64_t n2 = nrow - 1;
       const int64_t rest = n2 * (n2 + 1) / 2 + n2 * (p + 1);
       timer_begin(K_CHOL_UPDATE, st);
-      chol_trail_diag_kernel<<<(unsigned)(1 + rest), 256, 0, st>>>(A, Z, TinvT, info, mp, p, NB);
+      chol_trail_diag_kernel<<<(unsigned)(NB + rest), 256, 0, st>>>(A, Z, TinvT, info, mp, p, NB);
       timer_end(K_CHOL_UPDATE, st);
     }
   }
