@@ -230,7 +230,7 @@ int slim_tau_table(double lambda, int n_tau, float *out_host);
  * 3-sigma mask of each group's calibration); tau_idx uint8 [n, k] or NULL;
  * info int32 [1] (LAPACK convention for H_d; -1 for non-finite H or W;
  * outputs unspecified when info != 0).  Workspace:
- * slim_gptq_workspace(n, m, g) bytes (8 (2 m_p^2 + m^2 + n m) + 4 n m bytes
+ * slim_gptq_workspace(n, m, g) bytes (8 (2 m_p^2 + n m) + 4 n m bytes
  * and change, m_p = m rounded up to 64).  Requires n >= 1, m % group == 0,
  * damp_frac >= 0, the lambda / n_tau ranges of slim_sqc_calibrate.
  * ---------------------------------------------------------------------- */

@@ -37,30 +37,20 @@ namespace slim {
 
 constexpr int GQ_SB = 16;   // columns per sub-block of the sweep
 
-// U (m x m, upper, zeros below) and its transpose Ut from the inverse factor
-// Z (mp x mp) of the reversed matrix.
+// U (m x m, upper, zeros below) from the inverse factor Z (mp x mp) of the
+// reversed matrix.
 __global__ __launch_bounds__(256) void gptq_u_kernel(const double *__restrict__ Z, int64_t mp, int64_t m,
-                                                     double *__restrict__ U, double *__restrict__ Ut) {
+                                                     double *__restrict__ U) {
   const int64_t total = m * m;
   for (int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x; idx < total; idx += (int64_t)gridDim.x * 256) {
     const int64_t r = idx / m, c = idx % m;
-    const double v = c >= r ? Z[(m - 1 - r) * mp + (m - 1 - c)] : 0.0;
-    U[idx] = v;
-    Ut[c * m + r] = v;
+    U[idx] = c >= r ? Z[(m - 1 - r) * mp + (m - 1 - c)] : 0.0;
   }
 }
 
-// Ut = U^T for a factor the caller supplies; info starts at 0 (a fill
-// kernel rather than a memset, so the call stays capturable).
-__global__ __launch_bounds__(256) void gptq_ut_kernel(const double *__restrict__ U, int64_t m,
-                                                      double *__restrict__ Ut, int32_t *__restrict__ info) {
-  const int64_t total = m * m;
-  if (blockIdx.x == 0 && threadIdx.x == 0) *info = 0;
-  for (int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x; idx < total; idx += (int64_t)gridDim.x * 256) {
-    const int64_t r = idx / m, c = idx % m;
-    Ut[c * m + r] = U[idx];
-  }
-}
+// info starts at 0 when the caller supplies the factor (a fill kernel rather
+// than a memset, so the call stays capturable).
+__global__ void gptq_info_kernel(int32_t *__restrict__ info) { *info = 0; }
 
 // W64 = W, W32 = W (the float32 copy the group calibration reads); a
 // non-finite weight sets info = -1.
@@ -90,13 +80,16 @@ __global__ __launch_bounds__(256) void gptq_prep_kernel(const void *__restrict__
 template <int G>
 __global__ __launch_bounds__(64) void gptq_sweep_kernel(const double *__restrict__ W64, int64_t n, int64_t m,
                                                         int j, const double *__restrict__ U,
-                                                        const double *__restrict__ Ut,
                                                         const float *__restrict__ scale,
                                                         const float *__restrict__ zero,
                                                         const int8_t *__restrict__ bits, uint8_t *__restrict__ codes,
                                                         double *__restrict__ Err) {
   constexpr int NSB = G / GQ_SB;
   __shared__ double slab[NSB * 4 * 64];
+  // The group's diagonal block of U, ublk[r][c] = U[c0 + r][c0 + c]: every
+  // coefficient the sweep uses, staged once (G = 128: 128 KB) so that no
+  // column waits on a load from memory.
+  __shared__ __attribute__((aligned(16))) double ublk[G * G];
   const int lane = threadIdx.x;
   const int q = lane & 3;                 // lane in the quad
   const int qbase = lane & ~3;
@@ -105,6 +98,12 @@ __global__ __launch_bounds__(64) void gptq_sweep_kernel(const double *__restrict
   const int64_t il = live ? i : n - 1;
   const int64_t k = m / G;
   const int64_t c0 = (int64_t)j * G;
+  // 16-byte pieces: U is 16-byte aligned and m, c0 are even
+#pragma unroll 8
+  for (int idx = lane; idx < G * G / 2; idx += 64) {
+    const int r = idx / (G / 2), c = 2 * (idx % (G / 2));
+    *(double2 *)&ublk[r * G + c] = *(const double2 *)(U + (c0 + r) * m + c0 + c);
+  }
   for (int sb = 0; sb < NSB; ++sb) {
     const double2 *src = (const double2 *)(W64 + il * m + c0 + sb * GQ_SB + 4 * q);
     const double2 a = src[0], b = src[1];
@@ -116,8 +115,10 @@ __global__ __launch_bounds__(64) void gptq_sweep_kernel(const double *__restrict
   const float s = scale[il * k + j], z = zero[il * k + j];
   const float maxq = (float)((1 << bits[j]) - 1);
   const float r = 1.0f / s;
+  __syncthreads();
   for (int sb = 0; sb < NSB; ++sb) {
     const int64_t cb = c0 + sb * GQ_SB;   // first column of the sub-block
+    const double *ub = ublk + (sb * GQ_SB) * G + sb * GQ_SB;   // U[cb + c][cb + c2] = ub[c * G + c2]
     double w[GQ_SB], e[GQ_SB];
     {
       double mine[4];
@@ -139,7 +140,7 @@ __global__ __launch_bounds__(64) void gptq_sweep_kernel(const double *__restrict
       qv = fminf(fmaxf(qv, 0.0f), maxq);
       const float dq = qv - z;
       const float wh = dq * s;
-      const double *urow = U + (cb + c) * m + cb;
+      const double *urow = ub + c * G;
       e[c] = (w[c] - (double)wh) / urow[c];
 #pragma unroll
       for (int c2 = c + 1; c2 < GQ_SB; ++c2) w[c2] = w[c2] - e[c] * urow[c2];
@@ -157,14 +158,18 @@ __global__ __launch_bounds__(64) void gptq_sweep_kernel(const double *__restrict
     // the sub-block's errors onto this lane's columns of the later sub-blocks,
     // in column order within the update (four independent chains)
     for (int sb2 = sb + 1; sb2 < NSB; ++sb2) {
-      const double *ucol = Ut + (c0 + sb2 * GQ_SB + 4 * q) * m + cb;   // U[cb .. cb+15][column 4q + t]
+      const double *ucol = ub + (sb2 - sb) * GQ_SB + 4 * q;   // U[cb + c][c0 + 16 sb2 + 4q + t] = ucol[c * G + t]
       double v[4];
 #pragma unroll
       for (int t = 0; t < 4; ++t) v[t] = slab[(4 * sb2 + t) * 64 + lane];
 #pragma unroll
-      for (int c = 0; c < GQ_SB; ++c)
-#pragma unroll
-        for (int t = 0; t < 4; ++t) v[t] = v[t] - e[c] * ucol[t * m + c];
+      for (int c = 0; c < GQ_SB; ++c) {
+        const double2 u01 = *(const double2 *)(ucol + c * G), u23 = *(const double2 *)(ucol + c * G + 2);
+        v[0] = v[0] - e[c] * u01.x;
+        v[1] = v[1] - e[c] * u01.y;
+        v[2] = v[2] - e[c] * u23.x;
+        v[3] = v[3] - e[c] * u23.y;
+      }
 #pragma unroll
       for (int t = 0; t < 4; ++t) slab[(4 * sb2 + t) * 64 + lane] = v[t];
     }
@@ -227,7 +232,6 @@ size_t gptq_ws_bytes(int64_t n, int64_t m, int group) {
   off += align_up((size_t)NBK * NBK * 8, 256);    // TinvT
   off += align_up((size_t)mp * 8, 256);           // d
   off += 256;                                     // alpha
-  off += align_up((size_t)m * m * 8, 256);        // Ut
   off += align_up((size_t)n * m * 8, 256);        // W64
   off += align_up((size_t)n * m * 4, 256);        // W32
   off += align_up((size_t)n * group * 8, 256);    // Err
@@ -235,12 +239,12 @@ size_t gptq_ws_bytes(int64_t n, int64_t m, int group) {
 }
 
 template <int G>
-static void gq_group(double *W64, float *W32, int64_t n, int64_t m, int j, const double *U, const double *Ut,
+static void gq_group(double *W64, float *W32, int64_t n, int64_t m, int j, const double *U,
                      const float *scale, const float *zero, const int8_t *bits, uint8_t *codes, double *Err,
                      hipStream_t st) {
   const unsigned nrb = (unsigned)((n + 63) / 64);
   timer_begin(K_GPTQ_SWEEP, st);
-  gptq_sweep_kernel<G><<<(unsigned)((n + 15) / 16), 64, 0, st>>>(W64, n, m, j, U, Ut, scale, zero, bits, codes, Err);
+  gptq_sweep_kernel<G><<<(unsigned)((n + 15) / 16), 64, 0, st>>>(W64, n, m, j, U, scale, zero, bits, codes, Err);
   timer_end(K_GPTQ_SWEEP, st);
   const int64_t c1 = (int64_t)(j + 1) * G;
   if (c1 < m) {
@@ -268,8 +272,6 @@ hipError_t launch_gptq(const float *H, const double *Ugiven, int64_t m, double d
   off += align_up((size_t)mp * 8, 256);
   double *alpha = (double *)(base + off);
   off += 256;
-  double *Ut = (double *)(base + off);
-  off += align_up((size_t)m * m * 8, 256);
   double *W64 = (double *)(base + off);
   off += align_up((size_t)n * m * 8, 256);
   float *W32 = (float *)(base + off);
@@ -283,12 +285,12 @@ hipError_t launch_gptq(const float *H, const double *Ugiven, int64_t m, double d
     if (blocks > 65536) blocks = 65536;
     if (Ugiven) {
       // the factor of a salience call on the same H (slim_salience_u)
-      gptq_ut_kernel<<<(unsigned)blocks, 256, 0, st>>>(Ugiven, m, Ut, info);
+      gptq_info_kernel<<<1, 1, 0, st>>>(info);
     } else {
       e = launch_chol_inverse(H, m, damp, true, A, Z, TinvT, d, alpha, info, st);
       if (e != hipSuccess) return e;
       U = A;   // the factor is no longer needed once its inverse is formed
-      gptq_u_kernel<<<(unsigned)blocks, 256, 0, st>>>(Z, mp, m, A, Ut);
+      gptq_u_kernel<<<(unsigned)blocks, 256, 0, st>>>(Z, mp, m, A);
     }
     blocks = (n * m + 255) / 256;
     if (blocks > 65536) blocks = 65536;
@@ -302,11 +304,11 @@ hipError_t launch_gptq(const float *H, const double *Ugiven, int64_t m, double d
     e = launch_sqc(W32, false, n, m, group, bits, hinv, tt, n_tau, scale, zero, codes, mask, tau_idx, st, j, 1);
     if (e != hipSuccess) return e;
     if (group == 32)
-      gq_group<32>(W64, W32, n, m, j, U, Ut, scale, zero, bits, codes, Err, st);
+      gq_group<32>(W64, W32, n, m, j, U, scale, zero, bits, codes, Err, st);
     else if (group == 64)
-      gq_group<64>(W64, W32, n, m, j, U, Ut, scale, zero, bits, codes, Err, st);
+      gq_group<64>(W64, W32, n, m, j, U, scale, zero, bits, codes, Err, st);
     else
-      gq_group<128>(W64, W32, n, m, j, U, Ut, scale, zero, bits, codes, Err, st);
+      gq_group<128>(W64, W32, n, m, j, U, scale, zero, bits, codes, Err, st);
   }
   return hipGetLastError();
 }
