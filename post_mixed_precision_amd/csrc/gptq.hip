@@ -177,12 +177,17 @@ __global__ __launch_bounds__(64) void gptq_sweep_kernel(const double *__restrict
 }
 
 // W64[:, c1:] -= Err (n x G) . U[c1-G .. c1-1][c1:], 64 x 64 output tiles;
-// columns of the next group also go to the float32 copy.
+// columns of the next group also go to the float32 copy.  Every operand of
+// the tile (all K chunks and the W64 tile itself) is loaded into registers
+// first, so the loads are in flight together; the chunks then pass through
+// LDS one at a time.
 template <int G>
 __global__ __launch_bounds__(256) void gptq_trail_kernel(double *__restrict__ W64, float *__restrict__ W32,
                                                          int64_t n, int64_t m, int64_t c1,
                                                          const double *__restrict__ Err,
                                                          const double *__restrict__ U) {
+  constexpr int NKC = (G + NBK - 1) / NBK;   // K chunks of up to 64
+  constexpr int KC = G < NBK ? G : NBK;      // K columns per chunk
   __shared__ double sA[NBK * SP];
   __shared__ double sB[NBK * SP];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -190,21 +195,42 @@ __global__ __launch_bounds__(256) void gptq_trail_kernel(double *__restrict__ W6
   const int64_t r0 = (int64_t)blockIdx.x * NBK;
   const int64_t col0 = c1 + (int64_t)blockIdx.y * NBK;
   const int64_t u0 = c1 - G;   // first U row of the group
-  f64x4_t acc[2][2];
-  zero_acc(acc);
-  for (int kc = 0; kc < G; kc += NBK) {
-    // sA[kk][ii] = Err[r0+ii][kc+kk], sB[kk][cc] = U[u0+kc+kk][col0+cc]; zero outside
-#pragma unroll 4
+  // ra: Err[r0+ii][kc+kk] for sA[kk][ii]; rb: U[u0+kc+k2][col0+cc] for sB[k2][cc]; zero outside
+  double ra[NKC][16], rb[NKC][16];
+#pragma unroll
+  for (int c = 0; c < NKC; ++c)
+#pragma unroll
     for (int e = 0; e < 16; ++e) {
       const int idx = tid + e * 256;
-      const int ii = idx >> 6, kk = idx & 63;
-      sA[kk * SP + ii] = (r0 + ii < n && kc + kk < G) ? Err[(r0 + ii) * G + kc + kk] : 0.0;
-      const int k2 = idx >> 6, cc = idx & 63;
-      sB[k2 * SP + cc] = (kc + k2 < G && col0 + cc < m) ? U[(u0 + kc + k2) * m + col0 + cc] : 0.0;
+      const int hi = idx >> 6, lo = idx & 63;
+      ra[c][e] = (r0 + hi < n && lo < KC) ? Err[(r0 + hi) * G + c * NBK + lo] : 0.0;
+      rb[c][e] = (hi < KC && col0 + lo < m) ? U[(u0 + c * NBK + hi) * m + col0 + lo] : 0.0;
+    }
+  double wv[2][2][4];
+#pragma unroll
+  for (int a = 0; a < 2; ++a)
+#pragma unroll
+    for (int b = 0; b < 2; ++b)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int64_t row = r0 + wm * 32 + a * 16 + 4 * v + (lane >> 4);
+        const int64_t col = col0 + wn * 32 + b * 16 + (lane & 15);
+        wv[a][b][v] = (row < n && col < m) ? W64[row * m + col] : 0.0;
+      }
+  f64x4_t acc[2][2];
+  zero_acc(acc);
+#pragma unroll
+  for (int c = 0; c < NKC; ++c) {
+    if (c) __syncthreads();
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const int idx = tid + e * 256;
+      const int hi = idx >> 6, lo = idx & 63;
+      sA[lo * SP + hi] = ra[c][e];
+      sB[hi * SP + lo] = rb[c][e];
     }
     __syncthreads();
     gemm64(sA, sB, acc, lane, wm, wn);
-    __syncthreads();
   }
 #pragma unroll
   for (int a = 0; a < 2; ++a)
@@ -215,7 +241,7 @@ __global__ __launch_bounds__(256) void gptq_trail_kernel(double *__restrict__ W6
         const int64_t row = r0 + wm * 32 + a * 16 + 4 * v + (lane >> 4);
         const int64_t col = col0 + wn * 32 + b * 16 + (lane & 15);
         if (row < n && col < m) {
-          const double nv = W64[row * m + col] - acc[a][b][v];
+          const double nv = wv[a][b][v] - acc[a][b][v];
           W64[row * m + col] = nv;
           if (col < c1 + G) W32[row * m + col] = (float)nv;
         }
