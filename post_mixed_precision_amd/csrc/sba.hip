@@ -688,17 +688,34 @@ __global__ __launch_bounds__(256) void sba_combine_kernel(const float2 *__restri
     part[(blk_off + blockIdx.x) * R + r] = ((red[0][r] + red[1][r]) + red[2][r]) + red[3][r];
 }
 
-// Mean over tokens, first argmin, bit-widths at r*.
+// Mean over tokens, first argmin, bit-widths at r*.  Each step's block
+// partials are summed in block order; they pass through LDS a slice of
+// blocks at a time, so that the loads are coalesced and in flight together
+// while the sums stay sequential.
 __global__ __launch_bounds__(256) void sba_finalize_kernel(const double *__restrict__ part, int64_t nblk, int R,
                                                            int64_t T, const int *__restrict__ order, int k, int N,
                                                            double *__restrict__ kl, int32_t *__restrict__ r_star,
                                                            int8_t *__restrict__ bits) {
+  constexpr int STAGE = 2048;   // doubles per slice
   __shared__ double skl[1032];
+  __shared__ double stage[STAGE];
   __shared__ int srs;
+  const int64_t fb = STAGE / R;   // blocks per slice (R <= 1032)
+  for (int r = threadIdx.x; r < R; r += 256) skl[r] = 0.0;
+  for (int64_t b0 = 0; b0 < nblk; b0 += fb) {
+    const int64_t nb = min(fb, nblk - b0);
+    __syncthreads();
+    for (int64_t idx = threadIdx.x; idx < nb * R; idx += 256) stage[idx] = part[b0 * R + idx];
+    __syncthreads();
+    for (int r = threadIdx.x; r < R; r += 256) {
+      double s = skl[r];
+      for (int64_t b = 0; b < nb; ++b) s += stage[b * R + r];
+      skl[r] = s;
+    }
+  }
+  __syncthreads();
   for (int r = threadIdx.x; r < R; r += 256) {
-    double s = 0.0;
-    for (int64_t b = 0; b < nblk; ++b) s += part[b * R + r];
-    s = s / (double)T;
+    const double s = skl[r] / (double)T;
     skl[r] = s;
     kl[r] = s;
   }
