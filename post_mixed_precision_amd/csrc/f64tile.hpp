@@ -15,24 +15,25 @@ namespace slim {
 constexpr int NBK = 64;   // tile width
 constexpr int SP = 65;    // LDS pitch (doubles) of 64x64 operand tiles
 
-// sX[k][i] = src[(r0 + i) * ld + c0 + k]   (row-major source, k contiguous -> transposed)
-__device__ __forceinline__ void load_tile_T(double *sX, const double *__restrict__ src, int64_t ld, int64_t r0,
-                                            int64_t c0, int tid) {
-#pragma unroll 4
+// Register staging of a 64 x 64 operand tile.  Thread tid of the 256 holds
+// the elements (hi, lo) = ((tid + 256 e) / 64, (tid + 256 e) % 64), e < 16,
+// which the caller loads into registers (with every other load of the tile,
+// so that they are in flight together; lo runs along rows of the source, so
+// a wave's loads are coalesced), then stores to LDS:
+//   stash_T  sX[lo][hi] = r[e]   (the source's row index becomes the tile's column)
+//   stash_N  sX[hi][lo] = r[e]
+__device__ __forceinline__ void stash_T(double *sX, const double r[16], int tid) {
+#pragma unroll
   for (int e = 0; e < 16; ++e) {
     const int idx = tid + e * 256;
-    const int i = idx >> 6, k = idx & 63;
-    sX[k * SP + i] = src[(r0 + i) * ld + c0 + k];
+    sX[(idx & 63) * SP + (idx >> 6)] = r[e];
   }
 }
-// sX[k][c] = src[(r0 + k) * ld + c0 + c]
-__device__ __forceinline__ void load_tile_N(double *sX, const double *__restrict__ src, int64_t ld, int64_t r0,
-                                            int64_t c0, int tid) {
-#pragma unroll 4
+__device__ __forceinline__ void stash_N(double *sX, const double r[16], int tid) {
+#pragma unroll
   for (int e = 0; e < 16; ++e) {
     const int idx = tid + e * 256;
-    const int k = idx >> 6, c = idx & 63;
-    sX[k * SP + c] = src[(r0 + k) * ld + c0 + c];
+    sX[(idx >> 6) * SP + (idx & 63)] = r[e];
   }
 }
 

@@ -260,8 +260,17 @@ __global__ __launch_bounds__(256) void chol_panel_kernel(double *__restrict__ A,
   zero_acc(acc);
   if (w < nrow) {
     const int64_t r0 = k0 + (int64_t)(w + 1) * NBK;
-    load_tile_T(sA, A, mp, r0, k0, tid);        // A operand (i, k) = A[r0+i][k0+k]
-    load_tile_N(sB, TinvT, NBK, 0, 0, tid);     // B operand (k, c) = Tinv[c][k]
+    // A operand (i, k) = A[r0+i][k0+k], B operand (k, c) = Tinv[c][k]; all loads issued first
+    double ra[16], rb[16];
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const int idx = tid + e * 256;
+      const int hi = idx >> 6, lo = idx & 63;
+      ra[e] = A[(r0 + hi) * mp + k0 + lo];
+      rb[e] = TinvT[hi * NBK + lo];
+    }
+    stash_T(sA, ra, tid);
+    stash_N(sB, rb, tid);
     __syncthreads();
     gemm64(sA, sB, acc, lane, wm, wn);
 #pragma unroll
@@ -276,8 +285,17 @@ __global__ __launch_bounds__(256) void chol_panel_kernel(double *__restrict__ A,
         }
   } else {
     const int64_t c0 = (int64_t)(w - nrow) * NBK;
-    load_tile_N(sA, TinvT, NBK, 0, 0, tid);     // A operand (i, k) = Tinv[i][k] = TinvT[k][i]
-    load_tile_N(sB, Z, mp, k0, c0, tid);        // B operand (k, c) = R[k0+k][c0+c]
+    // A operand (i, k) = Tinv[i][k] = TinvT[k][i], B operand (k, c) = R[k0+k][c0+c]
+    double ra[16], rb[16];
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const int idx = tid + e * 256;
+      const int hi = idx >> 6, lo = idx & 63;
+      ra[e] = TinvT[hi * NBK + lo];
+      rb[e] = Z[(k0 + hi) * mp + c0 + lo];
+    }
+    stash_N(sA, ra, tid);
+    stash_N(sB, rb, tid);
     __syncthreads();
     gemm64(sA, sB, acc, lane, wm, wn);
     double cs[2] = {0.0, 0.0};
@@ -311,22 +329,25 @@ __global__ __launch_bounds__(256) void chol_panel_kernel(double *__restrict__ A,
 // One 64 x 64 tile of the trailing update of panel p:
 //   A tile (rows r0, cols c0):  A_ij -= L_ip L_jp^T
 //   Z tile (rows r0, cols c0):  Z_ib,cb -= L_ip Z_p,cb
+// Both operands and the tile itself are loaded into registers first, so all
+// of the loads are in flight together, then the operands pass through LDS.
 __device__ __forceinline__ void trail_tile(double *__restrict__ A, double *__restrict__ Z, int64_t mp, int64_t k0,
                                            int64_t r0, int64_t c0, bool zt) {
   __shared__ double sA[NBK * SP];
   __shared__ double sB[NBK * SP];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
-  load_tile_T(sA, A, mp, r0, k0, tid);
-  if (zt)
-    load_tile_N(sB, Z, mp, k0, c0, tid);
-  else
-    load_tile_T(sB, A, mp, c0, k0, tid);
-  __syncthreads();
-  f64x4_t acc[2][2];
-  zero_acc(acc);
-  gemm64(sA, sB, acc, lane, wm, wn);
   double *C = zt ? Z : A;
+  // ra[e] = A[r0+hi][k0+lo] -> sA[lo][hi]; rb[e] = Z[k0+hi][c0+lo] -> sB[hi][lo] (Z tile)
+  // or A[c0+hi][k0+lo] -> sB[lo][hi] (A tile)
+  double ra[16], rb[16], cv[2][2][4];
+#pragma unroll
+  for (int e = 0; e < 16; ++e) {
+    const int idx = tid + e * 256;
+    const int hi = idx >> 6, lo = idx & 63;
+    ra[e] = A[(r0 + hi) * mp + k0 + lo];
+    rb[e] = zt ? Z[(k0 + hi) * mp + c0 + lo] : A[(c0 + hi) * mp + k0 + lo];
+  }
 #pragma unroll
   for (int i = 0; i < 2; ++i)
 #pragma unroll
@@ -335,8 +356,26 @@ __device__ __forceinline__ void trail_tile(double *__restrict__ A, double *__res
       for (int v = 0; v < 4; ++v) {
         const int row = wm * 32 + i * 16 + 4 * v + (lane >> 4);
         const int col = wn * 32 + j * 16 + (lane & 15);
-        double *dst = C + (r0 + row) * mp + c0 + col;
-        *dst = *dst - acc[i][j][v];
+        cv[i][j][v] = C[(r0 + row) * mp + c0 + col];
+      }
+  stash_T(sA, ra, tid);
+  if (zt)
+    stash_N(sB, rb, tid);
+  else
+    stash_T(sB, rb, tid);
+  __syncthreads();
+  f64x4_t acc[2][2];
+  zero_acc(acc);
+  gemm64(sA, sB, acc, lane, wm, wn);
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int row = wm * 32 + i * 16 + 4 * v + (lane >> 4);
+        const int col = wn * 32 + j * 16 + (lane & 15);
+        C[(r0 + row) * mp + c0 + col] = cv[i][j][v] - acc[i][j][v];
       }
 }
 
