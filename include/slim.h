@@ -303,9 +303,14 @@ int slim_qlinear(const void *X, int xdt, int64_t t, int64_t m, const uint32_t *p
  * "gptq_sweep", "gptq_trail" (per group).
  * slim_timing_read synchronises those events
  * and returns the summed milliseconds and the launch count since the last
- * reset.  Returns SLIM_E_PARAM for an unknown name.
+ * reset.  Returns SLIM_E_PARAM for an unknown name.  slim_timing_enable(1)
+ * selects every kernel; slim_timing_select then leaves one out (on = 0) or
+ * takes it back, so that kernels launched many times per call (chol_update,
+ * gptq_sweep, gptq_trail: per panel or per group) need not add their event
+ * records to a timed run.
  * ---------------------------------------------------------------------- */
 int slim_timing_enable(int on);
+int slim_timing_select(const char *kernel, int on);
 int slim_timing_reset(void);
 int slim_timing_read(const char *kernel, double *total_ms, int64_t *launches);
 

@@ -17,9 +17,9 @@ device memory and the stream.
 """
 from ._lib import (SlimError, load_library, hessian, salience, sba_search, sba_search_ex, sqc_calibrate, gptq_quantize, pack, qlinear,
                    tau_table,
-                   timing_enable, timing_reset, timing_read, SLIM_F32, SLIM_BF16)
+                   timing_enable, timing_select, timing_reset, timing_read, SLIM_F32, SLIM_BF16)
 from .layer import quantize_layer
 
 __all__ = ["SlimError", "load_library", "hessian", "salience", "sba_search", "sba_search_ex", "sqc_calibrate", "gptq_quantize", "pack", "qlinear",
-           "tau_table", "timing_enable", "timing_reset", "timing_read", "quantize_layer", "SLIM_F32",
+           "tau_table", "timing_enable", "timing_select", "timing_reset", "timing_read", "quantize_layer", "SLIM_F32",
            "SLIM_BF16"]

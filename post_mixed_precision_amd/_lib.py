@@ -51,6 +51,7 @@ _SIGS = {
     "slim_qlinear": (_c_int, [_c_vp, _c_int, _c_i64, _c_i64, _c_vp, _c_vp, _c_int, _c_vp, _c_vp, _c_i64, _c_int,
                               _c_vp, _c_vp, _c_sz, _c_vp]),
     "slim_timing_enable": (_c_int, [_c_int]),
+    "slim_timing_select": (_c_int, [ctypes.c_char_p, _c_int]),
     "slim_timing_reset": (_c_int, []),
     "slim_timing_read": (_c_int, [ctypes.c_char_p, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(_c_i64)]),
 }
@@ -328,6 +329,11 @@ def tau_table(lam: float = 0.1, n_tau: int = 50) -> np.ndarray:
 
 def timing_enable(on: bool = True):
     load_library().slim_timing_enable(int(on))
+
+
+def timing_select(kernel: str, on: bool):
+    """Leave one timed kernel out of (on=False) or back in the enabled timing."""
+    check(load_library().slim_timing_select(kernel.encode(), int(on)), "slim_timing_select")
 
 
 def timing_reset():

@@ -32,6 +32,7 @@ struct TimerSlot {
 };
 std::mutex g_timer_mu;
 bool g_timer_on = false;
+bool g_timer_sel[slim::K_NUM_TIMED];   // per kernel, set by slim_timing_select (all on with each enable)
 TimerSlot g_slots[slim::K_NUM_TIMED];
 const char *g_timer_names[slim::K_NUM_TIMED] = {"hessian_gram", "chol_update", "sba_klgemm", "sqc_calibrate",
                                                 "pack_planes", "qlinear", "gptq_sweep", "gptq_trail"};
@@ -55,7 +56,7 @@ namespace slim {
 
 void timer_begin(int id, hipStream_t st) {
   std::lock_guard<std::mutex> lk(g_timer_mu);
-  if (!g_timer_on) return;
+  if (!g_timer_on || !g_timer_sel[id]) return;
   hipEvent_t e;
   if (hipEventCreate(&e) != hipSuccess) return;
   if (hipEventRecord(e, st) != hipSuccess) {
@@ -309,7 +310,20 @@ int slim_qlinear(const void *X, int xdt, int64_t t, int64_t m, const uint32_t *p
 int slim_timing_enable(int on) {
   std::lock_guard<std::mutex> lk(g_timer_mu);
   g_timer_on = on != 0;
+  for (bool &b : g_timer_sel) b = true;
   return SLIM_OK;
+}
+
+int slim_timing_select(const char *kernel, int on) {
+  if (!kernel) return SLIM_E_NULL;
+  std::lock_guard<std::mutex> lk(g_timer_mu);
+  for (int i = 0; i < slim::K_NUM_TIMED; ++i) {
+    if (strcmp(kernel, g_timer_names[i]) == 0) {
+      g_timer_sel[i] = on != 0;
+      return SLIM_OK;
+    }
+  }
+  return SLIM_E_PARAM;
 }
 
 int slim_timing_reset(void) {

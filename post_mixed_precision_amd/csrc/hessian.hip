@@ -358,6 +358,8 @@ __global__ __launch_bounds__(256) void hessian_reduce_kernel(const float *__rest
     const int idx = tid + e * 256;
     const int rr = idx / Q, c = (idx % Q) * 4;
     float4 s = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+    // unrolled so that several splits' loads are in flight; the sum stays in split order
+#pragma unroll 4
     for (int sp = 0; sp < nsplit; ++sp) {
       const float4 v = src[sp * sstride + idx];
       s.x += v.x;

@@ -48,7 +48,8 @@ __global__ __launch_bounds__(256) void sal_alpha_kernel(const float *__restrict_
 // A = lower(H) mirrored + alpha I (identity in the padding), Z = I, d = 0.
 // With reverse set, A holds J H J + alpha I instead (J reverses the index
 // order: A[i][j] = H[m-1-i][m-1-j]); its factor gives the upper Cholesky
-// factor of the inverse that GPTQ uses.
+// factor of the inverse that GPTQ uses.  Only 64 x 64 blocks on or below the
+// block diagonal are written: the sweep never reads A or Z above it.
 __global__ __launch_bounds__(256) void sal_init_kernel(const float *__restrict__ H, int64_t m, int64_t mp,
                                                        const double *__restrict__ alpha, double *__restrict__ A,
                                                        double *__restrict__ Z, double *__restrict__ d,
@@ -58,6 +59,7 @@ __global__ __launch_bounds__(256) void sal_init_kernel(const float *__restrict__
   bool bad = false;
   for (int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x; idx < total; idx += (int64_t)gridDim.x * 256) {
     const int64_t i = idx / mp, j = idx % mp;
+    if (j / NBK > i / NBK) continue;
     double v;
     if (i < m && j < m) {
       const int64_t hi = reverse ? m - 1 - i : i, hj = reverse ? m - 1 - j : j;

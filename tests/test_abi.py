@@ -139,6 +139,10 @@ def test_timing_interface(lib):
     assert _lib.timing_read("sba_klgemm") == (0.0, 0)
     ms, cnt = ctypes.c_double(), ctypes.c_int64()
     assert lib.slim_timing_read(b"nope", ctypes.byref(ms), ctypes.byref(cnt)) == -4
+    assert lib.slim_timing_select(b"nope", 0) == -4
+    assert lib.slim_timing_select(None, 0) == -1
+    assert lib.slim_timing_select(b"chol_update", 0) == 0
+    assert lib.slim_timing_enable(0) == 0
 
 
 def test_sba_variant_validation(lib):
