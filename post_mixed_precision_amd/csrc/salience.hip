@@ -83,14 +83,14 @@ __global__ __launch_bounds__(256) void sal_init_kernel(const float *__restrict__
 // part, column by column) with the same row operations applied to a
 // right-hand side R that starts as the identity; afterwards
 // L_ij = a_ij / sqrt(a_jj) and (L^-1)_ij = R_ij / sqrt(a_ii).  The columns are
-// taken four at a time: with P the 4 x 4 pivot block and v the row's four
-// entries in its columns (both as they stand when the block is reached),
-// eliminating the four columns one by one amounts to
+// taken EB (eight) at a time: with P the EB x EB pivot block and v the row's
+// EB entries in its columns (both as they stand when the block is reached),
+// eliminating those columns one by one amounts to
 //     a_i,c += h_i . v_c  (c past the block),   R_i += h_i . R_block,
 //     h_i = -P^-1 v_i,
 // and the row's entries in the block's columns become L_P^-1 v_i (P = L_P D
-// L_P^T, unit L_P, D the four pivots).  Every thread factors P itself, so one
-// barrier per four columns publishes the block's columns of A and rows of R.
+// L_P^T, unit L_P, D the EB pivots).  Every thread factors P itself, so one
+// barrier per EB columns publishes the block's columns of A and rows of R.
 // Thread t keeps its cells of row t / NS (DC contiguous columns) of both
 // arrays in registers.
 template <int NT>
@@ -98,7 +98,7 @@ __device__ __forceinline__ void chol_diag_body(double *__restrict__ A, int64_t m
                                                int32_t *__restrict__ info) {
   constexpr int DC = NBK * NBK / NT;   // columns per thread
   constexpr int NS = NBK / DC;         // column strips per row
-  constexpr int EB = 4;                // columns eliminated per barrier
+  constexpr int EB = 8;                // columns eliminated per barrier
   static_assert(DC % EB == 0, "a block of columns lies in one strip");
   // Ping-pong buffers: the block's columns of A (all rows) and rows of R,
   // both stored [t][pm(c)] with pm(c) = (c % DC) NS + c / DC, so the NS
