@@ -13,9 +13,10 @@
 // final (Z_p = L_pp^-1 R_p) and every later row block is updated
 // R_i -= L_ip Z_p.  Since H_d^-1 = Z^T Z, d_j is the squared norm of column j of
 // Z, accumulated panel by panel in a fixed order.  Per panel p, two launches:
-//   chol_panel       L_ip = A_ip L_pp^-T for the rows below; Z_p = L_pp^-1 R_p and d += col-norms^2
+//   chol_panel       L_ip = A_ip L_pp^-T for the rows below; Z_p = L_pp^-1 R_p and d += col-norms^2;
+//                    diagonal tile p+1 updated with its L tile
 //   chol_trail_diag  A_ij -= L_ip L_jp^T and R_ij -= L_ip Z_pj over the
-//                    trailing tiles, with diagonal block p+1 updated, factored
+//                    trailing tiles, with diagonal block p+1 factored
 //                    and inverted by workgroup 0 of the same launch (lookahead:
 //                    the one-workgroup step does not wait for the bulk update,
 //                    nor the bulk for it, and no cross-stream wait is needed)
@@ -246,7 +247,8 @@ __global__ __launch_bounds__(512) void chol_diag_kernel(double *__restrict__ A, 
   chol_diag_body<512>(A, mp, p, TinvT, info);
 }
 
-// Panel kernel.  Workgroups [0, nrow): row block ib = p+1+w: L_ib,p = A_ib,p Tinv^T.
+// Panel kernel.  Workgroups [0, nrow): row block ib = p+1+w: L_ib,p = A_ib,p Tinv^T
+// (workgroup 0 then also updates diagonal tile p+1 with its L tile).
 // Workgroups [nrow, nrow+p+1): column block cb: Z_p[:, cb] = Tinv R_p[:, cb], d[cb] += column norms^2.
 __global__ __launch_bounds__(256) void chol_panel_kernel(double *__restrict__ A, double *__restrict__ Z,
                                                          const double *__restrict__ TinvT, double *__restrict__ d,
@@ -262,6 +264,22 @@ __global__ __launch_bounds__(256) void chol_panel_kernel(double *__restrict__ A,
   zero_acc(acc);
   if (w < nrow) {
     const int64_t r0 = k0 + (int64_t)(w + 1) * NBK;
+    // Workgroup 0's row block is the next diagonal block: it also updates that
+    // tile, A_{p+1,p+1} -= L L^T with the L tile it forms, whose entries it
+    // loads here with the operands.
+    double cv[2][2][4];
+    if (w == 0) {
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+          for (int v = 0; v < 4; ++v) {
+            const int row = wm * 32 + i * 16 + 4 * v + (lane >> 4);
+            const int col = wn * 32 + j * 16 + (lane & 15);
+            cv[i][j][v] = A[(r0 + row) * mp + r0 + col];
+          }
+    }
     // A operand (i, k) = A[r0+i][k0+k], B operand (k, c) = Tinv[c][k]; all loads issued first
     double ra[16], rb[16];
 #pragma unroll
@@ -285,6 +303,34 @@ __global__ __launch_bounds__(256) void chol_panel_kernel(double *__restrict__ A,
           const int col = wn * 32 + j * 16 + (lane & 15);
           A[(r0 + row) * mp + k0 + col] = acc[i][j][v];
         }
+    if (w == 0) {
+      __syncthreads();   // the product's operand reads are done
+      // sA[k][i] = L[i][k] serves as both operands: the product is L L^T
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+          for (int v = 0; v < 4; ++v) {
+            const int row = wm * 32 + i * 16 + 4 * v + (lane >> 4);
+            const int col = wn * 32 + j * 16 + (lane & 15);
+            sA[col * SP + row] = acc[i][j][v];
+          }
+      __syncthreads();
+      f64x4_t acc2[2][2];
+      zero_acc(acc2);
+      gemm64(sA, sA, acc2, lane, wm, wn);
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+          for (int v = 0; v < 4; ++v) {
+            const int row = wm * 32 + i * 16 + 4 * v + (lane >> 4);
+            const int col = wn * 32 + j * 16 + (lane & 15);
+            A[(r0 + row) * mp + r0 + col] = cv[i][j][v] - acc2[i][j][v];
+          }
+    }
   } else {
     const int64_t c0 = (int64_t)(w - nrow) * NBK;
     // A operand (i, k) = Tinv[i][k] = TinvT[k][i], B operand (k, c) = R[k0+k][c0+c]
@@ -383,7 +429,8 @@ __device__ __forceinline__ void trail_tile(double *__restrict__ A, double *__res
 
 // Trailing update of panel p (NB panels in all), one launch with the next
 // diagonal block factored beside it (lookahead).  Workgroup b:
-//   b = 0          tile (p+1, p+1) of A, then factors and inverts that block
+//   b = 0          factors and inverts diagonal block p+1, which the panel
+//                  solve's workgroup for row block p+1 has already updated
 //                  (no other workgroup reads or writes it, nor TinvT);
 //   1 <= b < NB    the rest of block column p+1 of A (row blocks p+2 .. NB-1)
 //                  and row block p+1 of Z (column blocks 0 .. p);
@@ -429,16 +476,15 @@ __global__ __launch_bounds__(256) void chol_trail_diag_kernel(double *__restrict
                                                               double *__restrict__ TinvT,
                                                               int32_t *__restrict__ info, int64_t mp, int p,
                                                               int NB) {
+  if (blockIdx.x == 0) {
+    // tile (p+1, p+1) was updated by the panel solve
+    chol_diag_body<256>(A, mp, p + 1, TinvT, info);
+    return;
+  }
   int ii, jj;
   bool zt;
   trail_coords((int64_t)blockIdx.x, p, NB, ii, jj, zt);
   trail_tile(A, Z, mp, (int64_t)p * NBK, (int64_t)ii * NBK, (int64_t)jj * NBK, zt);
-  if (blockIdx.x == 0) {
-    // the block's updated entries were stored by other threads of this workgroup
-    __threadfence();
-    __syncthreads();
-    chol_diag_body<256>(A, mp, p + 1, TinvT, info);
-  }
 }
 
 // hinv[j] = d_j; after the reversed sweep d holds the diagonal in reverse order.
