@@ -135,6 +135,47 @@ def _dev(t):
     return t
 
 
+def _arg(t, name: str, shape=None, dtypes=None, min_numel=None):
+    """Check a tensor argument on the host before anything is launched: its
+    dtype and its exact shape (None entries are free) or minimum element
+    count.  The C ABI sees only pointers and the sizes passed beside them, so
+    a tensor of the wrong size would become an out-of-bounds access on the
+    device; this is where that is stopped.  Residency is checked afterwards,
+    for all arguments at once (_on_gpu)."""
+    torch = _torch()
+    if not isinstance(t, torch.Tensor):
+        raise SlimError(f"{name}: expected a torch tensor, got {type(t).__name__}")
+    if dtypes is not None and t.dtype not in dtypes:
+        raise SlimError(f"{name}: dtype {t.dtype}, expected one of {list(dtypes)}")
+    if shape is not None:
+        if t.dim() != len(shape) or any(s is not None and int(a) != int(s) for a, s in zip(t.shape, shape)):
+            raise SlimError(f"{name}: shape {tuple(t.shape)}, expected {tuple('*' if s is None else s for s in shape)}")
+    if min_numel is not None and t.numel() < min_numel:
+        raise SlimError(f"{name}: {t.numel()} elements, at least {min_numel} needed")
+    return t
+
+
+def _on_gpu(*ts):
+    """Every given tensor is contiguous, in GPU memory, on one device."""
+    ts = [t for t in ts if t is not None]
+    for t in ts:
+        _dev(t)
+    devs = {t.device for t in ts}
+    if len(devs) > 1:
+        raise SlimError(f"tensors live on different devices: {sorted(map(str, devs))}")
+
+
+def _group_count(m: int, group: int) -> int:
+    if group not in (32, 64, 128) or m % group != 0:
+        raise SlimError(f"group {group} must be 32, 64 or 128 and divide m = {m}")
+    return m // group
+
+
+def _float_types():
+    torch = _torch()
+    return (torch.bfloat16, torch.float32)
+
+
 def _ptr(t):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
 
@@ -151,10 +192,16 @@ def hessian(X, H=None, accumulate: bool = False):
     """H (+)= 2 X^T X, X [T, m] bf16/f32 on the GPU -> H float32 [m, m]."""
     torch = _torch()
     lib = load_library()
-    X = _dev(X)
+    X = _arg(X, "X", (None, None), _float_types())
     T, m = X.shape
     if H is None:
+        if accumulate:
+            raise SlimError("accumulate=True needs the H to add to")
+        _on_gpu(X)
         H = torch.empty((m, m), dtype=torch.float32, device=X.device)
+    else:
+        H = _arg(H, "H", (m, m), (torch.float32,))
+        _on_gpu(X, H)
     ws = _ws(lib.slim_hessian_workspace(T, m, _dtype_code(X)), X.device)
     check(lib.slim_hessian(_ptr(X), _dtype_code(X), T, m, _ptr(H), int(accumulate), _ptr(ws), ws.numel(),
                            _stream(X.device)), "slim_hessian")
@@ -166,9 +213,11 @@ def salience(H, W, group: int, damp_frac: float = 0.01, elem: bool = False, want
     want_u the upper Cholesky factor U f64 [m, m] of H_d^-1 appended (slim_salience_u)."""
     torch = _torch()
     lib = load_library()
-    H, W = _dev(H), _dev(W)
+    W = _arg(W, "W", (None, None), _float_types())
     n, m = W.shape
-    k = m // group
+    k = _group_count(m, group)
+    H = _arg(H, "H", (m, m), (torch.float32,))
+    _on_gpu(H, W)
     hinv = torch.empty(m, dtype=torch.float32, device=W.device)
     gsal = torch.empty(k, dtype=torch.float64, device=W.device)
     info = torch.zeros(1, dtype=torch.int32, device=W.device)
@@ -189,10 +238,13 @@ def sba_search(X, W, group_sal, group: int, avg_bits: int):
     """-> (bits int8 [k], kl f64 [k//2+1], r_star int32 [1])."""
     torch = _torch()
     lib = load_library()
-    X, W, group_sal = _dev(X), _dev(W), _dev(group_sal)
+    X = _arg(X, "X", (None, None), _float_types())
     T, m = X.shape
+    W = _arg(W, "W", (None, m), _float_types())
     n = W.shape[0]
-    k = m // group
+    k = _group_count(m, group)
+    group_sal = _arg(group_sal, "group_sal", (k,), (torch.float64,))
+    _on_gpu(X, W, group_sal)
     bits = torch.empty(k, dtype=torch.int8, device=W.device)
     kl = torch.empty(k // 2 + 1, dtype=torch.float64, device=W.device)
     rs = torch.empty(1, dtype=torch.int32, device=W.device)
@@ -211,18 +263,23 @@ def sba_search_ex(X, W, group: int, avg_bits: int, group_sal=None, order=None, o
     replaces the salience ranking.  -> (bits int8 [k], score f64 [k//2+1], r_star int32 [1])."""
     torch = _torch()
     lib = load_library()
-    X, W = _dev(X), _dev(W)
+    X = _arg(X, "X", (None, None), _float_types())
+    T, m = X.shape
+    W = _arg(W, "W", (None, m), _float_types())
+    k = _group_count(m, group)
+    if group_sal is None and order is None:
+        raise SlimError("give group_sal (salience ranking) or order")
     if group_sal is not None:
-        group_sal = _dev(group_sal)
+        group_sal = _arg(group_sal, "group_sal", (k,), (torch.float64,))
     if order is not None:
-        order = _dev(order)
-        if order.dtype != torch.int32:
-            raise SlimError("order must be int32")
+        order = _arg(order, "order", (k,), (torch.int32,))
+        # a permutation of the groups, checked on the host (k <= a few hundred)
+        if sorted(order.cpu().tolist()) != list(range(k)):
+            raise SlimError("order must be a permutation of 0..k-1")
     if objective not in OBJECTIVES:
         raise SlimError(f"unknown objective {objective!r}")
-    T, m = X.shape
+    _on_gpu(X, W, group_sal, order)
     n = W.shape[0]
-    k = m // group
     bits = torch.empty(k, dtype=torch.int8, device=W.device)
     score = torch.empty(k // 2 + 1, dtype=torch.float64, device=W.device)
     rs = torch.empty(1, dtype=torch.int32, device=W.device)
@@ -237,9 +294,12 @@ def sqc_calibrate(W, bits, hinv, group: int, lam: float = 0.1, n_tau: int = 50, 
     """-> dict(scale, zero [n, k] f32; codes [n, m] u8; mask [n, m/32] i32 bits; tau_idx [n, k] u8)."""
     torch = _torch()
     lib = load_library()
-    W, bits, hinv = _dev(W), _dev(bits), _dev(hinv)
+    W = _arg(W, "W", (None, None), _float_types())
     n, m = W.shape
-    k = m // group
+    k = _group_count(m, group)
+    bits = _arg(bits, "bits", (k,), (torch.int8,))
+    hinv = _arg(hinv, "hinv", (m,), (torch.float32,))
+    _on_gpu(W, bits, hinv)
     dev = W.device
     out = {
         "scale": torch.empty((n, k), dtype=torch.float32, device=dev),
@@ -262,9 +322,18 @@ def gptq_quantize(H, W, bits, hinv, group: int, damp_frac: float = 0.01, lam: fl
     (slim_gptq_quantize_u)."""
     torch = _torch()
     lib = load_library()
-    W, bits, hinv = _dev(W), _dev(bits), _dev(hinv)
+    W = _arg(W, "W", (None, None), _float_types())
     n, m = W.shape
-    k = m // group
+    k = _group_count(m, group)
+    bits = _arg(bits, "bits", (k,), (torch.int8,))
+    hinv = _arg(hinv, "hinv", (m,), (torch.float32,))
+    if U is not None:
+        U = _arg(U, "U", (m, m), (torch.float64,))
+    else:
+        if H is None:
+            raise SlimError("give H, or the factor U")
+        H = _arg(H, "H", (m, m), (torch.float32,))
+    _on_gpu(W, bits, hinv, U, H)
     dev = W.device
     out = {
         "scale": torch.empty((n, k), dtype=torch.float32, device=dev),
@@ -276,13 +345,11 @@ def gptq_quantize(H, W, bits, hinv, group: int, damp_frac: float = 0.01, lam: fl
     }
     ws = _ws(lib.slim_gptq_workspace(n, m, group), dev)
     if U is not None:
-        U = _dev(U)
         check(lib.slim_gptq_quantize_u(_ptr(U), m, _ptr(W), _dtype_code(W), n, group, _ptr(bits), _ptr(hinv),
                                        float(lam), int(n_tau), _ptr(out["scale"]), _ptr(out["zero"]),
                                        _ptr(out["codes"]), _ptr(out["mask"]), _ptr(out["tau_idx"]),
                                        _ptr(out["info"]), _ptr(ws), ws.numel(), _stream(dev)), "slim_gptq_quantize_u")
         return out
-    H = _dev(H)
     check(lib.slim_gptq_quantize(_ptr(H), m, float(damp_frac), _ptr(W), _dtype_code(W), n, group, _ptr(bits),
                                  _ptr(hinv), float(lam), int(n_tau), _ptr(out["scale"]), _ptr(out["zero"]),
                                  _ptr(out["codes"]), _ptr(out["mask"]), _ptr(out["tau_idx"]), _ptr(out["info"]),
@@ -294,8 +361,11 @@ def pack(codes, bits, group: int, avg_bits: int):
     """-> (packed int32 words [n*m*N/32] (uint32 bit patterns), info int32 [1])."""
     torch = _torch()
     lib = load_library()
-    codes, bits = _dev(codes), _dev(bits)
+    codes = _arg(codes, "codes", (None, None), (torch.uint8,))
     n, m = codes.shape
+    k = _group_count(m, group)
+    bits = _arg(bits, "bits", (k,), (torch.int8,))
+    _on_gpu(codes, bits)
     words = lib.slim_pack_words(n, m, avg_bits)
     if words < 0:
         raise SlimError("bad pack shape")
@@ -310,9 +380,18 @@ def qlinear(X, packed, bits, scale, zero, group: int, avg_bits: int):
     """Y = X W_hat^T from the packed planes: X [t, m] bf16/f32 (t <= 8) -> Y float32 [t, n]."""
     torch = _torch()
     lib = load_library()
-    X, packed, bits, scale, zero = _dev(X), _dev(packed), _dev(bits), _dev(scale), _dev(zero)
+    X = _arg(X, "X", (None, None), _float_types())
     T, m = X.shape
+    k = _group_count(m, group)
+    scale = _arg(scale, "scale", (None, k), (torch.float32,))
     n = scale.shape[0]
+    zero = _arg(zero, "zero", (n, k), (torch.float32,))
+    bits = _arg(bits, "bits", (k,), (torch.int8,))
+    words = lib.slim_pack_words(n, m, avg_bits)
+    if words < 0:
+        raise SlimError("bad layer shape or average width")
+    packed = _arg(packed, "packed", (None,), (torch.int32,), min_numel=words)
+    _on_gpu(X, packed, bits, scale, zero)
     Y = torch.empty((T, n), dtype=torch.float32, device=X.device)
     ws = _ws(lib.slim_qlinear_workspace(T, n, m, group), X.device)
     check(lib.slim_qlinear(_ptr(X), _dtype_code(X), T, m, _ptr(packed), _ptr(bits), int(avg_bits), _ptr(scale),
