@@ -39,6 +39,7 @@ from .sqc import mask_3sigma, sqc_calibrate
 from .pack import pack_bitplanes, unpack_bitplanes, packed_words
 from .qlinear import dequant_weights, qlinear
 from .gptq import upper_chol_inverse, gptq_quantize
+from .lwc import lwc_calibrate
 from .pipeline import quantize_layer
 
 __all__ = [
@@ -47,5 +48,5 @@ __all__ = [
     "fake_quant", "quant_codes", "rank_groups", "allocation", "trial_weights",
     "kl_divergence", "sba_search", "mask_3sigma", "sqc_calibrate", "pack_bitplanes",
     "unpack_bitplanes", "packed_words", "quantize_layer", "dequant_weights", "qlinear",
-    "upper_chol_inverse", "gptq_quantize",
+    "upper_chol_inverse", "gptq_quantize", "lwc_calibrate",
 ]
