@@ -5,11 +5,14 @@
 A step is one pass of the whole path over one linear layer whose inputs are
 already resident in HBM: Hessian 2X^TX, damped inverse-diagonal salience and
 group means, the SBA scan scored by output KL, SQC calibration and bit-plane
-packing.  The default workload is the LLaMA-7B-shaped attention projection:
-W 4096 x 4096 bf16 ~ N(0, 0.02^2), X 262144 calibration tokens (128 sequences
-of 2048) x 4096 bf16 with 1% clustered outlier channels, group 128, 2-bit
-average over {1, 2, 3}; synthetic, seeded (synth/).  value = n*m / 1e6 /
-seconds per step (Mparams quantized per second).
+packing.  The default workload is the largest single layer, the
+Llama-70B-shaped MLP projection: W 28672 x 8192 bf16 ~ N(0, 0.015^2), X 262144
+calibration tokens (128 sequences of 2048) x 8192 bf16 with 1% clustered
+outlier channels, group 128, 2-bit average over {1, 2, 3}; synthetic, seeded
+(synth/).  value = n*m / 1e6 / seconds per step (Mparams quantized per
+second).  --workload llama7b-attn-4096 --linear 0 gives the 4096 x 4096
+attention projection; --decoder-layer times a whole 7B-shaped decoder layer
+(seven linears, one Hessian per input width) and prints its own line.
 
 The JSON line also carries the roofline of the dominant kernel (the fused
 SBA GEMM + KL kernel, timed live with HIP events on its own launch stream)
@@ -30,6 +33,11 @@ sys.path.insert(0, ROOT)
 
 PEAK_BF16_FLOPS = 2.5e15   # MI355X dense bf16 MFMA
 PEAK_HBM_BPS = 8.0e12      # MI355X HBM3E
+# fp32 vector ALU: 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz, one lane-op per cycle
+PEAK_VALU_LANE_OPS = 256 * 4 * 16 * 2.4e9
+# SQC's algorithmic ALU work per weight: 51 tau candidates x 9 float32 lane-ops
+# (w*r, +z, round, clamp low, clamp high, -z, *s, w - w_hat, weighted square sum)
+SQC_LANE_OPS_PER_PARAM = 51 * 9
 
 
 def _dev(a, torch):
@@ -113,7 +121,13 @@ def run_step(slim, X, W, group, N, ev=None, variant=None, gptq=False):
 
 
 def cpu_baseline(wl, lin_idx, group, N, Xh, Wh):
-    """The oracle as it stands, on a bounded sample; stage costs scaled to the layer."""
+    """The oracle as it stands, on a bounded sample; stage costs scaled to the layer.
+
+    Hessian: a token sample (cost linear in T).  Salience: full width (its
+    inverse is O(m^3), its salience pass O(nm)).  SBA scan: a row sample of W,
+    timed at two token counts; the fitted fixed + per-token cost is scaled to
+    all tokens and to all rows (every step's work is linear in n).  SQC and
+    packing: row samples (linear in n)."""
     import oracle
     try:
         from threadpoolctl import threadpool_info
@@ -123,45 +137,59 @@ def cpu_baseline(wl, lin_idx, group, N, Xh, Wh):
     lin = wl.linears[lin_idx]
     n, m, T = lin.n, lin.m, wl.tokens
     storage = wl.dtype
-    t_h = min(T, 16384)
+    k = m // group
+    measured = 0.0
+    t_h = min(T, 4096)
     t0 = time.perf_counter()
     H = oracle.hessian(Xh[:t_h])
-    t_hsmp = time.perf_counter() - t0
-    s_hess = t_hsmp * T / t_h
+    dt = time.perf_counter() - t0
+    measured += dt
+    s_hess = dt * T / t_h
     # salience needs a full-width H; the sample's H stands in (same cost)
     t0 = time.perf_counter()
     d32, S, info = oracle.salience(H, Wh, group, 0.01)
     s_sal = time.perf_counter() - t0
-    # SBA: per-token cost of the scan on a token slice
-    t_s = min(T, 16384)
-    t0 = time.perf_counter()
-    bits, kl, rs = oracle.sba_search(Xh[:t_s], Wh, S, N, group, storage)
-    s_sba_slice = time.perf_counter() - t0
-    t0 = time.perf_counter()
-    oracle.trial_weights(Wh, bits, group, storage)
-    s_trial = time.perf_counter() - t0
-    k = m // group
-    per_tok = max(s_sba_slice - 3 * s_trial, 1e-9) / t_s
-    s_sba = per_tok * T + 3 * s_trial
+    measured += s_sal
+    # SBA: every step's cost is linear in the rows; fit fixed + per-token cost
+    n_s = min(n, max(256, n // 16))
+    rows = np.linspace(0, n - 1, n_s).astype(np.int64)
+    Ws = Wh[rows]
+    tk = (min(T, 128), min(T, 512))
+    secs = []
+    for ts in tk:
+        t0 = time.perf_counter()
+        bits, _, _ = oracle.sba_search(Xh[:ts], Ws, S, N, group, storage)
+        secs.append(time.perf_counter() - t0)
+    measured += sum(secs)
+    per_tok = max(secs[1] - secs[0], 0.0) / max(tk[1] - tk[0], 1)
+    fixed = max(secs[0] - per_tok * tk[0], 0.0)
+    s_sba = (fixed + per_tok * T) * n / n_s
     # SQC on a row sample
-    rows = min(n, 1024)
+    r_q = min(n, 256)
     t0 = time.perf_counter()
-    sq = oracle.sqc_calibrate(Wh, bits, d32, group, 0.1, 50, rows=np.arange(rows))
-    s_sqc = (time.perf_counter() - t0) * n / rows
-    codes = np.zeros((n, m), dtype=np.uint8)
-    codes[:rows] = sq["codes"]
+    sq = oracle.sqc_calibrate(Wh, bits, d32, group, 0.1, 50, rows=np.arange(r_q))
+    dt = time.perf_counter() - t0
+    measured += dt
+    s_sqc = dt * n / r_q
+    r_p = min(n, max(256, n // 16))
+    codes = np.zeros((r_p, m), dtype=np.uint8)
+    part = sq["codes"][:r_p]
+    codes[:len(part)] = part
     t0 = time.perf_counter()
     oracle.pack_bitplanes(codes, bits, group)
-    s_pack = time.perf_counter() - t0
+    dt = time.perf_counter() - t0
+    measured += dt
+    s_pack = dt * n / r_p
     total = s_hess + s_sal + s_sba + s_sqc + s_pack
     return {
         "value": n * m / 1e6 / total, "unit": "Mparams/s", "cores": int(threads), "kind": "oracle",
-        "sample": (f"Hessian on {t_h} tokens (x{T / t_h:g}); salience at full width {m}; SBA scan over all "
-                   f"{k // 2 + 1} steps on {t_s} tokens (per-token cost x{T}) plus 3 trial quantizations; "
-                   f"SQC on {rows} of {n} rows (x{n / rows:.0f}); packing in full"),
+        "sample": (f"Hessian on {t_h} of {T} tokens (x{T / t_h:g}); salience at full width {m}; SBA scan over all "
+                   f"{k // 2 + 1} steps on {n_s} of {n} rows at {tk[0]} and {tk[1]} tokens, fixed + per-token cost "
+                   f"fitted and scaled to {T} tokens and {n} rows; SQC on {r_q} rows (x{n / r_q:g}); "
+                   f"packing on {r_p} rows (x{n / r_p:g})"),
         "seconds_extrapolated": {"hessian": s_hess, "salience": s_sal, "sba": s_sba, "sqc": s_sqc,
                                  "pack": s_pack, "total": total},
-        "seconds_measured": round(t_hsmp + s_sal + s_sba_slice + s_trial + s_sqc * rows / n + s_pack, 2),
+        "seconds_measured": round(measured, 2),
     }
 
 
@@ -213,13 +241,75 @@ def qlinear_bench(slim, torch, args):
     print(json.dumps(out), flush=True)
 
 
+def decoder_layer_bench(slim, torch, synth, args):
+    """The whole 7B-shaped decoder layer: q/k/v/o 4096x4096, gate/up
+    11008x4096, down 4096x11008, bf16; one calibration X per input width
+    (262144 tokens each), so H is formed once per width and shared by the
+    linears that read it.  A step is both Hessians plus salience, SBA, SQC and
+    packing of all seven linears.  value = total params / 1e6 / seconds."""
+    wl = synth.WORKLOADS["llama7b-decoder-layer"]
+    group = args.group or 128
+    N = wl.avg_bits
+    Xd, Wd = {}, []
+    for m in wl.widths:
+        print(f"# generating X {wl.tokens}x{m}", file=sys.stderr, flush=True)
+        Xd[m] = _dev(synth.make_x(wl, m), torch)
+    for i, lin in enumerate(wl.linears):
+        Wd.append(_dev(synth.make_w(wl, i), torch))
+    torch.cuda.synchronize()
+
+    def step(ev=None):
+        H = {m: slim.hessian(X) for m, X in Xd.items()}
+        if ev is not None:
+            ev[1].record()
+        infos = []
+        for lin, W in zip(wl.linears, Wd):
+            X = Xd[lin.m]
+            hinv, gsal, info, _ = slim.salience(H[lin.m], W, group, 0.01)
+            bits, kl, rs = slim.sba_search(X, W, gsal, group, N)
+            sq = slim.sqc_calibrate(W, bits, hinv, group, 0.1, 50, want_tau=False)
+            packed, pinfo = slim.pack(sq["codes"], bits, group, N)
+            infos.append((info, pinfo))
+        return infos
+
+    for i in range(args.warmup):
+        infos = step()
+        torch.cuda.synchronize()
+        print(f"# warmup {i}", file=sys.stderr, flush=True)
+    assert all(int(a.item()) == 0 and int(b.item()) == 0 for a, b in infos)
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s_ in range(args.steps):
+        evs[s_][0].record()
+        step(evs[s_])
+        evs[s_][2].record()
+    torch.cuda.synchronize()
+    sec = (time.perf_counter() - t0) / args.steps
+    h_ms = float(np.median([e[0].elapsed_time(e[1]) for e in evs]))
+    params = sum(l.n * l.m for l in wl.linears)
+    out = {"metric": "Mparams quantized/s per decoder layer (seven linears, one Hessian per input width)",
+           "value": round(params / 1e6 / sec, 3), "unit": "Mparams/s", "n_gpus": 1, "steps": args.steps,
+           "warmup": args.warmup, "ms_per_step": round(sec * 1e3, 3), "higher_is_better": True,
+           "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+           "data": "synthetic (seeded; stands in for 128x2048 WikiText2 tokens and LLaMA weights)",
+           "config": {"workload": "llama7b-decoder-layer", "linears": [f"{l.name} {l.n}x{l.m}" for l in wl.linears],
+                      "tokens": wl.tokens, "group": group, "avg_bits": N, "hessians": len(Xd)},
+           "hessians_ms": round(h_ms, 3)}
+    print(json.dumps(out), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=5)
     ap.add_argument("--warmup", type=int, default=2)
-    ap.add_argument("--workload", default="llama7b-attn-4096")
-    ap.add_argument("--linear", type=int, default=0)
+    ap.add_argument("--workload", default="large-13b-70b")
+    ap.add_argument("--linear", type=int, default=None,
+                    help="index of the linear in the workload (default: the last, the largest of large-13b-70b)")
+    ap.add_argument("--decoder-layer", action="store_true",
+                    help="time the whole 7B-shaped decoder layer (seven linears, one Hessian per input width) "
+                         "and print its own JSON line")
     ap.add_argument("--group", type=int, default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--objective", choices=("kl", "mse"), default="kl",
@@ -253,7 +343,13 @@ def main():
         qlinear_bench(slim, torch, args)
         return
 
+    if args.decoder_layer:
+        decoder_layer_bench(slim, torch, synth, args)
+        return
+
     wl = synth.WORKLOADS[args.workload]
+    if args.linear is None:
+        args.linear = len(wl.linears) - 1
     lin = wl.linears[args.linear]
     group = args.group or wl.groups[0]
     N = wl.avg_bits
@@ -377,8 +473,14 @@ def main():
         out["roofline_other"] = {
             "hessian_gram": {"bound": "mfma", "achieved_tflops": round(hess_flops / (hms / hl * 1e-3) / 1e12, 2),
                              "frac": round(hess_flops / (hms / hl * 1e-3) / PEAK_BF16_FLOPS, 4)},
-            "sqc_calibrate": {"bound": "alu", "hbm_gbps": round(n * m * (2 + 1 + 0.125) / (q_step * 1e-3) / 1e9, 1)},
-            "pack_planes": {"bound": "hbm", "achieved_gbps": round(n * m * (1 + N / 8) / (pms / pl * 1e-3) / 1e9, 1),
+            "sqc_calibrate": {
+                "bound": "alu", "unit": "lane-op/s", "peak": PEAK_VALU_LANE_OPS,
+                "lane_ops_per_param": SQC_LANE_OPS_PER_PARAM,
+                "achieved": round(n * m * SQC_LANE_OPS_PER_PARAM / (q_step * 1e-3), -9),
+                "frac": round(n * m * SQC_LANE_OPS_PER_PARAM / (q_step * 1e-3) / PEAK_VALU_LANE_OPS, 4),
+                "hbm_gbps": round(n * m * (2 + 1 + 0.125) / (q_step * 1e-3) / 1e9, 1),
+                "hbm_frac": round(n * m * (2 + 1 + 0.125) / (q_step * 1e-3) / PEAK_HBM_BPS, 4)},
+            "pack_planes": {"bound": "hbm", "bytes": n * m * (1 + N / 8), "achieved_gbps": round(n * m * (1 + N / 8) / (pms / pl * 1e-3) / 1e9, 1),
                             "frac": round(n * m * (1 + N / 8) / (pms / pl * 1e-3) / PEAK_HBM_BPS, 4)},
         }
     # The quantized layer served from its own planes (the deployment side):

@@ -24,7 +24,10 @@
  *    workspace must be 16-byte aligned (SLIM_E_ALIGN otherwise).
  *  - The caller owns all memory.  The library allocates nothing and keeps no
  *    per-call state; scratch memory comes from a caller-provided workspace of
- *    at least the size the matching *_workspace() query returns.
+ *    at least the size the matching *_workspace() query returns.  One
+ *    exception, stated where it is declared: the optional kernel timers
+ *    (slim_timing_*), which keep process-wide state and create HIP events
+ *    while timing is enabled.
  *  - Every call enqueues its kernels on `stream` (a hipStream_t passed as
  *    void*, NULL = the default stream) and returns without synchronising.
  *  - Return value: SLIM_OK, or a negative SLIM_E_* code.  Arguments are
@@ -150,6 +153,13 @@ int slim_salience_u(const float *H, int64_t m, double damp_frac, const void *W, 
  * Requires t >= 1, n >= 1, m % group == 0, k <= SLIM_MAX_GROUPS and
  * 3 * n * m * sizeof(element) < 2^31 (the trial weights are addressed with
  * 32-bit offsets; 28672 x 8192 bf16 uses 1.4 GB).
+ *
+ * Workspace: slim_sba_workspace() gives the size that lets the tokens run in
+ * batches of up to 4 GB of per-token softmax statistics.  A smaller ws_bytes
+ * is accepted down to the size that holds one 256-token tile per batch: the
+ * tokens are then split into more batches (same result up to float rounding
+ * order inside each token's statistics, which do not depend on the batch);
+ * below that the call returns SLIM_E_WORKSPACE.
  * ---------------------------------------------------------------------- */
 size_t slim_sba_workspace(int64_t t, int64_t n, int64_t m, int group, int dtype);
 int slim_sba_search(const void *X, int xdt, int64_t t, const void *W, int wdt, int64_t n, int64_t m,
@@ -307,7 +317,8 @@ int slim_qlinear(const void *X, int xdt, int64_t t, int64_t m, const uint32_t *p
  * selects every kernel; slim_timing_select then leaves one out (on = 0) or
  * takes it back, so that kernels launched many times per call (chol_update,
  * gptq_sweep, gptq_trail: per panel or per group) need not add their event
- * records to a timed run.
+ * records to a timed run.  The timers are process-wide state: while timing is
+ * enabled every timed launch creates two HIP events (destroyed when read).
  * ---------------------------------------------------------------------- */
 int slim_timing_enable(int on);
 int slim_timing_select(const char *kernel, int on);

@@ -234,8 +234,10 @@ def salience(H, W, group: int, damp_frac: float = 0.01, elem: bool = False, want
     return hinv, gsal, info, esal
 
 
-def sba_search(X, W, group_sal, group: int, avg_bits: int):
-    """-> (bits int8 [k], kl f64 [k//2+1], r_star int32 [1])."""
+def sba_search(X, W, group_sal, group: int, avg_bits: int, ws_bytes: int | None = None):
+    """-> (bits int8 [k], kl f64 [k//2+1], r_star int32 [1]).  ws_bytes: a
+    workspace smaller than the preferred one makes the scan run its tokens
+    in more batches (slim_sba_search's workspace rule)."""
     torch = _torch()
     lib = load_library()
     X = _arg(X, "X", (None, None), _float_types())
@@ -248,7 +250,7 @@ def sba_search(X, W, group_sal, group: int, avg_bits: int):
     bits = torch.empty(k, dtype=torch.int8, device=W.device)
     kl = torch.empty(k // 2 + 1, dtype=torch.float64, device=W.device)
     rs = torch.empty(1, dtype=torch.int32, device=W.device)
-    ws = _ws(lib.slim_sba_workspace(T, n, m, group, _dtype_code(W)), W.device)
+    ws = _ws(lib.slim_sba_workspace(T, n, m, group, _dtype_code(W)) if ws_bytes is None else ws_bytes, W.device)
     check(lib.slim_sba_search(_ptr(X), _dtype_code(X), T, _ptr(W), _dtype_code(W), n, m, group, _ptr(group_sal),
                               int(avg_bits), _ptr(bits), _ptr(kl), _ptr(rs), _ptr(ws), ws.numel(),
                               _stream(W.device)), "slim_sba_search")

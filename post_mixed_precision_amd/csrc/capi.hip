@@ -54,6 +54,8 @@ void drain(TimerSlot &s) {
 
 namespace slim {
 
+void record_hip_error(hipError_t e) { g_last_hip_error = (int)e; }
+
 void timer_begin(int id, hipStream_t st) {
   std::lock_guard<std::mutex> lk(g_timer_mu);
   if (!g_timer_on || !g_timer_sel[id]) return;
@@ -181,8 +183,9 @@ int slim_sba_search_ex(const void *X, int xdt, int64_t t, const void *W, int wdt
   // the three trial-weight variants are addressed with 32-bit buffer offsets
   if ((double)n * (double)m * (xdt == SLIM_BF16 ? 2.0 : 4.0) * 3.0 > 2147483647.0) return SLIM_E_SHAPE;
   if (!aligned16(X) || !aligned16(W)) return SLIM_E_ALIGN;
-  const slim::SbaPlan p = slim::sba_plan(t, n, m, group, xdt == SLIM_BF16);
-  if (!ws || ws_bytes < p.ws_bytes) return SLIM_E_WORKSPACE;
+  if (!ws) return SLIM_E_WORKSPACE;
+  const slim::SbaPlan p = slim::sba_plan(t, n, m, group, xdt == SLIM_BF16, ws_bytes);
+  if (ws_bytes < p.ws_bytes) return SLIM_E_WORKSPACE;
   if (!aligned16(ws)) return SLIM_E_ALIGN;
   hipError_t e = slim::launch_sba(X, W, xdt == SLIM_BF16, t, n, m, group, group_sal, order, avg_bits, objective,
                                   bits, score, r_star, ws, p, (hipStream_t)stream);

@@ -48,7 +48,9 @@ struct SbaPlan {
   int64_t combine_blocks;    // total combine blocks over all batches
   size_t off_wv, off_order, off_sp, off_sq, off_part, ws_bytes;
 };
-SbaPlan sba_plan(int64_t t, int64_t n, int64_t m, int group, bool bf16);
+// ws_avail: the caller's workspace size; a smaller one (down to one token
+// tile of statistics per batch) splits the tokens into more batches.
+SbaPlan sba_plan(int64_t t, int64_t n, int64_t m, int group, bool bf16, size_t ws_avail = (size_t)-1);
 // ext_order: a caller-given group order (replaces the salience ranking) or null;
 // objective: 0 = output KL, 1 = output MSE.
 hipError_t launch_sba(const void *X, const void *W, bool bf16, int64_t t, int64_t n, int64_t m,
@@ -90,8 +92,12 @@ QlinearPlan qlinear_plan(int t, int64_t n, int64_t m, int group);
 void launch_qlinear_mma(const void *X, bool bf16, int t, int64_t m, const uint32_t *packed, const int8_t *bits,
                         int N, const float *scale, const float *zero, int64_t n, int group, int k, int gpr, int nrun,
                         float *out, hipStream_t st);
+// timed = false: no timing events are recorded, whatever slim_timing_enable says.
 hipError_t launch_qlinear(const void *X, bool bf16, int t, int64_t m, const uint32_t *packed, const int8_t *bits,
                           int N, const float *scale, const float *zero, int64_t n, int group, float *Y, void *ws,
-                          const QlinearPlan &p, hipStream_t st);
+                          const QlinearPlan &p, hipStream_t st, bool timed = true);
+
+// The error of a failed HIP call, for slim_last_hip_error() (per thread).
+void record_hip_error(hipError_t e);
 
 }  // namespace slim

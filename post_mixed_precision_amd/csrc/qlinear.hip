@@ -400,23 +400,23 @@ static void ql_launch_g(dim3 grid, size_t lds, int group, const void *X, int t, 
 
 hipError_t launch_qlinear(const void *X, bool bf16, int t, int64_t m, const uint32_t *packed, const int8_t *bits,
                           int N, const float *scale, const float *zero, int64_t n, int group, float *Y, void *ws,
-                          const QlinearPlan &p, hipStream_t st) {
+                          const QlinearPlan &p, hipStream_t st, bool timed) {
   float *out = p.nrun > 1 ? (float *)ws : Y;
   if (p.mma) {
-    timer_begin(K_QLINEAR, st);
+    if (timed) timer_begin(K_QLINEAR, st);
     launch_qlinear_mma(X, bf16, t, m, packed, bits, N, scale, zero, n, group, p.k, p.gpw, p.nrun, out, st);
     if (p.nrun > 1) {
       const int64_t e = (int64_t)t * n;
       qlinear_reduce_kernel<<<(unsigned)((e + 255) / 256), 256, 0, st>>>((const float *)ws, p.nrun, t, n, Y);
     }
-    timer_end(K_QLINEAR, st);
+    if (timed) timer_end(K_QLINEAR, st);
     return hipGetLastError();
   }
   dim3 grid((unsigned)p.nrb, (unsigned)p.nrun);
   // four groups per scale / zero load: runs start at multiples of 4 groups and
   // both arrays are 16-byte aligned
   const int szv = (p.k % 4 == 0 && p.gpw % 4 == 0 && ((uintptr_t)scale & 15) == 0 && ((uintptr_t)zero & 15) == 0);
-  timer_begin(K_QLINEAR, st);
+  if (timed) timer_begin(K_QLINEAR, st);
 #define SLIM_QL(BF, QT) \
   ql_launch_g<BF, QT>(grid, p.lds_bytes, group, X, t, m, packed, bits, N, scale, zero, n, p.k, p.gpw, szv, out, st)
   switch (ql_qt(t)) {
@@ -430,7 +430,7 @@ hipError_t launch_qlinear(const void *X, bool bf16, int t, int64_t m, const uint
     const int64_t e = (int64_t)t * n;
     qlinear_reduce_kernel<<<(unsigned)((e + 255) / 256), 256, 0, st>>>((const float *)ws, p.nrun, t, n, Y);
   }
-  timer_end(K_QLINEAR, st);
+  if (timed) timer_end(K_QLINEAR, st);
   return hipGetLastError();
 }
 

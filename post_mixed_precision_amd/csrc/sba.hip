@@ -23,17 +23,26 @@
 //
 // KL per token from chunk statistics.  With p = softmax(y), q = softmax(yhat):
 //     KL_t = sum_j p_j (y_j - yhat_j) - LSE(y) + LSE(yhat).
-// For each 128-output chunk c the kernel writes (M_c, Z_c) of y and, for every
-// step, (Mq_c, Zq_c, S_c = sum_j e^{y_j - M_c}(y_j - yhat_j)); a second kernel
-// merges chunks per token with the usual max/rescale rule, forms KL_t in
-// float64 and reduces over tokens in a fixed order.  A last single-workgroup
-// kernel takes the mean, the first argmin and the bit-widths, so nothing
-// returns to the host.
+// For each 128-output chunk c the kernel writes LSE_c(y) once and, for every
+// step, two floats: D_c = LSE_c(yhat) - LSE_c(y) and E_c = E_p[y - yhat] over
+// the chunk (sum_j e^{y_j - M_c}(y_j - yhat_j) / sum_j e^{y_j - M_c}).  A second
+// kernel turns the chunk LSEs into chunk weights w_c = e^{LSE_c(y) - LSE(y)},
+// a third forms KL_t = sum_c w_c E_c + ln sum_c w_c e^{D_c} in float64 per
+// (token, step) and reduces over tokens in a fixed order.  Both per-step
+// quantities are small and relative to the chunk's own y, so a float holds
+// them well.  A last single-workgroup kernel takes the mean, the first argmin
+// and the bit-widths, so nothing returns to the host.
 //
 // XCD-aware launch: consecutive workgroup ids land on different XCDs, so the
-// id is remapped such that each XCD owns a fixed subset of output chunks and
-// walks the token tiles in order; the weight chunks of an XCD then stay in
-// its L2 while every token tile is fetched once per XCD.
+// id is remapped such that each XCD owns a fixed subset of output chunks.
+// An XCD takes its chunks a block of CB at a time and walks every token tile
+// for that block before the next: the workgroups running together then share
+// CB weight chunks and about 32/CB token tiles, and the block's trial weights
+// stay resident in the last-level cache for the whole walk instead of being
+// fetched again for every token tile (at 28672 x 8192 one XCD's chunks hold
+// 224 MB of weights, far more than any cache level).
+#include <algorithm>
+
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -163,7 +172,7 @@ template <bool BF16, bool PARTIAL>
 __global__ __launch_bounds__(512, 1) void sba_klgemm_kernel(
     const void *__restrict__ X, const void *__restrict__ W, const void *__restrict__ Wv,
     const int *__restrict__ order, int64_t tok_base, int64_t tb_len, int64_t n, int64_t m, int g, int k, int R,
-    int NC, int NCX, int TT, int c_last, float4 *__restrict__ sq, float2 *__restrict__ sp, int mse) {
+    int NC, int NCX, int TT, int c_last, int CB, float2 *__restrict__ sq, float *__restrict__ sp, int mse) {
   constexpr int ESZ = BF16 ? 2 : 4;
   constexpr int KT = BF16 ? 64 : 32;  // K elements per stage (128 bytes per row)
   constexpr int EPP = 16 / ESZ;       // elements per 16-byte piece
@@ -186,9 +195,12 @@ __global__ __launch_bounds__(512, 1) void sba_klgemm_kernel(
     tt = blockIdx.x;
   } else {
     const int pid = blockIdx.x;
-    const int xcd = pid & 7, q = pid >> 3;
-    c = xcd * NCX + (q % NCX);
-    tt = q / NCX;
+    const int xcd = pid & 7, q = pid >> 3;   // q < NCX * TT
+    const int cb = q / (CB * TT);            // chunk block; the last one may be narrower
+    const int rem = q - cb * CB * TT;
+    const int width = min(CB, NCX - cb * CB);
+    tt = rem / width;
+    c = xcd * NCX + cb * CB + rem % width;
     if (c >= c_last || tt >= TT) return;
   }
 
@@ -428,7 +440,7 @@ __global__ __launch_bounds__(512, 1) void sba_klgemm_kernel(
           const int tok = wt * 64 + tb * 32 + lane;
           const int64_t tg = tok0 + tok;
           if (tg < tb_len)
-            sq[((int64_t)r * NC + c) * tb_len + tg] = make_float4(0.0f, 0.0f, xq[0][tok].z + xq[1][tok].z, 0.0f);
+            sq[((int64_t)r * NC + c) * tb_len + tg] = make_float2(0.0f, xq[0][tok].z + xq[1][tok].z);
         }
       }
       return;
@@ -507,11 +519,13 @@ __global__ __launch_bounds__(512, 1) void sba_klgemm_kernel(
           const float2 p0 = xp[0][tok], p1 = xp[1][tok];
           const float M = fmaxf(p0.x, p1.x);
           const float a0 = __expf(p0.x - M), a1 = __expf(p1.x - M);
-          if (r == 0) sp[(int64_t)c * tb_len + tg] = make_float2(M, p0.y * a0 + p1.y * a1);
+          const float Z = p0.y * a0 + p1.y * a1;
+          if (r == 0) sp[(int64_t)c * tb_len + tg] = M + logf(Z);
           const float4 q0 = xq[0][tok], q1 = xq[1][tok];
           const float Mq = fmaxf(q0.x, q1.x);
           const float Zq = q0.y * __expf(q0.x - Mq) + q1.y * __expf(q1.x - Mq);
-          sq[((int64_t)r * NC + c) * tb_len + tg] = make_float4(Mq, Zq, q0.z * a0 + q1.z * a1, 0.0f);
+          // D = LSE(yhat) - LSE(y) over the chunk, E = S / Z = E_p[y - yhat] over the chunk
+          sq[((int64_t)r * NC + c) * tb_len + tg] = make_float2((Mq - M) + logf(Zq / Z), (q0.z * a0 + q1.z * a1) / Z);
         }
       }
     }
@@ -637,55 +651,60 @@ __global__ __launch_bounds__(512, 1) void sba_klgemm_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// Merge chunk statistics per token, KL_t in float64, per-block sums per step.
-__global__ __launch_bounds__(256) void sba_combine_kernel(const float2 *__restrict__ sp, const float4 *__restrict__ sq,
+// Chunk weights per token: w_c = e^{LSE_c(y) - LSE(y)}, the share of chunk c
+// in the softmax of y, written over the chunk LSEs (one thread per token).
+__global__ __launch_bounds__(256) void sba_weights_kernel(float *__restrict__ sp, int64_t tb, int NC) {
+  const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (t >= tb) return;
+  double M = -INFINITY;
+  for (int c = 0; c < NC; ++c) M = fmax(M, (double)sp[(int64_t)c * tb + t]);
+  double Z = 0.0;
+  for (int c = 0; c < NC; ++c) Z += exp((double)sp[(int64_t)c * tb + t] - M);
+  const double lse = M + log(Z);
+  for (int c = 0; c < NC; ++c) {
+    const int64_t i = (int64_t)c * tb + t;
+    sp[i] = (float)exp((double)sp[i] - lse);
+  }
+}
+
+// KL per (token, step) from the chunk statistics, then per-block sums per step.
+// With w_c the chunk weights, D_c = LSE_c(yhat) - LSE_c(y) and
+// E_c = E_p[y - yhat] over chunk c:
+//     KL_t = sum_c w_c E_c + ln sum_c w_c e^{D_c}
+// (= E_p[y - yhat] - LSE(y) + LSE(yhat)), in float64, with the float weights
+// renormalised by their float64 sum.  One thread per (token,
+// step): blockIdx.y is the step.  MSE: the chunks' squared-error sums add up.
+__global__ __launch_bounds__(256) void sba_combine_kernel(const float *__restrict__ w, const float2 *__restrict__ sq,
                                                           int64_t tb, int NC, int R, double *__restrict__ part,
                                                           int64_t blk_off, int mse) {
-  __shared__ double red[4][1032];
+  __shared__ double red[4];
   const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  const bool valid = t < tb;
+  const int r = blockIdx.y;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  float M = -INFINITY;
-  double Z = 0.0;
-  if (valid && !mse) {
-    for (int c = 0; c < NC; ++c) {
-      const float2 v = sp[(int64_t)c * tb + t];
-      if (v.x > M) {
-        Z = Z * (double)expf(M - v.x) + (double)v.y;
-        M = v.x;
-      } else {
-        Z += (double)v.y * (double)expf(v.x - M);
-      }
-    }
-  }
-  const double lse_p = (double)M + log(Z);
-  for (int r = 0; r < R; ++r) {
-    double kl = 0.0;
-    if (valid && mse) {            // squared output error: the chunks' partial sums add up
-      for (int c = 0; c < NC; ++c) kl += (double)sq[((int64_t)r * NC + c) * tb + t].z;
-    } else if (valid) {
-      float Mq = -INFINITY;
-      double Zq = 0.0, S = 0.0;
+  double kl = 0.0;
+  if (t < tb) {
+    const float2 *q = sq + (int64_t)r * NC * tb + t;
+    if (mse) {
+      for (int c = 0; c < NC; ++c) kl += (double)q[(int64_t)c * tb].y;
+    } else {
+      // normalised by the weights' own sum (1 up to their float rounding):
+      // where every D_c is 0, B and Wsum are the same sum and KL_t is 0 exactly
+      double A = 0.0, B = 0.0, Wsum = 0.0;
       for (int c = 0; c < NC; ++c) {
-        const float4 v = sq[((int64_t)r * NC + c) * tb + t];
-        const float mc = sp[(int64_t)c * tb + t].x;
-        S += (double)v.z * (double)expf(mc - M);
-        if (v.x > Mq) {
-          Zq = Zq * (double)expf(Mq - v.x) + (double)v.y;
-          Mq = v.x;
-        } else {
-          Zq += (double)v.y * (double)expf(v.x - Mq);
-        }
+        const float2 v = q[(int64_t)c * tb];
+        const double wc = (double)w[(int64_t)c * tb + t];
+        Wsum += wc;
+        A += wc * (double)v.y;
+        B += wc * exp((double)v.x);
       }
-      kl = S / Z - lse_p + ((double)Mq + log(Zq));
+      kl = A / Wsum + log(B / Wsum);
     }
-#pragma unroll
-    for (int d = 32; d > 0; d >>= 1) kl += __shfl_xor(kl, d, 64);
-    if (lane == 0) red[wave][r] = kl;
   }
+#pragma unroll
+  for (int d = 32; d > 0; d >>= 1) kl += __shfl_xor(kl, d, 64);
+  if (lane == 0) red[wave] = kl;
   __syncthreads();
-  for (int r = threadIdx.x; r < R; r += 256)
-    part[(blk_off + blockIdx.x) * R + r] = ((red[0][r] + red[1][r]) + red[2][r]) + red[3][r];
+  if (threadIdx.x == 0) part[(blk_off + blockIdx.x) * R + r] = ((red[0] + red[1]) + red[2]) + red[3];
 }
 
 // Mean over tokens, first argmin, bit-widths at r*.  Each step's block
@@ -740,14 +759,32 @@ __global__ __launch_bounds__(256) void sba_finalize_kernel(const double *__restr
 }
 
 // ---------------------------------------------------------------------------
-SbaPlan sba_plan(int64_t t, int64_t n, int64_t m, int group, bool bf16) {
+// Output chunks per block of an XCD's walk (see the launch mapping above):
+// four, measured against 1, 2, 8 and all of an XCD's chunks at the 4096 x
+// 4096, 13824 x 5120 and 28672 x 8192 layers.
+static int sba_chunk_block(int ncx) { return ncx < 4 ? (ncx > 0 ? ncx : 1) : 4; }
+
+SbaPlan sba_plan(int64_t t, int64_t n, int64_t m, int group, bool bf16, size_t ws_avail) {
   SbaPlan p;
   const int esz = bf16 ? 2 : 4;
   p.k = (int)(m / group);
   p.R = p.k / 2 + 1;
   p.nchunk = (int)((n + SBO - 1) / SBO);
-  const size_t per_tok = (size_t)p.nchunk * (8 + 16 * (size_t)p.R);
-  const size_t budget = (size_t)4 << 30;  // chunk statistics per batch (HBM is 288 GB)
+  // Parts that do not depend on the batch size: the trial weights, the order
+  // and the per-block partial sums (at most one partly filled block per
+  // batch, and at most one batch per token tile, so 2 ceil(t/256) blocks).
+  const size_t fixed = align_up((size_t)3 * n * m * esz, 256) + align_up((size_t)p.k * 4, 256) +
+                       align_up((size_t)2 * ((t + 255) / 256) * p.R * 8, 256);
+  // Chunk statistics per token: LSE(y) once, (D, E) per step.  A batch
+  // holds at most 4 GB of them (HBM is 288 GB), or what the caller's
+  // workspace leaves room for; the batch is a whole number of token tiles.
+  const size_t per_tok = (size_t)p.nchunk * (4 + 8 * (size_t)p.R);
+  size_t budget = (size_t)4 << 30;
+  if (ws_avail != (size_t)-1) {
+    const SbaPlan full = sba_plan(t, n, m, group, bf16);   // the size slim_sba_workspace() reports
+    if (ws_avail >= full.ws_bytes) return full;
+    budget = ws_avail > fixed + 1024 ? std::min(budget, ws_avail - fixed - 1024) : 0;
+  }
   int64_t cap = (int64_t)(budget / per_tok) / SBT * SBT;
   if (cap < SBT) cap = SBT;
   p.nbatch = (int)((t + cap - 1) / cap);
@@ -767,9 +804,9 @@ SbaPlan sba_plan(int64_t t, int64_t n, int64_t m, int group, bool bf16) {
   p.off_order = off;
   off += align_up((size_t)p.k * 4, 256);
   p.off_sp = off;
-  off += align_up((size_t)p.nchunk * tb * 8, 256);
+  off += align_up((size_t)p.nchunk * tb * 4, 256);
   p.off_sq = off;
-  off += align_up((size_t)p.R * p.nchunk * tb * 16, 256);
+  off += align_up((size_t)p.R * p.nchunk * tb * 8, 256);
   p.off_part = off;
   off += align_up((size_t)p.combine_blocks * p.R * 8, 256);
   p.ws_bytes = off;
@@ -783,8 +820,8 @@ hipError_t launch_sba(const void *X, const void *W, bool bf16, int64_t t, int64_
   void *Wv = base + p.off_wv;
   int *order = ext_order ? (int *)ext_order : (int *)(base + p.off_order);
   const int mse = objective == 1;
-  float2 *sp = (float2 *)(base + p.off_sp);
-  float4 *sq = (float4 *)(base + p.off_sq);
+  float *sp = (float *)(base + p.off_sp);
+  float2 *sq = (float2 *)(base + p.off_sq);
   double *part = (double *)(base + p.off_part);
 
   // trial weights
@@ -807,6 +844,7 @@ hipError_t launch_sba(const void *X, const void *W, bool bf16, int64_t t, int64_
   const int NC = p.nchunk;
   const int NCF = (int)(n / SBO);          // complete chunks
   const int NCX = (NCF + 7) / 8;
+  const int CB = sba_chunk_block(NCX);
   int64_t blk_off = 0;
   for (int b = 0; b < p.nbatch; ++b) {
     const int64_t t0 = (int64_t)b * p.tb;
@@ -817,22 +855,23 @@ hipError_t launch_sba(const void *X, const void *W, bool bf16, int64_t t, int64_
       const unsigned grid = (unsigned)(8 * NCX * TT);
       if (bf16)
         sba_klgemm_kernel<true, false><<<grid, 512, 0, st>>>(X, W, Wv, order, t0, len, n, m, group, p.k, p.R, NC, NCX,
-                                                             TT, NCF, sq, sp, mse);
+                                                             TT, NCF, CB, sq, sp, mse);
       else
         sba_klgemm_kernel<false, false><<<grid, 512, 0, st>>>(X, W, Wv, order, t0, len, n, m, group, p.k, p.R, NC,
-                                                              NCX, TT, NCF, sq, sp, mse);
+                                                              NCX, TT, NCF, CB, sq, sp, mse);
     }
     if (NC > NCF) {
       if (bf16)
         sba_klgemm_kernel<true, true><<<TT, 512, 0, st>>>(X, W, Wv, order, t0, len, n, m, group, p.k, p.R, NC, NCX, TT,
-                                                          NCF, sq, sp, mse);
+                                                          NCF, 1, sq, sp, mse);
       else
         sba_klgemm_kernel<false, true><<<TT, 512, 0, st>>>(X, W, Wv, order, t0, len, n, m, group, p.k, p.R, NC, NCX,
-                                                           TT, NCF, sq, sp, mse);
+                                                           TT, NCF, 1, sq, sp, mse);
     }
     timer_end(K_SBA_KLGEMM, st);
     const unsigned cb = (unsigned)((len + 255) / 256);
-    sba_combine_kernel<<<cb, 256, 0, st>>>(sp, sq, len, NC, p.R, part, blk_off, mse);
+    if (!mse) sba_weights_kernel<<<cb, 256, 0, st>>>(sp, len, NC);
+    sba_combine_kernel<<<dim3(cb, (unsigned)p.R), 256, 0, st>>>(sp, sq, len, NC, p.R, part, blk_off, mse);
     blk_off += cb;
     e = hipGetLastError();
     if (e != hipSuccess) return e;

@@ -18,10 +18,18 @@ at these sizes the HIP results are checked
   sizes 64 and 32, the 13B and 70B MLPs): Hessian and salience at full width
   from token slices, SQC on sampled rows, packing of the whole layer, the SBA
   scan on token slices, and the 70B layer's SBA at all 262144 tokens (token
-  batches of the statistics workspace) on the properties above.
+  batches of the statistics workspace) on the properties above;
+* against stored oracle results (tests/golden/sba_*.json, written by
+  tests/golden/make_sba_goldens.py from the oracle alone): the SBA scan of the
+  4096 x 4096 layer over all 262144 tokens, of the 28672 x 8192 MLP on its
+  last 256 tokens and on 2048 tokens run in several statistics batches (a
+  small workspace), and of the 13824 x 5120 MLP over 8192 tokens.
 
 Tolerances are those of the small-size parity tests.
 """
+import json
+import os
+
 import numpy as np
 import pytest
 
@@ -311,3 +319,73 @@ def test_shape_sba(slim, layer):
     np.testing.assert_allclose(kl, 0.5 * (kl_a + kl_b), rtol=1e-9, atol=0)
     del Xd, Wd
     torch.cuda.empty_cache()
+
+
+# -------------------------------------------------------------- stored oracle scans
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def _golden(name):
+    path = os.path.join(GOLDEN, f"sba_{name}.json")
+    if not os.path.exists(path):
+        pytest.skip(f"{path} not generated (python tests/golden/make_sba_goldens.py {name})")
+    with open(path) as f:
+        return json.load(f)
+
+
+def _check_against_golden(gold, bits, kl, rs):
+    """KL curve within 1e-3 relative; r* and bits exact unless the oracle's
+    best two KL values are a near tie (counted by the stored gap)."""
+    kl_o = np.asarray(gold["kl"], dtype=np.float64)
+    err = float(np.max(np.abs(kl - kl_o) / np.abs(kl_o)))
+    _say(f"  KL max rel err {err:.2e}; r* gpu {rs} oracle {gold['r_star']}; best-two gap {gold['best_two_rel_gap']:.2e}")
+    assert err <= 1e-3, (err, kl, kl_o)
+    S = np.asarray(gold["group_sal"], dtype=np.float64)
+    _check_sba_properties(bits, kl, rs, S, gold["avg_bits"])
+    if gold["best_two_rel_gap"] >= 1e-6:
+        assert rs == gold["r_star"]
+        np.testing.assert_array_equal(bits, np.asarray(gold["bits"]))
+    else:
+        _say("  near tie: r* not compared")
+
+
+def _golden_scan(slim, name, ws_tokens=None):
+    gold = _golden(name)
+    wl = synth.WORKLOADS[gold["workload"]]
+    idx = [l.name for l in wl.linears].index(gold["linear"])
+    t0, t1 = gold["tokens"]
+    _say(f"sba {gold['workload']}/{gold['linear']} {gold['n']}x{gold['m']} tokens [{t0}, {t1}) vs stored oracle scan"
+         + (f", workspace for {ws_tokens} tokens per batch" if ws_tokens else ""))
+    W = synth.make_w(wl, idx)
+    X = synth.make_x(wl, gold["m"], t0, t1)
+    Xd, Wd = dev(X, torch, True), dev(W, torch, True)
+    del X, W
+    ws = None
+    if ws_tokens:
+        lib = slim.load_library()
+        ws = lib.slim_sba_workspace(ws_tokens, gold["n"], gold["m"], gold["group"], 1)
+        assert 0 < ws < lib.slim_sba_workspace(t1 - t0, gold["n"], gold["m"], gold["group"], 1)
+    bits, kl, rs = slim.sba_search(Xd, Wd, torch.from_numpy(np.asarray(gold["group_sal"])).to("cuda:0"),
+                                   gold["group"], gold["avg_bits"], ws_bytes=ws)
+    _sync()
+    _check_against_golden(gold, host(bits).astype(int), host(kl), int(host(rs)[0]))
+    del Xd, Wd
+    torch.cuda.empty_cache()
+
+
+def test_golden_attn_sba_all_tokens(slim):
+    _golden_scan(slim, "attn-full")
+
+
+def test_golden_mlp70b_sba_last_tokens(slim):
+    _golden_scan(slim, "mlp70b-slice")
+
+
+def test_golden_mlp70b_sba_several_batches(slim):
+    # a workspace with room for 640 tokens of statistics: 2048 tokens run in
+    # four batches, the first boundary inside the range
+    _golden_scan(slim, "mlp70b-batches", ws_tokens=640)
+
+
+def test_golden_mlp13b_sba(slim):
+    _golden_scan(slim, "mlp13b-full-width")
