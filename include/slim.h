@@ -24,10 +24,11 @@
  *    workspace must be 16-byte aligned (SLIM_E_ALIGN otherwise).
  *  - The caller owns all memory.  The library allocates nothing and keeps no
  *    per-call state; scratch memory comes from a caller-provided workspace of
- *    at least the size the matching *_workspace() query returns.  One
- *    exception, stated where it is declared: the optional kernel timers
- *    (slim_timing_*), which keep process-wide state and create HIP events
- *    while timing is enabled.
+ *    at least the size the matching *_workspace() query returns.  Two
+ *    exceptions, both stated where they are declared: the optional kernel
+ *    timers (slim_timing_*), which keep process-wide state and create HIP
+ *    events while timing is enabled, and slim_qlinear_noalloc, whose scratch
+ *    is a fixed device array inside the library.
  *  - Every call enqueues its kernels on `stream` (a hipStream_t passed as
  *    void*, NULL = the default stream) and returns without synchronising.
  *  - Return value: SLIM_OK, or a negative SLIM_E_* code.  Arguments are
@@ -304,6 +305,33 @@ size_t slim_qlinear_workspace(int64_t t, int64_t n, int64_t m, int group);
 int slim_qlinear(const void *X, int xdt, int64_t t, int64_t m, const uint32_t *packed, const int8_t *bits,
                  int avg_bits, const float *scale, const float *zero, int64_t n, int group, float *Y, void *ws,
                  size_t ws_bytes, void *stream);
+
+/* ------------------------------------------------------------------------
+ * slim_qlinear without a workspace, for callers that cannot allocate device
+ * memory: code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc.
+ *
+ * Same arguments, computation and results as slim_qlinear (bit for bit: the
+ * same plan and kernels) without ws / ws_bytes.  The partial sums go to a
+ * device array of SLIM_NOALLOC_SCRATCH_BYTES (32 MiB) inside the library's
+ * code object, which every GPU the library runs on holds from module load
+ * until the process ends; the call itself allocates nothing and records no
+ * timing events.  Its device address is looked up on the first call on each
+ * device (with that device current).  A layer whose partial sums need more
+ * than the array (slim_qlinear_workspace(t, n, m, g) >
+ * SLIM_NOALLOC_SCRATCH_BYTES) gets SLIM_E_WORKSPACE before anything is
+ * enqueued.  Nothing in the array has to start at zero: every call writes the
+ * partial sums it reads.  The array is shared by all calls on one GPU and
+ * keeps the last call's contents: calls that overlap on one GPU (on
+ * different streams, or from host threads without ordering) race on it and
+ * their results are undefined, so order them on one stream.  The call runs on
+ * the current device; `stream` must belong to it.
+ * ---------------------------------------------------------------------- */
+#define SLIM_NOALLOC_SCRATCH_BYTES (32u << 20)
+size_t slim_qlinear_noalloc_scratch_bytes(void);
+int slim_qlinear_noalloc(const void *X, int xdt, int64_t t, int64_t m, const uint32_t *packed, const int8_t *bits,
+                         int avg_bits, const float *scale, const float *zero, int64_t n, int group, float *Y,
+                         void *stream);
 
 /* ------------------------------------------------------------------------
  * Kernel timing (instrumentation, not part of the method).  When enabled,

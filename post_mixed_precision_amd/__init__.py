@@ -11,15 +11,16 @@ hand-written HIP kernels:
                    (gptq_quantize: the same quantizer inside GPTQ's error-compensating sweep)
     pack           group-structured bit-planes                  (HBM)
     qlinear        Y = X W_hat^T read from the planes (decode-sized batches)
+                   (qlinear_noalloc: the same with no workspace, for callers that cannot allocate)
 
 ``quantize_layer`` chains them on the current stream.  PyTorch only provides
 device memory and the stream.
 """
-from ._lib import (SlimError, load_library, hessian, salience, sba_search, sba_search_ex, sqc_calibrate, gptq_quantize, pack, qlinear,
-                   tau_table,
+from ._lib import (SlimError, load_library, hessian, salience, sba_search, sba_search_ex, sqc_calibrate, gptq_quantize,
+                   pack, qlinear, qlinear_noalloc, tau_table,
                    timing_enable, timing_select, timing_reset, timing_read, SLIM_F32, SLIM_BF16)
 from .layer import quantize_layer
 
-__all__ = ["SlimError", "load_library", "hessian", "salience", "sba_search", "sba_search_ex", "sqc_calibrate", "gptq_quantize", "pack", "qlinear",
-           "tau_table", "timing_enable", "timing_select", "timing_reset", "timing_read", "quantize_layer", "SLIM_F32",
+__all__ = ["SlimError", "load_library", "hessian", "salience", "sba_search", "sba_search_ex", "sqc_calibrate",
+           "gptq_quantize", "pack", "qlinear", "qlinear_noalloc", "tau_table", "timing_enable", "timing_select", "timing_reset", "timing_read", "quantize_layer", "SLIM_F32",
            "SLIM_BF16"]

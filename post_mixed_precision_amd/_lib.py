@@ -50,6 +50,9 @@ _SIGS = {
     "slim_qlinear_workspace": (_c_sz, [_c_i64, _c_i64, _c_i64, _c_int]),
     "slim_qlinear": (_c_int, [_c_vp, _c_int, _c_i64, _c_i64, _c_vp, _c_vp, _c_int, _c_vp, _c_vp, _c_i64, _c_int,
                               _c_vp, _c_vp, _c_sz, _c_vp]),
+    "slim_qlinear_noalloc_scratch_bytes": (_c_sz, []),
+    "slim_qlinear_noalloc": (_c_int, [_c_vp, _c_int, _c_i64, _c_i64, _c_vp, _c_vp, _c_int, _c_vp, _c_vp, _c_i64,
+                                      _c_int, _c_vp, _c_vp]),
     "slim_timing_enable": (_c_int, [_c_int]),
     "slim_timing_select": (_c_int, [ctypes.c_char_p, _c_int]),
     "slim_timing_reset": (_c_int, []),
@@ -398,6 +401,34 @@ def qlinear(X, packed, bits, scale, zero, group: int, avg_bits: int):
     ws = _ws(lib.slim_qlinear_workspace(T, n, m, group), X.device)
     check(lib.slim_qlinear(_ptr(X), _dtype_code(X), T, m, _ptr(packed), _ptr(bits), int(avg_bits), _ptr(scale),
                            _ptr(zero), n, group, _ptr(Y), _ptr(ws), ws.numel(), _stream(X.device)), "slim_qlinear")
+    return Y
+
+
+def qlinear_noalloc(X, packed, bits, scale, zero, group: int, avg_bits: int, Y=None):
+    """slim_qlinear_noalloc: as qlinear, with the partial sums in the library's
+    fixed device scratch instead of a workspace.  Y (float32 [t, n] on the
+    GPU) may be given; then nothing at all is allocated for the call."""
+    torch = _torch()
+    lib = load_library()
+    X = _arg(X, "X", (None, None), _float_types())
+    T, m = X.shape
+    k = _group_count(m, group)
+    scale = _arg(scale, "scale", (None, k), (torch.float32,))
+    n = scale.shape[0]
+    zero = _arg(zero, "zero", (n, k), (torch.float32,))
+    bits = _arg(bits, "bits", (k,), (torch.int8,))
+    words = lib.slim_pack_words(n, m, avg_bits)
+    if words < 0:
+        raise SlimError("bad layer shape or average width")
+    packed = _arg(packed, "packed", (None,), (torch.int32,), min_numel=words)
+    if Y is not None:
+        Y = _arg(Y, "Y", (T, n), (torch.float32,))
+    _on_gpu(X, packed, bits, scale, zero, Y)
+    if Y is None:
+        Y = torch.empty((T, n), dtype=torch.float32, device=X.device)
+    check(lib.slim_qlinear_noalloc(_ptr(X), _dtype_code(X), T, m, _ptr(packed), _ptr(bits), int(avg_bits),
+                                   _ptr(scale), _ptr(zero), n, group, _ptr(Y), _stream(X.device)),
+          "slim_qlinear_noalloc")
     return Y
 
 
