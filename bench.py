@@ -89,7 +89,7 @@ def measured_traffic(workload: str, linear: str, group: int):
         return None
 
 
-def run_step(slim, X, W, group, N, ev=None, variant=None, gptq=False):
+def run_step(slim, X, W, group, N, ev=None, variant=None, gptq=False, lwc_iters=0):
     """One pass of the whole path; optional event list records stage boundaries."""
     def mark(i):
         if ev is not None:
@@ -111,6 +111,9 @@ def run_step(slim, X, W, group, N, ev=None, variant=None, gptq=False):
     mark(3)
     if gptq:   # the quantizer inside GPTQ's error-compensating sweep
         sq = slim.gptq_quantize(None, W, bits, hinv, group, 0.01, 0.1, 50, want_tau=False, U=U)
+    elif lwc_iters:   # SliM-LLM+: learnable weight clipping in place of SQC
+        sq = slim.lwc_calibrate(W, bits, H, X.shape[0], group, iters=lwc_iters)
+        run_step.lwc_loss = sq["loss"]
     else:
         sq = slim.sqc_calibrate(W, bits, hinv, group, 0.1, 50, want_tau=False)
     mark(4)
@@ -320,6 +323,8 @@ def main():
                     help="also run the scan once per objective/order and report r* and the best score")
     ap.add_argument("--gptq", action="store_true",
                     help="calibrate and quantize the groups inside GPTQ's error-compensating sweep")
+    ap.add_argument("--lwc", type=int, default=0, metavar="ITERS",
+                    help="SliM-LLM+: calibrate with learnable weight clipping (ITERS Adam steps) in place of SQC")
     ap.add_argument("--qlinear-shape", default=None,
                     help="NxM: time only the packed-plane linear layer on a synthetic N x M layer "
                          "(random planes, widths avg_bits +- 1) and print its own JSON line")
@@ -383,7 +388,7 @@ def main():
         variant = (args.objective, order)
 
     for i in range(args.warmup):
-        info, pinfo, rs, kl = run_step(slim, X, W, group, N, variant=variant, gptq=args.gptq)
+        info, pinfo, rs, kl = run_step(slim, X, W, group, N, variant=variant, gptq=args.gptq, lwc_iters=args.lwc)
         torch.cuda.synchronize()
         print(f"# warmup {i}: info={int(info.item())} r*={int(rs.item())}", file=sys.stderr, flush=True)
     assert int(info.item()) == 0 and int(pinfo.item()) == 0
@@ -400,7 +405,7 @@ def main():
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for s in range(args.steps):
-        run_step(slim, X, W, group, N, evs[s], variant=variant, gptq=args.gptq)
+        run_step(slim, X, W, group, N, evs[s], variant=variant, gptq=args.gptq, lwc_iters=args.lwc)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     slim.timing_enable(False)
@@ -416,6 +421,7 @@ def main():
     flops_per_launch = 6.0 * T * m * n / launches_per_step
     achieved = flops_per_launch / (ms_per_launch * 1e-3)
     hms, hl = slim.timing_read("hessian_gram")
+    lwc_ms, lwc_l = slim.timing_read("lwc_dh")
     qms, ql = slim.timing_read("sqc_calibrate")
     q_step = qms / args.steps
     pms, pl = slim.timing_read("pack_planes")
@@ -425,7 +431,7 @@ def main():
                "gptq_sweep", "gptq_trail"):
         slim.timing_select(nm, nm in per_panel)
     slim.timing_reset()
-    run_step(slim, X, W, group, N, variant=variant, gptq=args.gptq)
+    run_step(slim, X, W, group, N, variant=variant, gptq=args.gptq, lwc_iters=args.lwc)
     torch.cuda.synchronize()
     slim.timing_enable(False)
     if args.gptq:
@@ -446,7 +452,8 @@ def main():
         "config": {"workload": args.workload, "linear": lin.name, "n": n, "m": m, "tokens": T,
                    "group": group, "avg_bits": N, "tau_lambda": wl.tau_lambda, "tau_steps": wl.tau_steps,
                    "sba_objective": args.objective, "sba_order": args.order,
-                   "backbone": "gptq" if args.gptq else "none"},
+                   "backbone": "gptq" if args.gptq else "none",
+                   "calibration": f"lwc ({args.lwc} Adam steps)" if args.lwc else "sqc"},
         "roofline": {"bound": "mfma", "kernel": "sba_klgemm", "achieved": round(achieved / 1e12, 2),
                      "peak": PEAK_BF16_FLOPS / 1e12, "unit": "TFLOP/s",
                      "frac": round(achieved / PEAK_BF16_FLOPS, 4), "traffic": None,
@@ -469,20 +476,22 @@ def main():
     from post_mixed_precision_amd import _lib as _slim_lib
     out["library_built_from_tree"] = _slim_lib.library_is_current()
     hess_flops = T * m * (m + 1)
+    ro = out.setdefault("roofline_other", {})
     if hl:
-        out["roofline_other"] = {
-            "hessian_gram": {"bound": "mfma", "achieved_tflops": round(hess_flops / (hms / hl * 1e-3) / 1e12, 2),
-                             "frac": round(hess_flops / (hms / hl * 1e-3) / PEAK_BF16_FLOPS, 4)},
-            "sqc_calibrate": {
-                "bound": "alu", "unit": "lane-op/s", "peak": PEAK_VALU_LANE_OPS,
-                "lane_ops_per_param": SQC_LANE_OPS_PER_PARAM,
-                "achieved": round(n * m * SQC_LANE_OPS_PER_PARAM / (q_step * 1e-3), -9),
-                "frac": round(n * m * SQC_LANE_OPS_PER_PARAM / (q_step * 1e-3) / PEAK_VALU_LANE_OPS, 4),
-                "hbm_gbps": round(n * m * (2 + 1 + 0.125) / (q_step * 1e-3) / 1e9, 1),
-                "hbm_frac": round(n * m * (2 + 1 + 0.125) / (q_step * 1e-3) / PEAK_HBM_BPS, 4)},
-            "pack_planes": {"bound": "hbm", "bytes": n * m * (1 + N / 8), "achieved_gbps": round(n * m * (1 + N / 8) / (pms / pl * 1e-3) / 1e9, 1),
-                            "frac": round(n * m * (1 + N / 8) / (pms / pl * 1e-3) / PEAK_HBM_BPS, 4)},
-        }
+        ro["hessian_gram"] = {"bound": "mfma", "achieved_tflops": round(hess_flops / (hms / hl * 1e-3) / 1e12, 2),
+                              "frac": round(hess_flops / (hms / hl * 1e-3) / PEAK_BF16_FLOPS, 4)}
+    if ql and q_step > 0:
+        ro["sqc_calibrate"] = {
+            "bound": "alu", "unit": "lane-op/s", "peak": PEAK_VALU_LANE_OPS,
+            "lane_ops_per_param": SQC_LANE_OPS_PER_PARAM,
+            "achieved": round(n * m * SQC_LANE_OPS_PER_PARAM / (q_step * 1e-3), -9),
+            "frac": round(n * m * SQC_LANE_OPS_PER_PARAM / (q_step * 1e-3) / PEAK_VALU_LANE_OPS, 4),
+            "hbm_gbps": round(n * m * (2 + 1 + 0.125) / (q_step * 1e-3) / 1e9, 1),
+            "hbm_frac": round(n * m * (2 + 1 + 0.125) / (q_step * 1e-3) / PEAK_HBM_BPS, 4)}
+    if pl:
+        ro["pack_planes"] = {"bound": "hbm", "bytes": n * m * (1 + N / 8),
+                             "achieved_gbps": round(n * m * (1 + N / 8) / (pms / pl * 1e-3) / 1e9, 1),
+                             "frac": round(n * m * (1 + N / 8) / (pms / pl * 1e-3) / PEAK_HBM_BPS, 4)}
     # The quantized layer served from its own planes (the deployment side):
     # Y = X W_hat^T for decode batches, timed per call with HIP events around
     # its kernels; outside the step's timed region.
@@ -503,6 +512,16 @@ def main():
         tflops = n * m * (m - group) / (gtms * 1e-3) / 1e12 if gtl else 0.0
         out.setdefault("roofline_other", {})["gptq_trail"] = {"bound": "mfma", "achieved_tflops": round(tflops, 2),
                                                               "peak": 78.6, "frac": round(tflops / 78.6, 4)}
+    if args.lwc:
+        lms, ll = lwc_ms, lwc_l
+        f = 2.0 * n * m * m           # D H per iteration
+        out["kernels_ms_per_step"]["lwc_dh"] = round(lms / args.steps, 3)
+        if ll:
+            out.setdefault("roofline_other", {})["lwc_dh"] = {
+                "bound": "mfma", "dtype": "f64", "achieved_tflops": round(f / (lms / ll * 1e-3) / 1e12, 2),
+                "peak": 78.6, "frac": round(f / (lms / ll * 1e-3) / 78.6e12, 4)}
+        lo = run_step.lwc_loss.cpu().numpy()
+        out["lwc_output_mse"] = {"start": float(lo[0]), "end": float(lo[-1]), "iters": args.lwc}
     if args.ablation_report:
         # The pages' ablation structure on this layer: the scan under each
         # objective and group order (untimed; r* and the best score).

@@ -15,6 +15,7 @@
  *   slim_sqc_calibrate  3-sigma mask + tau-grid search of scale and zero       (component two)
  *   slim_gptq_quantize  the same quantizer inside GPTQ's error-compensating sweep  (core design: GPTQ backbone)
  *   slim_gptq_quantize_u  the same with that factor given (no second factorisation)
+ *   slim_lwc_calibrate  learnable weight clipping in place of SQC (SliM-LLM+)  (FAQ: GPTQ / AWQ / OmniQuant)
  *   slim_pack           group-structured bit-planes, no bitmap                (FAQ: storage)
  *   slim_qlinear        Y = X W_hat^T read from the planes (decode batches)    (FAQ: deployment)
  *
@@ -262,6 +263,37 @@ int slim_gptq_quantize_u(const double *U, int64_t m, const void *W, int wdt, int
                          size_t ws_bytes, void *stream);
 
 /* ------------------------------------------------------------------------
+ * SliM-LLM+: learnable weight clipping in place of SQC (rkmt.cn digest, FAQ
+ * on GPTQ / AWQ / OmniQuant: SliM-LLM+ replaces SQC with OmniQuant's
+ * learnable weight clipping; scime.ai summary, opening paragraph and "Key
+ * results": gradient-based calibration with SBA's widths).
+ *
+ * Per row segment (row i, group q, b = bits[q], maxq = 2^b - 1), two logits
+ * gamma, beta (start value `init`) clip the segment's range, float64:
+ *   hi = sigmoid(gamma) max(w), lo = sigmoid(beta) min(w),
+ *   s = (hi - lo)/maxq (1 if hi <= lo), z = -lo/s,
+ *   w_hat = (clamp(rint(w (1/s) + z), 0, maxq) - z) s.
+ * They are trained for `iters` full-batch Adam steps (beta1 0.9, beta2
+ * 0.999, eps 1e-8, learning rate lr) on the layer's output MSE over the
+ * t_tokens calibration tokens, L = tr((W - W_hat) H (W - W_hat)^T) / (2 t),
+ * through a straight-through rounding (no gradient where the clamp holds).
+ * H is the slim_hessian output for those tokens (float32 [m, m]).  Then the
+ * clipped range is rounded once to float32 and SQC's float32 min-max
+ * quantizer at tau = 1 gives scale, zero (float32 [n, k]) and codes (uint8
+ * [n, m]), which slim_pack and slim_qlinear take as they take SQC's.
+ * loss: float64 [iters + 1], L before each step and after the last;
+ * logits: float64 [2, n, k] (gamma, then beta) or NULL.  W: [n, m] in dtype
+ * wdt.  Requires 0 <= iters <= SLIM_LWC_MAX_ITERS, lr > 0.  Workspace:
+ * slim_lwc_workspace(n, m, g, iters) bytes (two float64 [n, m] matrices and
+ * per-segment state).
+ * ---------------------------------------------------------------------- */
+#define SLIM_LWC_MAX_ITERS 10000
+size_t slim_lwc_workspace(int64_t n, int64_t m, int group, int iters);
+int slim_lwc_calibrate(const void *W, int wdt, int64_t n, int64_t m, int group, const int8_t *bits, const float *H,
+                       int64_t t_tokens, int iters, double lr, double init, float *scale, float *zero,
+                       uint8_t *codes, double *logits, double *loss, void *ws, size_t ws_bytes, void *stream);
+
+/* ------------------------------------------------------------------------
  * Packing (FAQ on storage: group-wise bit-widths need no bitmap or codebook
  * and no extra storage; dequantization keeps the uniform-quantizer form).
  *
@@ -338,7 +370,8 @@ int slim_qlinear_noalloc(const void *X, int xdt, int64_t t, int64_t m, const uin
  * the library records a pair of HIP events on the launch stream around every
  * launch of the named kernels: "hessian_gram", "chol_update", "sba_klgemm",
  * "sqc_calibrate", "pack_planes", "qlinear" (its one or two kernels),
- * "gptq_sweep", "gptq_trail" (per group).
+ * "gptq_sweep", "gptq_trail" (per group), "lwc_dh" (the product D H of each
+ * learnable-clipping iteration).
  * slim_timing_read synchronises those events
  * and returns the summed milliseconds and the launch count since the last
  * reset.  Returns SLIM_E_PARAM for an unknown name.  slim_timing_enable(1)

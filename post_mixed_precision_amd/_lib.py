@@ -44,6 +44,9 @@ _SIGS = {
                                     _c_int, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_sz, _c_vp]),
     "slim_gptq_quantize_u": (_c_int, [_c_vp, _c_i64, _c_vp, _c_int, _c_i64, _c_int, _c_vp, _c_vp, _c_dbl, _c_int,
                                       _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_sz, _c_vp]),
+    "slim_lwc_workspace": (_c_sz, [_c_i64, _c_i64, _c_int, _c_int]),
+    "slim_lwc_calibrate": (_c_int, [_c_vp, _c_int, _c_i64, _c_i64, _c_int, _c_vp, _c_vp, _c_i64, _c_int, _c_dbl,
+                                    _c_dbl, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_sz, _c_vp]),
     "slim_tau_table": (_c_int, [_c_dbl, _c_int, _c_vp]),
     "slim_pack_words": (_c_i64, [_c_i64, _c_i64, _c_int]),
     "slim_pack": (_c_int, [_c_vp, _c_i64, _c_i64, _c_int, _c_vp, _c_int, _c_vp, _c_vp, _c_vp]),
@@ -359,6 +362,35 @@ def gptq_quantize(H, W, bits, hinv, group: int, damp_frac: float = 0.01, lam: fl
                                  _ptr(hinv), float(lam), int(n_tau), _ptr(out["scale"]), _ptr(out["zero"]),
                                  _ptr(out["codes"]), _ptr(out["mask"]), _ptr(out["tau_idx"]), _ptr(out["info"]),
                                  _ptr(ws), ws.numel(), _stream(dev)), "slim_gptq_quantize")
+    return out
+
+
+def lwc_calibrate(W, bits, H, tokens: int, group: int, iters: int = 20, lr: float = 1e-2, init: float = 4.0,
+                  want_logits: bool = False):
+    """SliM-LLM+ learnable weight clipping -> dict(scale, zero [n, k] f32; codes [n, m] u8;
+    loss f64 [iters+1]; logits f64 [2, n, k] or None).  H: the float32 Hessian of the
+    `tokens` calibration tokens (slim.hessian)."""
+    torch = _torch()
+    lib = load_library()
+    W = _arg(W, "W", (None, None), _float_types())
+    n, m = W.shape
+    k = _group_count(m, group)
+    bits = _arg(bits, "bits", (k,), (torch.int8,))
+    H = _arg(H, "H", (m, m), (torch.float32,))
+    _on_gpu(W, bits, H)
+    dev = W.device
+    out = {
+        "scale": torch.empty((n, k), dtype=torch.float32, device=dev),
+        "zero": torch.empty((n, k), dtype=torch.float32, device=dev),
+        "codes": torch.empty((n, m), dtype=torch.uint8, device=dev),
+        "loss": torch.empty(iters + 1, dtype=torch.float64, device=dev),
+        "logits": torch.empty((2, n, k), dtype=torch.float64, device=dev) if want_logits else None,
+    }
+    ws = _ws(lib.slim_lwc_workspace(n, m, group, iters), dev)
+    check(lib.slim_lwc_calibrate(_ptr(W), _dtype_code(W), n, m, group, _ptr(bits), _ptr(H), int(tokens), int(iters),
+                                 float(lr), float(init), _ptr(out["scale"]), _ptr(out["zero"]), _ptr(out["codes"]),
+                                 _ptr(out["logits"]), _ptr(out["loss"]), _ptr(ws), ws.numel(), _stream(dev)),
+          "slim_lwc_calibrate")
     return out
 
 

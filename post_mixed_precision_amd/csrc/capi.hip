@@ -35,7 +35,7 @@ bool g_timer_on = false;
 bool g_timer_sel[slim::K_NUM_TIMED];   // per kernel, set by slim_timing_select (all on with each enable)
 TimerSlot g_slots[slim::K_NUM_TIMED];
 const char *g_timer_names[slim::K_NUM_TIMED] = {"hessian_gram", "chol_update", "sba_klgemm", "sqc_calibrate",
-                                                "pack_planes", "qlinear", "gptq_sweep", "gptq_trail"};
+                                                "pack_planes", "qlinear", "gptq_sweep", "gptq_trail", "lwc_dh"};
 
 void drain(TimerSlot &s) {
   for (auto &pr : s.pending) {
@@ -281,6 +281,31 @@ int slim_pack(const uint8_t *codes, int64_t n, int64_t m, int group, const int8_
   if (!codes || !bits || !packed) return SLIM_E_NULL;
   if (!aligned16(codes) || !aligned16(packed)) return SLIM_E_ALIGN;
   hipError_t e = slim::launch_pack(codes, n, m, group, bits, avg_bits, packed, info, (hipStream_t)stream);
+  return e == hipSuccess ? SLIM_OK : hip_fail(e);
+}
+
+// ---------------------------------------------------------------- learnable weight clipping
+size_t slim_lwc_workspace(int64_t n, int64_t m, int group, int iters) {
+  if (n < 1 || m < 1 || m > SLIM_MAX_WIDTH || !valid_group(group) || m % group || iters < 0 || iters > SLIM_LWC_MAX_ITERS)
+    return 0;
+  return slim::lwc_plan(n, m, group, iters).ws_bytes;
+}
+
+int slim_lwc_calibrate(const void *W, int wdt, int64_t n, int64_t m, int group, const int8_t *bits, const float *H,
+                       int64_t t_tokens, int iters, double lr, double init, float *scale, float *zero,
+                       uint8_t *codes, double *logits, double *loss, void *ws, size_t ws_bytes, void *stream) {
+  if (!W || !bits || !H || !scale || !zero || !codes || !loss) return SLIM_E_NULL;
+  if (!valid_dtype(wdt)) return SLIM_E_DTYPE;
+  if (n < 1 || m < 1 || m > SLIM_MAX_WIDTH || t_tokens < 1) return SLIM_E_SHAPE;
+  if (!valid_group(group) || m % group) return SLIM_E_SHAPE;
+  if (iters < 0 || iters > SLIM_LWC_MAX_ITERS) return SLIM_E_PARAM;
+  if (!(lr > 0.0) || !isfinite(lr) || !isfinite(init)) return SLIM_E_PARAM;
+  if (!aligned16(W) || !aligned16(H)) return SLIM_E_ALIGN;
+  const slim::LwcPlan p = slim::lwc_plan(n, m, group, iters);
+  if (!ws || ws_bytes < p.ws_bytes) return SLIM_E_WORKSPACE;
+  if (!aligned16(ws)) return SLIM_E_ALIGN;
+  hipError_t e = slim::launch_lwc(W, wdt == SLIM_BF16, n, m, group, bits, H, (double)t_tokens, iters, lr, init, scale,
+                                  zero, codes, logits, loss, ws, p, (hipStream_t)stream);
   return e == hipSuccess ? SLIM_OK : hip_fail(e);
 }
 

@@ -11,7 +11,8 @@ namespace slim {
 void timer_begin(int kernel_id, hipStream_t st);
 void timer_end(int kernel_id, hipStream_t st);
 enum TimedKernel {
-  K_HESSIAN = 0, K_CHOL_UPDATE, K_SBA_KLGEMM, K_SQC, K_PACK, K_QLINEAR, K_GPTQ_SWEEP, K_GPTQ_TRAIL, K_NUM_TIMED
+  K_HESSIAN = 0, K_CHOL_UPDATE, K_SBA_KLGEMM, K_SQC, K_PACK, K_QLINEAR, K_GPTQ_SWEEP, K_GPTQ_TRAIL, K_LWC_DH,
+  K_NUM_TIMED
 };
 
 inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
@@ -75,6 +76,16 @@ hipError_t launch_gptq(const float *H, const double *Ugiven, int64_t m, double d
                        int64_t n, int group, const int8_t *bits, const float *hinv, const TauTable &tt, int n_tau,
                        float *scale, float *zero, uint8_t *codes, uint32_t *mask, uint8_t *tau_idx, int32_t *info,
                        void *ws, hipStream_t st);
+
+// ---- Learnable weight clipping (SliM-LLM+) ----
+struct LwcPlan {
+  int64_t nblk;              // per-segment kernel blocks (16 segments each)
+  size_t off_D, off_P, off_st, off_part, ws_bytes;
+};
+LwcPlan lwc_plan(int64_t n, int64_t m, int group, int iters);
+hipError_t launch_lwc(const void *W, bool bf16, int64_t n, int64_t m, int group, const int8_t *bits, const float *H,
+                      double T, int iters, double lr, double init, float *scale, float *zero, uint8_t *codes,
+                      double *logits, double *loss, void *ws, const LwcPlan &p, hipStream_t st);
 
 // ---- Pack ----
 hipError_t launch_pack(const uint8_t *codes, int64_t n, int64_t m, int group, const int8_t *bits,
