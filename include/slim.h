@@ -319,20 +319,21 @@ int slim_pack(const uint8_t *codes, int64_t n, int64_t m, int group, const int8_
  *
  * q is decoded from packed (the slim_pack layout, widths bits[k]); scale and
  * zero are the float32 [n, k] outputs of slim_sqc_calibrate.  X: [t, m] in
- * dtype xdt (bfloat16 or float32), t <= SLIM_QLINEAR_MAX_T (decode-sized
- * batches); Y: float32 [t, n].  Accumulation is float32; for a given t the
- * sum over groups runs in a fixed order (bitwise reproducible).  Up to two
- * tokens the codes are summed through nibble tables; from three on they are
- * expanded to bfloat16 integers for the matrix cores (float32 X as three
- * exact bfloat16 terms), so results for different t agree to float32
- * rounding, not bit for bit.  bits must
+ * dtype xdt (bfloat16 or float32), 1 <= t <= SLIM_QLINEAR_MAX_T (decode
+ * batches and prefill); Y: float32 [t, n].  Accumulation is float32; for a
+ * given t the sum over groups runs in a fixed order (bitwise reproducible).
+ * Up to two tokens the codes are summed through nibble tables; from three
+ * to eight they are expanded to bfloat16 integers for the matrix cores
+ * (float32 X as three exact bfloat16 terms); above eight a GEMM over the
+ * planes expands each code once per 128 tokens.  Results for different t
+ * agree to float32 rounding, not bit for bit.  bits must
  * hold widths in 1 .. 8 adding up to k * avg_bits, as slim_pack requires;
  * otherwise every output is NaN (checked before any plane is read).  Workspace:
  * slim_qlinear_workspace(t, n, m, g) bytes (partial sums over runs of
- * groups when the layer is split along its input; its contents on entry do
- * not matter).
+ * groups when the layer is split along its input, or the group sums of X for
+ * t > 8; its contents on entry do not matter).
  * ---------------------------------------------------------------------- */
-#define SLIM_QLINEAR_MAX_T 8
+#define SLIM_QLINEAR_MAX_T 65536
 size_t slim_qlinear_workspace(int64_t t, int64_t n, int64_t m, int group);
 int slim_qlinear(const void *X, int xdt, int64_t t, int64_t m, const uint32_t *packed, const int8_t *bits,
                  int avg_bits, const float *scale, const float *zero, int64_t n, int group, float *Y, void *ws,

@@ -414,7 +414,8 @@ def pack(codes, bits, group: int, avg_bits: int):
 
 
 def qlinear(X, packed, bits, scale, zero, group: int, avg_bits: int):
-    """Y = X W_hat^T from the packed planes: X [t, m] bf16/f32 (t <= 8) -> Y float32 [t, n]."""
+    """Y = X W_hat^T from the packed planes: X [t, m] bf16/f32 (decode batches or prefill,
+    t <= 65536) -> Y float32 [t, n]."""
     torch = _torch()
     lib = load_library()
     X = _arg(X, "X", (None, None), _float_types())

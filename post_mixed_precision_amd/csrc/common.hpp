@@ -82,4 +82,29 @@ __device__ __forceinline__ uint32_t group_or(uint32_t v) {
   return v;
 }
 
+// Sum over aligned groups of WIDTH (<= 32) lanes with ds_swizzle in its
+// bit-mask mode: each step reads lane i ^ d (d = 1, 2, 4, ...), the same
+// partners and association as the __shfl_xor butterfly of group_sum, so every
+// lane of a group ends with the bit-identical sum.  The swizzle runs on the
+// LDS unit beside the vector ALUs and needs no address register.  A double
+// moves as its two 32-bit halves.
+template <int D>
+__device__ __forceinline__ double swz_xor(double v) {
+  static_assert(D >= 1 && D < 32, "swizzle xor within 32 lanes");
+  constexpr int PAT = 0x1F | (D << 10);       // and 0x1f, or 0, xor D
+  const uint64_t u = __double_as_longlong(v);
+  const int lo = __builtin_amdgcn_ds_swizzle((int)(uint32_t)u, PAT);
+  const int hi = __builtin_amdgcn_ds_swizzle((int)(uint32_t)(u >> 32), PAT);
+  return __longlong_as_double((long long)(((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo));
+}
+template <int WIDTH>
+__device__ __forceinline__ double swz_group_sum(double v) {
+  static_assert(WIDTH == 4 || WIDTH == 8 || WIDTH == 16, "swizzle groups are 4, 8 or 16 lanes");
+  v += swz_xor<1>(v);
+  v += swz_xor<2>(v);
+  if (WIDTH >= 8) v += swz_xor<4>(v);
+  if (WIDTH >= 16) v += swz_xor<8>(v);
+  return v;
+}
+
 }  // namespace slim

@@ -361,6 +361,16 @@ QlinearPlan qlinear_plan(int t, int64_t n, int64_t m, int group) {
   QlinearPlan p;
   const int qt = ql_qt(t);
   p.k = (int)(m / group);
+  p.gemm = t > 16;  // prefill-sized batches: every code is expanded once per tile of tokens
+  if (p.gemm) {
+    p.mma = true;
+    p.nrb = (n + 127) / 128;
+    p.gpw = p.k;
+    p.nrun = 1;
+    p.lds_bytes = 0;
+    p.ws_bytes = align_up((size_t)t * p.k * sizeof(float), 256);
+    return p;
+  }
   p.mma = t >= 3;   // measured: the tables win up to two tokens, the matrix cores from three
   if (p.mma) {
     // 16 rows per wave, 64 per workgroup; runs of groups per wave, halved
@@ -401,6 +411,12 @@ static void ql_launch_g(dim3 grid, size_t lds, int group, const void *X, int t, 
 hipError_t launch_qlinear(const void *X, bool bf16, int t, int64_t m, const uint32_t *packed, const int8_t *bits,
                           int N, const float *scale, const float *zero, int64_t n, int group, float *Y, void *ws,
                           const QlinearPlan &p, hipStream_t st, bool timed) {
+  if (p.gemm) {
+    if (timed) timer_begin(K_QLINEAR, st);
+    launch_qlinear_gemm(X, bf16, t, m, packed, bits, N, scale, zero, n, group, p.k, (float *)ws, Y, st);
+    if (timed) timer_end(K_QLINEAR, st);
+    return hipGetLastError();
+  }
   float *out = p.nrun > 1 ? (float *)ws : Y;
   if (p.mma) {
     if (timed) timer_begin(K_QLINEAR, st);

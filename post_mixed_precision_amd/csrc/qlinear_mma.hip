@@ -1,5 +1,5 @@
 // Mixed-precision linear layer from the packed bit-planes, for batches of
-// 2 .. 8 tokens, on the matrix cores of gfx950.
+// 3 .. 16 tokens (and, further below, prefill batches), on the matrix cores of gfx950.
 //
 // "SliM-LLM" blog digest (rkmt.cn), FAQ on storage and deployment: the codes
 // are stored as plain integers per group (no bitmap or codebook) and the
@@ -40,6 +40,8 @@
 namespace slim {
 
 typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4_t;
+
+constexpr int QM_TOK = 16;   // token rows of the 16x16x32 MFMA: the batch the decode kernel takes
 
 __device__ __forceinline__ f32x4_t mfma16x32(uint4 a, uint4 b, f32x4_t c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, b),
@@ -132,7 +134,8 @@ __device__ __forceinline__ void qm_x(const void *__restrict__ Xv, int64_t idx, b
 // acc1 += X 1.
 template <int NP, int KS, int NT>
 __device__ __forceinline__ void qm_group(const uint32_t (&wc)[8], const uint4 *__restrict__ xl, int xstride,
-                                         int qbase, bool tok, int col, int sh, f32x4_t &acc, f32x4_t &acc1) {
+                                         int xrows, int qbase, bool tok, int col, int sh, f32x4_t &acc,
+                                         f32x4_t &acc1) {
   const uint4 ones = make_uint4(0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u);
 #pragma unroll
   for (int s = 0; s < KS; ++s) {
@@ -142,7 +145,7 @@ __device__ __forceinline__ void qm_group(const uint32_t (&wc)[8], const uint4 *_
     const uint4 bq = qm_codes<NP>(wd, sh);
 #pragma unroll
     for (int e = 0; e < NT; ++e) {
-      const uint4 xa = tok ? xl[e * 8 * xstride + qbase + 4 * s] : make_uint4(0u, 0u, 0u, 0u);
+      const uint4 xa = tok ? xl[e * xrows * xstride + qbase + 4 * s] : make_uint4(0u, 0u, 0u, 0u);
       acc = mfma16x32(xa, bq, acc);
       acc1 = mfma16x32(xa, ones, acc1);
     }
@@ -150,7 +153,7 @@ __device__ __forceinline__ void qm_group(const uint32_t (&wc)[8], const uint4 *_
 }
 
 template <bool XBF16, int G>
-__global__ __launch_bounds__(256) void qlinear_mma_kernel(const void *__restrict__ Xv, int t, int64_t m,
+__global__ __launch_bounds__(256) void qlinear_mma_kernel(const void *__restrict__ Xv, int t, int xrows, int64_t m,
                                                           const uint32_t *__restrict__ packed,
                                                           const int8_t *__restrict__ bits, int N,
                                                           const float *__restrict__ scale,
@@ -158,7 +161,7 @@ __global__ __launch_bounds__(256) void qlinear_mma_kernel(const void *__restrict
                                                           float *__restrict__ out) {
   constexpr int KS = G / 32;          // 32-column K slices per group = words per row and plane
   constexpr int NT = XBF16 ? 1 : 3;   // bfloat16 terms of X
-  // X of the run as bfloat16 terms: [term][token < 8][column / 8] (16-byte chunks)
+  // X of the run as bfloat16 terms: [term][token < 16][column / 8] (16-byte chunks)
   extern __shared__ uint4 qm_x_lds[];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane((int)(tid >> 6));
@@ -176,7 +179,7 @@ __global__ __launch_bounds__(256) void qlinear_mma_kernel(const void *__restrict
       uint4 xa[NT];
       qm_x<XBF16>(Xv, (int64_t)a * m + (int64_t)j0 * G + 8 * q, true, xa);
 #pragma unroll
-      for (int u = 0; u < NT; ++u) qm_x_lds[(u * 8 + a) * xstride + q] = xa[u];
+      for (int u = 0; u < NT; ++u) qm_x_lds[(u * xrows + a) * xstride + q] = xa[u];
     }
   }
   // Widths: all in 1..8 and summing to k N, else NaN outputs and no plane
@@ -217,14 +220,14 @@ __global__ __launch_bounds__(256) void qlinear_mma_kernel(const void *__restrict
       const int qbase = (tok ? col : 0) * xstride + (j - j0) * (G / 8) + quad;   // rows past the batch read as zero
       f32x4_t acc = {0.0f, 0.0f, 0.0f, 0.0f}, acc1 = {0.0f, 0.0f, 0.0f, 0.0f};
       switch (b) {
-        case 1: qm_group<1, KS, NT>(wc, qm_x_lds, xstride, qbase, tok, col, sh, acc, acc1); break;
-        case 2: qm_group<2, KS, NT>(wc, qm_x_lds, xstride, qbase, tok, col, sh, acc, acc1); break;
-        case 3: qm_group<3, KS, NT>(wc, qm_x_lds, xstride, qbase, tok, col, sh, acc, acc1); break;
-        case 4: qm_group<4, KS, NT>(wc, qm_x_lds, xstride, qbase, tok, col, sh, acc, acc1); break;
-        case 5: qm_group<5, KS, NT>(wc, qm_x_lds, xstride, qbase, tok, col, sh, acc, acc1); break;
-        case 6: qm_group<6, KS, NT>(wc, qm_x_lds, xstride, qbase, tok, col, sh, acc, acc1); break;
-        case 7: qm_group<7, KS, NT>(wc, qm_x_lds, xstride, qbase, tok, col, sh, acc, acc1); break;
-        default: qm_group<8, KS, NT>(wc, qm_x_lds, xstride, qbase, tok, col, sh, acc, acc1); break;
+        case 1: qm_group<1, KS, NT>(wc, qm_x_lds, xstride, xrows, qbase, tok, col, sh, acc, acc1); break;
+        case 2: qm_group<2, KS, NT>(wc, qm_x_lds, xstride, xrows, qbase, tok, col, sh, acc, acc1); break;
+        case 3: qm_group<3, KS, NT>(wc, qm_x_lds, xstride, xrows, qbase, tok, col, sh, acc, acc1); break;
+        case 4: qm_group<4, KS, NT>(wc, qm_x_lds, xstride, xrows, qbase, tok, col, sh, acc, acc1); break;
+        case 5: qm_group<5, KS, NT>(wc, qm_x_lds, xstride, xrows, qbase, tok, col, sh, acc, acc1); break;
+        case 6: qm_group<6, KS, NT>(wc, qm_x_lds, xstride, xrows, qbase, tok, col, sh, acc, acc1); break;
+        case 7: qm_group<7, KS, NT>(wc, qm_x_lds, xstride, xrows, qbase, tok, col, sh, acc, acc1); break;
+        default: qm_group<8, KS, NT>(wc, qm_x_lds, xstride, xrows, qbase, tok, col, sh, acc, acc1); break;
       }
       const float sc = live ? scale[i * k + j] : 0.0f;
       const float zp = live ? zero[i * k + j] : 0.0f;
@@ -262,13 +265,256 @@ __global__ __launch_bounds__(256) void qlinear_mma_kernel(const void *__restrict
   }
 }
 
+// ---------------------------------------------------------------------------
+// Prefill-sized batches (t > 16): a GEMM over the planes.
+//
+//   Y[a, i] = sum_j s[i, j] (P[a, i, j] - z[i, j] Xs[a, j])
+//
+// Workgroup tile: TOK tokens (256 for bfloat16 X, 128 for float32 X, whose
+// three bfloat16 terms triple the LDS tile) x 128 output rows; waves of
+// 64 x 64 (2 x 2 blocks of v_mfma_f32_32x32x16_bf16).  Per group j the
+// workgroup expands its rows' codes from the planes into bfloat16 integers in
+// LDS once (exact) and stages the group's X columns beside them; the matrix
+// cores then form P for the group over K = g, and the group's scale and zero
+// are applied to it in registers.  Each code is expanded once per TOK tokens.
+// The next group's plane words and X columns are loaded into registers while
+// the current group is multiplied, so their latency hides behind the MFMAs.
+// Xs (the group sums of X) comes from a small kernel ahead.
+constexpr int QG_OUT = 128;
+
+// Xs[a, j] = sum of X[a, c] over group j (float32), one thread per (token, group).
+template <bool XBF16>
+__global__ __launch_bounds__(256) void qlinear_xsum_kernel(const void *__restrict__ Xv, int64_t t, int64_t m, int g,
+                                                           int k, float *__restrict__ Xs) {
+  const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (e >= t * k) return;
+  const int64_t a = e / k, j = e % k;
+  float s = 0.0f;
+  if constexpr (XBF16) {
+    const uint4 *p = (const uint4 *)((const uint16_t *)Xv + a * m + j * g);
+    for (int q = 0; q < g / 8; ++q) {
+      const uint4 v = p[q];
+      const uint32_t u[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int h = 0; h < 4; ++h) s += __uint_as_float(u[h] << 16) + __uint_as_float(u[h] & 0xffff0000u);
+    }
+  } else {
+    const float4 *p = (const float4 *)((const float *)Xv + a * m + j * g);
+    for (int q = 0; q < g / 4; ++q) {
+      const float4 v = p[q];
+      s += (v.x + v.y) + (v.z + v.w);
+    }
+  }
+  Xs[e] = s;
+}
+
+template <bool XBF16>
+struct QgShape {
+  static constexpr int TOK = XBF16 ? 256 : 128;    // tokens per workgroup
+  static constexpr int NTH = 2 * TOK;              // threads: (TOK / 64) x 2 waves of 64 x 64
+};
+
+template <bool XBF16, int G>
+__global__ __launch_bounds__(QgShape<XBF16>::NTH, 1) void qlinear_gemm_kernel(
+    const void *__restrict__ Xv, int64_t t, int64_t m, const uint32_t *__restrict__ packed,
+    const int8_t *__restrict__ bits, int N, const float *__restrict__ scale, const float *__restrict__ zero,
+    int64_t n, int k, const float *__restrict__ Xs, float *__restrict__ Y) {
+  constexpr int TOK = QgShape<XBF16>::TOK, NTH = QgShape<XBF16>::NTH;
+  constexpr int NT = XBF16 ? 1 : 3;           // bfloat16 terms of X
+  constexpr int SLOTS = G / 8;                // 16-byte slots per tile row (8 bf16 each)
+  constexpr int SWZ = SLOTS < 8 ? SLOTS - 1 : 7;
+  constexpr int WPR = G / 32;                 // plane words per row and plane
+  constexpr int XPT = TOK * SLOTS / NTH;      // X slots each thread stages per group
+  constexpr int QIT = (QG_OUT * WPR + NTH - 1) / NTH;   // (row, word) code items per thread
+  static_assert(TOK * SLOTS % NTH == 0, "X slots divide over the threads");
+  // [term][token][slot] and [output row][slot], slot s of row r stored at s ^ (r & SWZ)
+  __shared__ uint4 xt[NT][TOK][SLOTS];
+  __shared__ uint4 qt[QG_OUT][SLOTS];
+  __shared__ float xs_s[TOK];
+  __shared__ int s_bad;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane((int)(tid >> 6));
+  const int wo = wave & 1, wt = wave >> 1;
+  const int64_t i0 = (int64_t)blockIdx.x * QG_OUT, a0 = (int64_t)blockIdx.y * TOK;
+  const int64_t pstride = n * WPR;            // words between planes of a group
+
+  // widths: all in 1..8 and summing to k N, else every output is NaN
+  if (tid < 64) {
+    int tot = 0, badw = 0;
+    for (int j = lane; j < k; j += 64) {
+      const int b = bits[j];
+      badw |= (b < 1) | (b > 8);
+      tot += b;
+    }
+#pragma unroll
+    for (int d = 32; d > 0; d >>= 1) {
+      tot += __shfl_xor(tot, d, 64);
+      badw |= __shfl_xor(badw, d, 64);
+    }
+    if (lane == 0) s_bad = badw || tot != k * N;
+  }
+  __syncthreads();
+  const bool ok = !s_bad;
+
+  // registers holding one group's operands until they go to LDS
+  uint4 xr[XPT][NT];
+  uint32_t wr[QIT][8];
+  float xsr = 0.0f;
+  auto fetch = [&](int j, int b, int64_t off) __attribute__((always_inline)) {
+#pragma unroll
+    for (int q = 0; q < XPT; ++q) {
+      const int e = tid + q * NTH;
+      const int r = e / SLOTS, sl = e % SLOTS;
+      const int64_t a = a0 + r;
+      qm_x<XBF16>(Xv, a * m + (int64_t)j * G + 8 * sl, a < t, xr[q]);
+    }
+#pragma unroll
+    for (int q = 0; q < QIT; ++q) {
+      const int e = tid + q * NTH;
+      const int r = e / WPR, w = e % WPR;
+      const int64_t i = i0 + r;
+      const bool live = e < QG_OUT * WPR && i < n;
+#pragma unroll
+      for (int p = 0; p < 8; ++p) wr[q][p] = (p < b && live) ? packed[off + (int64_t)p * pstride + i * WPR + w] : 0u;
+    }
+    if (tid < TOK) xsr = a0 + tid < t ? Xs[(a0 + tid) * k + j] : 0.0f;
+  };
+  auto stash = [&](int b) __attribute__((always_inline)) {
+#pragma unroll
+    for (int q = 0; q < XPT; ++q) {
+      const int e = tid + q * NTH;
+      const int r = e / SLOTS, sl = e % SLOTS;
+#pragma unroll
+      for (int u = 0; u < NT; ++u) xt[u][r][sl ^ (r & SWZ)] = xr[q][u];
+    }
+#pragma unroll
+    for (int q = 0; q < QIT; ++q) {
+      const int e = tid + q * NTH;
+      if (e >= QG_OUT * WPR) break;
+      const int r = e / WPR, w = e % WPR;
+#pragma unroll
+      for (int h = 0; h < 4; ++h) {
+        uint4 c;
+        switch (b) {
+          case 1: c = qm_codes<1>(*(const uint32_t(*)[1])wr[q], 8 * h); break;
+          case 2: c = qm_codes<2>(*(const uint32_t(*)[2])wr[q], 8 * h); break;
+          case 3: c = qm_codes<3>(*(const uint32_t(*)[3])wr[q], 8 * h); break;
+          case 4: c = qm_codes<4>(*(const uint32_t(*)[4])wr[q], 8 * h); break;
+          case 5: c = qm_codes<5>(*(const uint32_t(*)[5])wr[q], 8 * h); break;
+          case 6: c = qm_codes<6>(*(const uint32_t(*)[6])wr[q], 8 * h); break;
+          case 7: c = qm_codes<7>(*(const uint32_t(*)[7])wr[q], 8 * h); break;
+          default: c = qm_codes<8>(wr[q], 8 * h); break;
+        }
+        const int sl = 4 * w + h;
+        qt[r][sl ^ (r & SWZ)] = c;
+      }
+    }
+    if (tid < TOK) xs_s[tid] = xsr;
+  };
+
+  f32x16_t y[2][2];
+#pragma unroll
+  for (int tb = 0; tb < 2; ++tb)
+#pragma unroll
+    for (int ob = 0; ob < 2; ++ob)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) y[tb][ob][v] = ok ? 0.0f : __builtin_nanf("");
+  int64_t off = 0;                            // first word of group j
+  int b = ok ? __builtin_amdgcn_readfirstlane((int)bits[0]) : 0;
+  if (ok) fetch(0, b, off);
+  const int fr = lane & 31;
+  for (int j = 0; j < k && ok; ++j) {
+    if (j) __syncthreads();                   // the previous group's tiles are consumed
+    stash(b);
+    __syncthreads();
+    // the next group's operands go out now and land during this group's products
+    const int64_t off_n = off + (int64_t)b * pstride;
+    const int bn = j + 1 < k ? __builtin_amdgcn_readfirstlane((int)bits[j + 1]) : 0;
+    if (j + 1 < k) fetch(j + 1, bn, off_n);
+    // P for the group: K = G in steps of 16
+    f32x16_t acc[2][2];
+#pragma unroll
+    for (int tb = 0; tb < 2; ++tb)
+#pragma unroll
+      for (int ob = 0; ob < 2; ++ob)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) acc[tb][ob][v] = 0.0f;
+#pragma unroll
+    for (int kk = 0; kk < G / 16; ++kk) {
+      const int sl = 2 * kk + (lane >> 5);
+      uint4 bq[2];
+#pragma unroll
+      for (int ob = 0; ob < 2; ++ob) {
+        const int r = wo * 64 + ob * 32 + fr;
+        bq[ob] = qt[r][sl ^ (r & SWZ)];
+      }
+#pragma unroll
+      for (int u = 0; u < NT; ++u)
+#pragma unroll
+        for (int tb = 0; tb < 2; ++tb) {
+          const int r = wt * 64 + tb * 32 + fr;
+          const uint4 xa = xt[u][r][sl ^ (r & SWZ)];
+#pragma unroll
+          for (int ob = 0; ob < 2; ++ob) acc[tb][ob] = mfma_bf16(xa, bq[ob], acc[tb][ob]);
+        }
+    }
+    // y += s (P - z Xs) for the lane's output column of each block
+#pragma unroll
+    for (int ob = 0; ob < 2; ++ob) {
+      const int64_t i = i0 + wo * 64 + ob * 32 + fr;
+      const float sc = i < n ? scale[i * k + j] : 0.0f;
+      const float zp = i < n ? zero[i * k + j] : 0.0f;
+#pragma unroll
+      for (int tb = 0; tb < 2; ++tb)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const float xsv = xs_s[wt * 64 + tb * 32 + acc32_row(v, lane)];
+          y[tb][ob][v] = __builtin_fmaf(sc, __builtin_fmaf(-zp, xsv, acc[tb][ob][v]), y[tb][ob][v]);
+        }
+    }
+    off = off_n;
+    b = bn;
+  }
+#pragma unroll
+  for (int tb = 0; tb < 2; ++tb)
+#pragma unroll
+    for (int ob = 0; ob < 2; ++ob) {
+      const int64_t i = i0 + wo * 64 + ob * 32 + (lane & 31);
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int64_t a = a0 + wt * 64 + tb * 32 + acc32_row(v, lane);
+        if (a < t && i < n) Y[a * n + i] = y[tb][ob][v];
+      }
+    }
+}
+
+void launch_qlinear_gemm(const void *X, bool bf16, int64_t t, int64_t m, const uint32_t *packed, const int8_t *bits,
+                         int N, const float *scale, const float *zero, int64_t n, int group, int k, float *Xs,
+                         float *Y, hipStream_t st) {
+  const unsigned xb = (unsigned)((t * k + 255) / 256);
+  if (bf16) qlinear_xsum_kernel<true><<<xb, 256, 0, st>>>(X, t, m, group, k, Xs);
+  else qlinear_xsum_kernel<false><<<xb, 256, 0, st>>>(X, t, m, group, k, Xs);
+  const int tok = bf16 ? QgShape<true>::TOK : QgShape<false>::TOK;
+  const int nth = bf16 ? QgShape<true>::NTH : QgShape<false>::NTH;
+  const dim3 grid((unsigned)((n + QG_OUT - 1) / QG_OUT), (unsigned)((t + tok - 1) / tok));
+#define SLIM_QG(BF, G) \
+  qlinear_gemm_kernel<BF, G><<<grid, nth, 0, st>>>(X, t, m, packed, bits, N, scale, zero, n, k, Xs, Y)
+  switch (group) {
+    case 32: if (bf16) SLIM_QG(true, 32); else SLIM_QG(false, 32); break;
+    case 64: if (bf16) SLIM_QG(true, 64); else SLIM_QG(false, 64); break;
+    default: if (bf16) SLIM_QG(true, 128); else SLIM_QG(false, 128); break;
+  }
+#undef SLIM_QG
+}
+
 void launch_qlinear_mma(const void *X, bool bf16, int t, int64_t m, const uint32_t *packed, const int8_t *bits,
                         int N, const float *scale, const float *zero, int64_t n, int group, int k, int gpr, int nrun,
                         float *out, hipStream_t st) {
   const dim3 grid((unsigned)((n + 63) / 64), (unsigned)nrun);
-  const size_t lds = (size_t)(bf16 ? 1 : 3) * 8 * gpr * group * 2;   // X terms of a run, bfloat16
+  const int xrows = t <= 8 ? 8 : QM_TOK;   // token rows staged: no more LDS than the batch needs
+  const size_t lds = (size_t)(bf16 ? 1 : 3) * xrows * gpr * group * 2;   // X terms of a run, bfloat16
 #define SLIM_QM(BF, G) \
-  qlinear_mma_kernel<BF, G><<<grid, 256, lds, st>>>(X, t, m, packed, bits, N, scale, zero, n, k, gpr, out)
+  qlinear_mma_kernel<BF, G><<<grid, 256, lds, st>>>(X, t, xrows, m, packed, bits, N, scale, zero, n, k, gpr, out)
   switch (group) {
     case 32: if (bf16) SLIM_QM(true, 32); else SLIM_QM(false, 32); break;
     case 64: if (bf16) SLIM_QM(true, 64); else SLIM_QM(false, 64); break;

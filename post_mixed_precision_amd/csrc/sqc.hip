@@ -10,7 +10,10 @@
 //
 // One row segment (row i, group q: g weights) is held by g/8 lanes, 8 weights
 // per lane in registers, so a wave calibrates 64/(g/8) segments at once and
-// the per-candidate error needs only log2(g/8) butterfly steps.  The
+// the per-candidate error needs only log2(g/8) butterfly steps.  Inside the
+// 51-candidate loop they are ds_swizzle exchanges, which run on the LDS unit
+// beside the vector ALUs that bound this kernel (DPP moves would be more
+// VALU instructions; measured slower).  The
 // quantizer is the fixed float32 sequence (no contraction: the library is
 // built with -ffp-contract=off):
 //     r = 1/s;  t = w*r;  t = t + z;  q = clamp(rint(t), 0, maxq);  e = w - (q - z)*s
@@ -137,7 +140,7 @@ __global__ __launch_bounds__(256) void sqc_kernel(const void *__restrict__ W, in
       const double ed = (double)err;
       E += a[e] * (ed * ed);
     }
-    E = group_sum<LPS>(E);
+    E = swz_group_sum<LPS>(E);
     if (E < best) {
       best = E;
       best_i = ti;

@@ -162,12 +162,14 @@ def test_qlinear_validation(lib):
                                 kw.get("ws", 1 << 40), None)
     assert call(X=None) == -1
     assert call(xdt=3) == -3
-    assert call(t=0) == -2 and call(t=9) == -2
+    assert call(t=0) == -2 and call(t=65537) == -2   # above SLIM_QLINEAR_MAX_T
     assert call(m=96) == -2
     assert call(N=9) == -4
     assert call(ws=0) == -5
     assert lib.slim_qlinear_workspace(1, 4096, 4096, 128) > 0
-    assert lib.slim_qlinear_workspace(9, 4096, 4096, 128) == 0
+    assert lib.slim_qlinear_workspace(65537, 4096, 4096, 128) == 0
+    # prefill sizes: the group sums of X, t * k floats
+    assert lib.slim_qlinear_workspace(2048, 4096, 4096, 128) == 2048 * 32 * 4
 
 
 def test_gptq_validation(lib):

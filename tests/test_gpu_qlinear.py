@@ -1,5 +1,7 @@
 """Parity of the mixed-precision linear layer on the packed planes (slim_qlinear)
-with the oracle, through the C ABI.
+with the oracle, through the C ABI: decode batches (t <= 8: nibble tables and
+the small matrix-core kernel) and prefill batches (t > 8: the GEMM over the
+planes).
 
 Inputs are drawn by the test (codes per group width, scale, zero, X) or come
 from the oracle's calibration and packing; the oracle dequantizes and forms
@@ -78,6 +80,45 @@ def test_qlinear_parity(slim, t, n, m, g, N, dtype):
     bits, codes, scale, zero, packed = _layer(n + m, n, m, g, N)
     X = _x(t + m, t, m, dtype)
     _check(_run(slim, X, packed, bits, scale, zero, g, N, dtype), X, codes, bits, scale, zero, packed, n, m, g)
+
+
+@pytest.mark.parametrize("t,n,m,g,N,dtype", [
+    (9, 64, 256, 128, 4, "bf16"),      # the smallest prefill batch; widths 3..5
+    (16, 300, 512, 128, 2, "bf16"),    # ragged row tile
+    (129, 200, 256, 64, 3, "f32"),     # ragged token tile; float32 X as three bfloat16 terms
+    (300, 130, 384, 32, 2, "bf16"),    # one plane word per row segment
+    (40, 96, 256, 64, 7, "f32"),       # widths 6..8: the byte conversion of the codes
+    (512, 1024, 1024, 128, 2, "bf16"), # several tiles both ways
+])
+def test_qlinear_prefill_parity(slim, t, n, m, g, N, dtype):
+    # t > 8: the GEMM over the planes
+    print(f"qlinear prefill t={t} n={n} m={m} g={g} N={N} {dtype}", flush=True)
+    bits, codes, scale, zero, packed = _layer(n + m + t, n, m, g, N)
+    X = _x(t + 2 * m, t, m, dtype)
+    _check(_run(slim, X, packed, bits, scale, zero, g, N, dtype), X, codes, bits, scale, zero, packed, n, m, g)
+
+
+def test_qlinear_prefill_70b_sampled_rows(slim):
+    # the 70B-shaped MLP (28672 x 8192) at 256 tokens, sampled rows against the
+    # float64 product of the dequantized weights; and every row of the batch
+    # against the decode kernel's one-token result for that row
+    print("qlinear prefill 28672 x 8192, t = 256", flush=True)
+    bits, codes, scale, zero, packed = _layer(13, 28672, 8192, 128, 2)
+    X = _x(14, 256, 8192, "bf16")
+    Y = _run(slim, X, packed, bits, scale, zero, 128, 2, "bf16")
+    rows = np.concatenate([np.random.default_rng(6).choice(28672, 29, replace=False), [0, 28671]])
+    import synth
+    xf = synth.as_float(X).astype(np.float64)
+    q = codes[rows].astype(np.float32)
+    z = np.repeat(zero[rows], 128, axis=1)
+    sc = np.repeat(scale[rows], 128, axis=1)
+    Wh = ((q - z).astype(np.float32) * sc).astype(np.float32).astype(np.float64)
+    mag = np.abs(xf) @ ((q + np.abs(z)) * sc).astype(np.float64).T
+    err = np.abs(Y[:, rows].astype(np.float64) - xf @ Wh.T)
+    assert np.all(err <= 3e-5 * mag + 1e-30), float(np.max(err / (3e-5 * mag + 1e-30)))
+    for a in (0, 100, 255):
+        Y1 = _run(slim, X[a:a + 1], packed, bits, scale, zero, 128, 2, "bf16")
+        np.testing.assert_allclose(Y[a], Y1[0], rtol=1e-5, atol=1e-5 * float(np.abs(Y1).max()))
 
 
 def test_qlinear_on_calibrated_layer(slim):
