@@ -162,6 +162,12 @@ int slim_salience_u(const float *H, int64_t m, double damp_frac, const void *W, 
  * tokens are then split into more batches (same result up to float rounding
  * order inside each token's statistics, which do not depend on the batch);
  * below that the call returns SLIM_E_WORKSPACE.
+ *
+ * With bf16 operands, the KL objective, g = 64 or 128 and an even number of
+ * 64-column stages over m, the scan reduces a step's softmax statistics
+ * during the next step's matrix products; the results are bit-identical to
+ * the plain scan, which the environment variable SLIM_SBA_NO_OVERLAP (any
+ * value, read at each call) selects instead.
  * ---------------------------------------------------------------------- */
 size_t slim_sba_workspace(int64_t t, int64_t n, int64_t m, int group, int dtype);
 int slim_sba_search(const void *X, int xdt, int64_t t, const void *W, int wdt, int64_t n, int64_t m,

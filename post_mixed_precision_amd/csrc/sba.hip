@@ -42,6 +42,7 @@
 // fetched again for every token tile (at 28672 x 8192 one XCD's chunks hold
 // 224 MB of weights, far more than any cache level).
 #include <algorithm>
+#include <cstdlib>
 
 #include "common.hpp"
 #include "kernels.hpp"
@@ -168,7 +169,11 @@ __global__ __launch_bounds__(256) void sba_rank_kernel(const double *__restrict_
 // PARTIAL = false: launched over the complete 128-output chunks with the
 // XCD-aware id.  PARTIAL = true: one launch over token tiles for the last,
 // incomplete chunk `c_last` (n % 128 != 0); only it checks output rows.
-template <bool BF16, bool PARTIAL>
+// OVS = 2 or 4: the KL scan with token block 1's statistics overlapped with
+// the next step (bf16, OVS = 2g / 64 stages per step, an even number of
+// stages over m, at least one update step).  Each is an instance of its own:
+// the register allocation of one loop is then not shaped by the others.
+template <bool BF16, bool PARTIAL, int OVS>
 __global__ __launch_bounds__(512, 1) void sba_klgemm_kernel(
     const void *__restrict__ X, const void *__restrict__ W, const void *__restrict__ Wv,
     const int *__restrict__ order, int64_t tok_base, int64_t tb_len, int64_t n, int64_t m, int g, int k, int R,
@@ -415,6 +420,87 @@ __global__ __launch_bounds__(512, 1) void sba_klgemm_kernel(
   // relative to its own maxima; the halves are then merged through LDS:
   //   M = max(m0, m1), Z = sum_h z_h e^{m_h - M}, S = sum_h S_h e^{m_h - M}.
   float m_own[2] = {-INFINITY, -INFINITY}, sy_own[2] = {0.0f, 0.0f};
+  // Masked (PARTIAL) elements: output row ob*32 + acc32_row(v, lane) of the half must be below lim.
+  auto row_ok = [&](int ob, int v) __attribute__((always_inline)) {
+    const int lim = s_rows_ok - wo * 64 - 4 * (lane >> 5);
+    return !PARTIAL || ob * 32 + 8 * (v >> 2) + (v & 3) < lim;
+  };
+  // r = 0: softmax statistics of y over the wave's 64 outputs for token block
+  // tb; accY is replaced by e^(y - M) (zero for masked rows), the weights every
+  // later step reuses.  Returns the pair-summed Z; keeps M and sum e*y.
+  auto y_stats = [&](int tb) __attribute__((always_inline)) {
+    float mx = -INFINITY;
+#pragma unroll
+    for (int ob = 0; ob < 2; ++ob)
+#pragma unroll
+      for (int v = 0; v < 16; ++v)
+        if (row_ok(ob, v)) mx = fmaxf(mx, accY[ob * 2 + tb][v]);
+    mx = pair_max32(mx);
+    float z = 0.0f, sy = 0.0f;
+    const float mx2 = mx * 1.44269504088896341f;   // the same exp form as for yhat below
+#pragma unroll
+    for (int ob = 0; ob < 2; ++ob)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const float y = accY[ob * 2 + tb][v];
+        float e = 0.0f;
+        if (row_ok(ob, v)) e = __builtin_amdgcn_exp2f(__builtin_fmaf(y, 1.44269504088896341f, -mx2));
+        accY[ob * 2 + tb][v] = e;
+        z += e;
+        sy = __builtin_fmaf(e, y, sy);
+      }
+    z = pair_sum32(z);
+    sy = pair_sum32(sy);
+    m_own[tb] = mx;
+    sy_own[tb] = sy;
+    return z;
+  };
+  // Statistics of yhat for token block tb, from its two 32 x 32 blocks q0
+  // (outputs 0..31 of the half) and q1 (32..63): the pair max, then the sums
+  // e^(yhat - mq) and sum e^(y - M) yhat, in the order ob = 0, 1 and v = 0..15.
+  auto yh_max = [&](int tb, const f32x16_t &q0, const f32x16_t &q1) __attribute__((always_inline)) {
+    float mq = -INFINITY;
+#pragma unroll
+    for (int v = 0; v < 16; ++v)
+      if (row_ok(0, v)) mq = fmaxf(mq, q0[v]);
+#pragma unroll
+    for (int v = 0; v < 16; ++v)
+      if (row_ok(1, v)) mq = fmaxf(mq, q1[v]);
+    return pair_max32(mq);
+  };
+  // e^(yh - mq) as 2^(yh log2 e - mq log2 e): one fused multiply-add before v_exp
+  auto yh_sums = [&](int tb, int ob, const f32x16_t &q, float mq2, float &zq, float &se) __attribute__((always_inline)) {
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const float yh = q[v];
+      if (row_ok(ob, v)) zq += __builtin_amdgcn_exp2f(__builtin_fmaf(yh, 1.44269504088896341f, -mq2));
+      se = __builtin_fmaf(accY[ob * 2 + tb][v], yh, se);
+    }
+  };
+  // The half's (max, sum e^(yhat - max), S) row for each token of block tb.
+  auto yh_publish = [&](int tb, float mq, float zq, float se) __attribute__((always_inline)) {
+    zq = pair_sum32(zq);
+    se = pair_sum32(se);
+    if (lane < 32) xq[wo][wt * 64 + tb * 32 + lane] = make_float4(mq, zq, sy_own[tb] - se, 0.0f);
+  };
+  // Merge of the two halves for one token of block tb (lanes < 32 of the
+  // wo = 0 waves, after the halves' rows are visible): the chunk's LSE(y) at
+  // r = 0, and D = LSE(yhat) - LSE(y), E = S / Z = E_p[y - yhat] over the chunk.
+  auto merge_tok = [&](int tb, int r) __attribute__((always_inline)) {
+    const int tok = wt * 64 + tb * 32 + lane;
+    const int64_t tg = tok0 + tok;
+    if (tg < tb_len) {
+      const float2 p0 = xp[0][tok], p1 = xp[1][tok];
+      const float M = fmaxf(p0.x, p1.x);
+      const float a0 = __expf(p0.x - M), a1 = __expf(p1.x - M);
+      const float Z = p0.y * a0 + p1.y * a1;
+      if (r == 0) sp[(int64_t)c * tb_len + tg] = M + logf(Z);
+      const float4 q0 = xq[0][tok], q1 = xq[1][tok];
+      const float Mq = fmaxf(q0.x, q1.x);
+      const float Zq = q0.y * __expf(q0.x - Mq) + q1.y * __expf(q1.x - Mq);
+      sq[((int64_t)r * NC + c) * tb_len + tg] = make_float2((Mq - M) + logf(Zq / Z), (q0.z * a0 + q1.z * a1) / Z);
+    }
+  };
   auto epilogue = [&](int r) __attribute__((always_inline)) {
     // output row inside the half of accumulator element (ob, v): ob*32 + acc32_row(v, lane)
     const int lim = PARTIAL ? s_rows_ok - wo * 64 - 4 * (lane >> 5) : 64;
@@ -445,89 +531,25 @@ __global__ __launch_bounds__(512, 1) void sba_klgemm_kernel(
       }
       return;
     }
-    float pz[2] = {0.0f, 0.0f}, qm[2], qz[2], qs[2];
+    float pz[2] = {0.0f, 0.0f};
+    if (r == 0) {
+#pragma unroll
+      for (int tb = 0; tb < 2; ++tb) pz[tb] = y_stats(tb);
+    }
 #pragma unroll
     for (int tb = 0; tb < 2; ++tb) {
-      if (r == 0) {
-        float mx = -INFINITY;
-#pragma unroll
-        for (int ob = 0; ob < 2; ++ob)
-#pragma unroll
-          for (int v = 0; v < 16; ++v)
-            if (!PARTIAL || ob * 32 + 8 * (v >> 2) + (v & 3) < lim) mx = fmaxf(mx, accY[ob * 2 + tb][v]);
-        mx = pair_max32(mx);
-        float z = 0.0f, sy = 0.0f;
-        const float mx2 = mx * 1.44269504088896341f;   // the same exp form as for yhat below
-#pragma unroll
-        for (int ob = 0; ob < 2; ++ob)
-#pragma unroll
-          for (int v = 0; v < 16; ++v) {
-            const float y = accY[ob * 2 + tb][v];
-            float e = 0.0f;
-            if (!PARTIAL || ob * 32 + 8 * (v >> 2) + (v & 3) < lim)
-              e = __builtin_amdgcn_exp2f(__builtin_fmaf(y, 1.44269504088896341f, -mx2));
-            accY[ob * 2 + tb][v] = e;
-            z += e;
-            sy = __builtin_fmaf(e, y, sy);
-          }
-        z = pair_sum32(z);
-        sy = pair_sum32(sy);
-        m_own[tb] = mx;
-        sy_own[tb] = sy;
-        pz[tb] = z;
-      }
-      float mq = -INFINITY;
-#pragma unroll
-      for (int ob = 0; ob < 2; ++ob)
-#pragma unroll
-        for (int v = 0; v < 16; ++v)
-          if (!PARTIAL || ob * 32 + 8 * (v >> 2) + (v & 3) < lim) mq = fmaxf(mq, accQ[ob * 2 + tb][v]);
-      mq = pair_max32(mq);
-      float zq = 0.0f, se = 0.0f;
-      // e^(yh - mq) as 2^(yh log2 e - mq log2 e): one fused multiply-add before v_exp
+      const float mq = yh_max(tb, accQ[tb], accQ[2 + tb]);
       const float mq2 = mq * 1.44269504088896341f;
-#pragma unroll
-      for (int ob = 0; ob < 2; ++ob)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const float yh = accQ[ob * 2 + tb][v];
-          if (!PARTIAL || ob * 32 + 8 * (v >> 2) + (v & 3) < lim)
-            zq += __builtin_amdgcn_exp2f(__builtin_fmaf(yh, 1.44269504088896341f, -mq2));
-          se = __builtin_fmaf(accY[ob * 2 + tb][v], yh, se);
-        }
-      zq = pair_sum32(zq);
-      se = pair_sum32(se);
-      qm[tb] = mq;
-      qz[tb] = zq;
-      qs[tb] = sy_own[tb] - se;
-    }
-    if (lane < 32) {
-#pragma unroll
-      for (int tb = 0; tb < 2; ++tb) {
-        const int tok = wt * 64 + tb * 32 + lane;
-        xq[wo][tok] = make_float4(qm[tb], qz[tb], qs[tb], 0.0f);
-        if (r == 0) xp[wo][tok] = make_float2(m_own[tb], pz[tb]);
-      }
+      float zq = 0.0f, se = 0.0f;
+      yh_sums(tb, 0, accQ[tb], mq2, zq, se);
+      yh_sums(tb, 1, accQ[2 + tb], mq2, zq, se);
+      yh_publish(tb, mq, zq, se);
+      if (r == 0 && lane < 32) xp[wo][wt * 64 + tb * 32 + lane] = make_float2(m_own[tb], pz[tb]);
     }
     __syncthreads();
     if (wo == 0 && lane < 32) {
 #pragma unroll
-      for (int tb = 0; tb < 2; ++tb) {
-        const int tok = wt * 64 + tb * 32 + lane;
-        const int64_t tg = tok0 + tok;
-        if (tg < tb_len) {
-          const float2 p0 = xp[0][tok], p1 = xp[1][tok];
-          const float M = fmaxf(p0.x, p1.x);
-          const float a0 = __expf(p0.x - M), a1 = __expf(p1.x - M);
-          const float Z = p0.y * a0 + p1.y * a1;
-          if (r == 0) sp[(int64_t)c * tb_len + tg] = M + logf(Z);
-          const float4 q0 = xq[0][tok], q1 = xq[1][tok];
-          const float Mq = fmaxf(q0.x, q1.x);
-          const float Zq = q0.y * __expf(q0.x - Mq) + q1.y * __expf(q1.x - Mq);
-          // D = LSE(yhat) - LSE(y) over the chunk, E = S / Z = E_p[y - yhat] over the chunk
-          sq[((int64_t)r * NC + c) * tb_len + tg] = make_float2((Mq - M) + logf(Zq / Z), (q0.z * a0 + q1.z * a1) / Z);
-        }
-      }
+      for (int tb = 0; tb < 2; ++tb) merge_tok(tb, r);
     }
   };
 
@@ -629,6 +651,222 @@ __global__ __launch_bounds__(512, 1) void sba_klgemm_kernel(
   if (st < KM) {
     main_stage(st, lds0, lds1);
     ++st;
+  }
+  if constexpr (OVS != 0) {
+    // KL objective, stage pairs aligned (step r starts in lds0).  The yhat
+    // statistics of a step run among the next step's MFMAs instead of in
+    // lockstep between them; the arithmetic is the epilogue's, element for
+    // element, so the results are the plain scan's bit for bit.
+    //   token block 1: its accumulators are copied (the snapshot) after the
+    //     step's last products and reduced from the copy during the next step;
+    //   token block 0 (OVS = 4): the step's first and last stages run the two
+    //     token blocks' products one after the other, so block 0's max and
+    //     first half are taken while block 1's last products run and its
+    //     second half while block 1's first products of the next step run;
+    //     (OVS = 2: block 0 is reduced right after the step's last products);
+    //   the halves of both blocks are merged at the start of a later stage.
+    // A row written before a stage's closing barrier is read after it, and
+    // rewritten only after another barrier past that read.
+    //   OVS = 4: S0 = [block 1 products | block 0 second half, row],
+    //                 [block 0 products];
+    //            S1 = products | block 1 max and first half;
+    //            S2 = products | block 1 second half, row;
+    //            S3 = merges of both blocks, [block 0 products], [block 1
+    //                 products | block 0 max and first half], snapshot of block 1.
+    //   OVS = 2: S0 = block-0 merge, products | block 1 in full, row;
+    //            S1 = block-1 merge, products, block 0 in full, snapshot.
+    // (Merges and snapshots sit where the register budget allows: 256.)
+    f32x16_t snapA, snapB;   // token block 1 (outputs 0..31, 32..63 of the half) of the deferred step
+    auto snap1 = [&]() __attribute__((always_inline)) {
+      snapA = accQ[1];
+      snapB = accQ[3];
+    };
+    auto block0 = [&]() __attribute__((always_inline)) {
+      const float mq = yh_max(0, accQ[0], accQ[2]);
+      const float mq2 = mq * 1.44269504088896341f;
+      float zq = 0.0f, se = 0.0f;
+      yh_sums(0, 0, accQ[0], mq2, zq, se);
+      yh_sums(0, 1, accQ[2], mq2, zq, se);
+      yh_publish(0, mq, zq, se);
+    };
+    float d0mq = 0.0f, d0mq2 = 0.0f, d0zq = 0.0f, d0se = 0.0f;   // token block 0, in progress
+    auto b0_first = [&]() __attribute__((always_inline)) {
+      d0mq = yh_max(0, accQ[0], accQ[2]);
+      d0mq2 = d0mq * 1.44269504088896341f;
+      d0zq = 0.0f;
+      d0se = 0.0f;
+      yh_sums(0, 0, accQ[0], d0mq2, d0zq, d0se);
+    };
+    auto b0_second = [&]() __attribute__((always_inline)) {
+      yh_sums(0, 1, accQ[2], d0mq2, d0zq, d0se);
+      yh_publish(0, d0mq, d0zq, d0se);
+    };
+    float dmq = 0.0f, dmq2 = 0.0f, dzq = 0.0f, dse = 0.0f;   // token block 1, in progress
+    auto b1_first = [&]() __attribute__((always_inline)) {
+      dmq = yh_max(1, snapA, snapB);
+      dmq2 = dmq * 1.44269504088896341f;
+      dzq = 0.0f;
+      dse = 0.0f;
+      yh_sums(1, 0, snapA, dmq2, dzq, dse);
+    };
+    auto b1_second = [&]() __attribute__((always_inline)) {
+      yh_sums(1, 1, snapB, dmq2, dzq, dse);
+      yh_publish(1, dmq, dzq, dse);
+    };
+    auto nothing = [&]() __attribute__((always_inline)) {};
+    // The next stage's DMA: after the last step this loads step R's first
+    // stage, which nothing reads; s_order[R - 1] and s_order[k - R] are still
+    // in range (R = k/2 + 1).
+    auto issue_next = [&](unsigned char *nxt, int nr, int nsub) __attribute__((always_inline)) {
+      unsigned char *dst = nxt + lds_row0 * SBP;
+      const int c0 = nsub * KT;
+      const int gu = s_order[nr - 1], gd = s_order[k - nr];
+      const uint32_t vup = kind == 0 ? 2u * vstride : (kind == 1 ? vstride : 0u);
+      const uint32_t vdn = kind == 1 ? vstride : 0u;
+      const uint32_t so = __builtin_amdgcn_readfirstlane(c0 < g ? vup + (uint32_t)((gu * g + c0) * ESZ)
+                                                                : vdn + (uint32_t)((gd * g + c0 - g) * ESZ));
+#pragma unroll
+      for (int q = 0; q < 8; ++q)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rUpd, (lds_void_t *)(dst + q * 8 * SBP), 16, (int)voff[q], (int)so,
+                                                 0, 0);
+    };
+    auto advance = [&](int &nr, int &nsub) __attribute__((always_inline)) {
+      nr = cr;
+      nsub = csub + 1;
+      if (nsub == SPR) {
+        nsub = 0;
+        ++nr;
+      }
+    };
+    // One update stage: the next stage's DMA, this stage's MFMAs, then `work`
+    // (registers and the LDS rows only, never the stage buffers).
+    auto ov_stage = [&](const unsigned char *cur, unsigned char *nxt, auto &&work) __attribute__((always_inline)) {
+      int nr, nsub;
+      advance(nr, nsub);
+      issue_next(nxt, nr, nsub);
+      compute_update(cur);
+      work();
+      pin_first_k_step();
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+      cr = nr;
+      csub = nsub;
+    };
+    // The products of one token block tb over a stage (both output blocks,
+    // K steps in order): a block's own accumulation order is the plain
+    // stage's, whichever block goes first.  The fragment offset passes through
+    // an empty asm statement (no instruction), so the two passes of a split
+    // stage read their weight fragments each for themselves instead of the
+    // second keeping the first's 64 registers alive.
+    auto update_pass = [&](const unsigned char *L, int tb) __attribute__((always_inline)) {
+      const unsigned char *Bt = L + (2 * SBO + wt * 64 + tb * 32 + (lane & 31)) * SBP;
+      const unsigned char *A0 = L + (wo * 64 + (lane & 31)) * SBP;
+      const unsigned char *A1 = L + (SBO + wo * 64 + (lane & 31)) * SBP;
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) {
+        int off = ((2 * kk + (lane >> 5)) ^ sw) * 16;
+        asm volatile("" : "+v"(off));
+        const uint4 b = *(const uint4 *)(Bt + off);
+        uint4 a0[2], a1[2];
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+          a0[i] = *(const uint4 *)(A0 + i * 32 * SBP + off);
+          a1[i] = *(const uint4 *)(A1 + i * 32 * SBP + off);
+          a1[i].x ^= 0x80008000u; a1[i].y ^= 0x80008000u; a1[i].z ^= 0x80008000u; a1[i].w ^= 0x80008000u;
+        }
+#pragma unroll
+        for (int ob = 0; ob < 2; ++ob) {
+          accQ[ob * 2 + tb] = mfma_bf16(a0[ob], b, accQ[ob * 2 + tb]);
+          accQ[ob * 2 + tb] = mfma_bf16(a1[ob], b, accQ[ob * 2 + tb]);
+        }
+      }
+    };
+    // Split stage: token block `first` over all K steps, then the other one;
+    // workA among the first pass, workB among the second; the next stage's DMA
+    // goes out among the first four products.
+    auto ov_split_stage = [&](const unsigned char *cur, unsigned char *nxt, int first, auto &&workA,
+                              auto &&workB) __attribute__((always_inline)) {
+      int nr, nsub;
+      advance(nr, nsub);
+      issue_next(nxt, nr, nsub);
+      update_pass(cur, first);
+      workA();
+      __builtin_amdgcn_sched_group_barrier(0x100, 5, 0);
+      for (int j = 0; j < 4; ++j) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x020, 2, 0);
+      }
+      for (int j = 0; j < 3; ++j) {
+        __builtin_amdgcn_sched_group_barrier(0x100, 5, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+      }
+      __builtin_amdgcn_sched_barrier(0);   // the first block's products all come first
+      update_pass(cur, 1 - first);
+      workB();
+      for (int j = 0; j < 4; ++j) {
+        __builtin_amdgcn_sched_group_barrier(0x100, 5, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+      }
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+      cr = nr;
+      csub = nsub;
+    };
+
+    // step 0: y statistics of both token blocks, then what is due of yhat's
+    float2 pz01;
+    pz01.x = y_stats(0);
+    pz01.y = y_stats(1);
+    if (lane < 32) {
+      xp[wo][wt * 64 + lane] = make_float2(m_own[0], pz01.x);
+      xp[wo][wt * 64 + 32 + lane] = make_float2(m_own[1], pz01.y);
+    }
+    if constexpr (OVS == 4)
+      b0_first();
+    else
+      block0();
+    snap1();
+    __syncthreads();
+    cr = 1;
+    csub = 0;
+    if constexpr (OVS == 4) {
+      for (int r = 1; r < R; ++r) {
+        ov_split_stage(lds0, lds1, 1, b0_second, nothing);
+        ov_stage(lds1, lds0, b1_first);
+        ov_stage(lds0, lds1, b1_second);
+        if (wo == 0 && lane < 32) merge_tok(0, r - 1);
+        if (wo == 1 && lane < 32) merge_tok(1, r - 1);
+        ov_split_stage(lds1, lds0, 0, nothing, [&]() __attribute__((always_inline)) {
+          b0_first();
+          snap1();
+        });
+      }
+      b0_second();
+      b1_first();
+      b1_second();
+      __syncthreads();
+      if (wo == 0 && lane < 32) merge_tok(0, R - 1);
+      if (wo == 1 && lane < 32) merge_tok(1, R - 1);
+    } else {
+      for (int r = 1; r < R; ++r) {
+        if (wo == 0 && lane < 32) merge_tok(0, r - 1);
+        ov_stage(lds0, lds1, [&]() __attribute__((always_inline)) {
+          b1_first();
+          b1_second();
+        });
+        if (wo == 1 && lane < 32) merge_tok(1, r - 1);
+        ov_stage(lds1, lds0, [&]() __attribute__((always_inline)) {
+          block0();
+          snap1();
+        });
+      }
+      if (wo == 0 && lane < 32) merge_tok(0, R - 1);
+      b1_first();
+      b1_second();
+      __syncthreads();
+      if (wo == 1 && lane < 32) merge_tok(1, R - 1);
+    }
+    return;
   }
   epilogue(0);
   if (st < total && (st & 1)) {
@@ -843,6 +1081,10 @@ hipError_t launch_sba(const void *X, const void *W, bool bf16, int64_t t, int64_
 
   const int NC = p.nchunk;
   const int NCF = (int)(n / SBO);          // complete chunks
+  // the overlapped KL scan (see the kernel): bf16, 64-column stages within
+  // a group, an even number of them over m, and at least one update step
+  const bool ov = bf16 && !mse && (group == 64 || group == 128) && ((m + 63) / 64) % 2 == 0 && p.R >= 2 &&
+                  std::getenv("SLIM_SBA_NO_OVERLAP") == nullptr;
   const int NCX = (NCF + 7) / 8;
   const int CB = sba_chunk_block(NCX);
   int64_t blk_off = 0;
@@ -853,20 +1095,32 @@ hipError_t launch_sba(const void *X, const void *W, bool bf16, int64_t t, int64_
     timer_begin(K_SBA_KLGEMM, st);
     if (NCF > 0) {
       const unsigned grid = (unsigned)(8 * NCX * TT);
-      if (bf16)
-        sba_klgemm_kernel<true, false><<<grid, 512, 0, st>>>(X, W, Wv, order, t0, len, n, m, group, p.k, p.R, NC, NCX,
-                                                             TT, NCF, CB, sq, sp, mse);
+      if (ov && group == 128)
+        sba_klgemm_kernel<true, false, 4><<<grid, 512, 0, st>>>(X, W, Wv, order, t0, len, n, m, group, p.k, p.R, NC,
+                                                                NCX, TT, NCF, CB, sq, sp, mse);
+      else if (ov)
+        sba_klgemm_kernel<true, false, 2><<<grid, 512, 0, st>>>(X, W, Wv, order, t0, len, n, m, group, p.k, p.R, NC,
+                                                                NCX, TT, NCF, CB, sq, sp, mse);
+      else if (bf16)
+        sba_klgemm_kernel<true, false, 0><<<grid, 512, 0, st>>>(X, W, Wv, order, t0, len, n, m, group, p.k, p.R,
+                                                                    NC, NCX, TT, NCF, CB, sq, sp, mse);
       else
-        sba_klgemm_kernel<false, false><<<grid, 512, 0, st>>>(X, W, Wv, order, t0, len, n, m, group, p.k, p.R, NC,
-                                                              NCX, TT, NCF, CB, sq, sp, mse);
+        sba_klgemm_kernel<false, false, 0><<<grid, 512, 0, st>>>(X, W, Wv, order, t0, len, n, m, group, p.k, p.R,
+                                                                     NC, NCX, TT, NCF, CB, sq, sp, mse);
     }
     if (NC > NCF) {
-      if (bf16)
-        sba_klgemm_kernel<true, true><<<TT, 512, 0, st>>>(X, W, Wv, order, t0, len, n, m, group, p.k, p.R, NC, NCX, TT,
-                                                          NCF, 1, sq, sp, mse);
+      if (ov && group == 128)
+        sba_klgemm_kernel<true, true, 4><<<TT, 512, 0, st>>>(X, W, Wv, order, t0, len, n, m, group, p.k, p.R, NC, NCX,
+                                                             TT, NCF, 1, sq, sp, mse);
+      else if (ov)
+        sba_klgemm_kernel<true, true, 2><<<TT, 512, 0, st>>>(X, W, Wv, order, t0, len, n, m, group, p.k, p.R, NC, NCX,
+                                                             TT, NCF, 1, sq, sp, mse);
+      else if (bf16)
+        sba_klgemm_kernel<true, true, 0><<<TT, 512, 0, st>>>(X, W, Wv, order, t0, len, n, m, group, p.k, p.R, NC,
+                                                                 NCX, TT, NCF, 1, sq, sp, mse);
       else
-        sba_klgemm_kernel<false, true><<<TT, 512, 0, st>>>(X, W, Wv, order, t0, len, n, m, group, p.k, p.R, NC, NCX,
-                                                           TT, NCF, 1, sq, sp, mse);
+        sba_klgemm_kernel<false, true, 0><<<TT, 512, 0, st>>>(X, W, Wv, order, t0, len, n, m, group, p.k, p.R, NC,
+                                                                  NCX, TT, NCF, 1, sq, sp, mse);
     }
     timer_end(K_SBA_KLGEMM, st);
     const unsigned cb = (unsigned)((len + 255) / 256);

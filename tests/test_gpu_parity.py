@@ -159,6 +159,38 @@ def test_sba_parity(slim, T, n, m, g, N, dtype):
     _sba_check(slim, X, W, S, g, N, dtype)
 
 
+@pytest.mark.parametrize("T,n,m,g,N", [
+    (700, 256, 512, 128, 2),    # four stages per step, several chunks
+    (513, 200, 256, 64, 2),     # two stages per step, partial output chunk
+    (1000, 300, 1024, 128, 2),  # partial chunk with four stages per step, k = 8
+    (777, 384, 768, 64, 3),     # g = 64, k = 12, avg 3 bits
+    (256, 128, 256, 128, 2),    # k = 2: a single update step
+])
+def test_sba_overlapped_equals_plain(slim, T, n, m, g, N, monkeypatch):
+    # The bf16 KL scan computes token block 1's statistics one step late,
+    # among the next step's matrix products; the arithmetic per element is the
+    # plain scan's, so both give the same bits (SLIM_SBA_NO_OVERLAP selects the
+    # plain scan at launch).
+    print(f"sba overlap T={T} n={n} m={m} g={g} N={N}", flush=True)
+    wl, X, W = _case_inputs(T, n, m, "bf16", dist="t5", wid=57, avg_bits=N)
+    _, S, _ = oracle.salience(oracle.hessian(X), W, g)
+    Xd, Wd = dev(X, torch, True), dev(W, torch, True)
+    Sd = torch.from_numpy(np.asarray(S, dtype=np.float64)).to("cuda:0")
+    out = []
+    for plain in (False, True):
+        if plain:
+            monkeypatch.setenv("SLIM_SBA_NO_OVERLAP", "1")
+        else:
+            monkeypatch.delenv("SLIM_SBA_NO_OVERLAP", raising=False)
+        bits, kl, rs = slim.sba_search(Xd, Wd, Sd, g, N)
+        _sync()
+        out.append((host(bits), host(kl), int(host(rs)[0])))
+    np.testing.assert_array_equal(out[0][1].view(np.uint64), out[1][1].view(np.uint64))
+    np.testing.assert_array_equal(out[0][0], out[1][0])
+    assert out[0][2] == out[1][2]
+    _sba_check(slim, X, W, S, g, N, "bf16")
+
+
 def test_sba_parity_tiny_layer(slim):
     wl = synth.WORKLOADS["tiny-512"]
     X, W = synth.make_x(wl, 512), synth.make_w(wl, 0)
