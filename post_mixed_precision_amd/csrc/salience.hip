@@ -12,15 +12,26 @@
 // substitution L Z = I: when panel p is factored, its rows of Z = L^-1 become
 // final (Z_p = L_pp^-1 R_p) and every later row block is updated
 // R_i -= L_ip Z_p.  Since H_d^-1 = Z^T Z, d_j is the squared norm of column j of
-// Z, accumulated panel by panel in a fixed order.  Per panel p, two launches:
+// Z, accumulated panel by panel in a fixed order.  Panels come in groups of
+// four; per panel:
 //   chol_panel       L_ip = A_ip L_pp^-T for the rows below; Z_p = L_pp^-1 R_p and d += col-norms^2;
-//                    diagonal tile p+1 updated with its L tile
-//   chol_trail_diag  A_ij -= L_ip L_jp^T and R_ij -= L_ip Z_pj over the
-//                    trailing tiles, with diagonal block p+1 factored
-//                    and inverted by workgroup 0 of the same launch (lookahead:
+//                    inside a group, diagonal tile p+1 updated with its L tile
+//   chol_inner       (not after a group's last panel) A_iq -= L_ip L_qp^T and
+//                    R_qj -= L_qp Z_pj for the group's later block columns /
+//                    row blocks q only, with diagonal block p+1 factored and
+//                    inverted by workgroup 0 of the same launch (lookahead:
 //                    the one-workgroup step does not wait for the bulk update,
 //                    nor the bulk for it, and no cross-stream wait is needed)
+// and per group, after its last panel:
+//   chol_group_update  A_ij -= sum_p L_ip L_jp^T and R_ij -= sum_p L_ip Z_pj
+//                    over everything right of / below the group, the sum over
+//                    the group's panels kept in the accumulators, so each tile
+//                    of A and Z is read and written once per group (the sweep
+//                    is bound by that traffic: A and Z are 2 m^2 doubles);
+//                    workgroup 0 updates and factors the next diagonal block.
 // The GEMM-shaped work uses v_mfma_f64_16x16x4_f64 on 64x64 tiles.
+
+#include <algorithm>
 
 #include "common.hpp"
 #include "f64tile.hpp"
@@ -94,9 +105,12 @@ __global__ __launch_bounds__(256) void sal_init_kernel(const float *__restrict__
 // barrier per EB columns publishes the block's columns of A and rows of R.
 // Thread t keeps its cells of row t / NS (DC contiguous columns) of both
 // arrays in registers.
+// LDS: `smem` holds DIAG_LDS doubles (carved below), so a launch that also
+// runs tile products can hand over the same buffer.
+constexpr int DIAG_LDS = 2 * 2 * 8 * NBK + NBK;
 template <int NT>
 __device__ __forceinline__ void chol_diag_body(double *__restrict__ A, int64_t mp, int p, double *__restrict__ TinvT,
-                                               int32_t *__restrict__ info) {
+                                               int32_t *__restrict__ info, double *__restrict__ smem) {
   constexpr int DC = NBK * NBK / NT;   // columns per thread
   constexpr int NS = NBK / DC;         // column strips per row
   constexpr int EB = 8;                // columns eliminated per barrier
@@ -104,10 +118,11 @@ __device__ __forceinline__ void chol_diag_body(double *__restrict__ A, int64_t m
   // Ping-pong buffers: the block's columns of A (all rows) and rows of R,
   // both stored [t][pm(c)] with pm(c) = (c % DC) NS + c / DC, so the NS
   // strips of a row, reading column c0 + q at once, touch consecutive words.
-  __shared__ __attribute__((aligned(16))) double colJ[2][EB][NBK];
-  __shared__ __attribute__((aligned(16))) double rowJ[2][EB][NBK];
+  static_assert(DIAG_LDS == 2 * 2 * EB * NBK + NBK, "LDS carve-up");
+  double(*colJ)[EB][NBK] = reinterpret_cast<double(*)[EB][NBK]>(smem);
+  double(*rowJ)[EB][NBK] = reinterpret_cast<double(*)[EB][NBK]>(smem + 2 * EB * NBK);
+  double *piv = smem + 4 * EB * NBK;
   auto pm = [](int c) __attribute__((always_inline)) { return (c % DC) * NS + c / DC; };
-  __shared__ double piv[NBK];
   const int tid = threadIdx.x;
   const int oi = tid / NS, c0 = DC * (tid % NS);   // this thread: row oi, columns c0 .. c0 + DC - 1
   const int64_t k0 = (int64_t)p * NBK;
@@ -244,15 +259,18 @@ __device__ __forceinline__ void chol_diag_body(double *__restrict__ A, int64_t m
 
 __global__ __launch_bounds__(512) void chol_diag_kernel(double *__restrict__ A, int64_t mp, int p,
                                                         double *__restrict__ TinvT, int32_t *__restrict__ info) {
-  chol_diag_body<512>(A, mp, p, TinvT, info);
+  __shared__ __attribute__((aligned(16))) double smem[DIAG_LDS];
+  chol_diag_body<512>(A, mp, p, TinvT, info, smem);
 }
 
 // Panel kernel.  Workgroups [0, nrow): row block ib = p+1+w: L_ib,p = A_ib,p Tinv^T
-// (workgroup 0 then also updates diagonal tile p+1 with its L tile).
+// (with `look`, workgroup 0 then also updates diagonal tile p+1 with its L
+// tile: inside a group of panels; after a group's last panel the group
+// update takes that tile).
 // Workgroups [nrow, nrow+p+1): column block cb: Z_p[:, cb] = Tinv R_p[:, cb], d[cb] += column norms^2.
 __global__ __launch_bounds__(256) void chol_panel_kernel(double *__restrict__ A, double *__restrict__ Z,
                                                          const double *__restrict__ TinvT, double *__restrict__ d,
-                                                         int64_t mp, int p, int nrow) {
+                                                         int64_t mp, int p, int nrow, int look) {
   __shared__ double sA[NBK * SP];
   __shared__ double sB[NBK * SP];
   __shared__ double colsum[2][64];
@@ -268,7 +286,7 @@ __global__ __launch_bounds__(256) void chol_panel_kernel(double *__restrict__ A,
     // tile, A_{p+1,p+1} -= L L^T with the L tile it forms, whose entries it
     // loads here with the operands.
     double cv[2][2][4];
-    if (w == 0) {
+    if (w == 0 && look) {
 #pragma unroll
       for (int i = 0; i < 2; ++i)
 #pragma unroll
@@ -303,7 +321,7 @@ __global__ __launch_bounds__(256) void chol_panel_kernel(double *__restrict__ A,
           const int col = wn * 32 + j * 16 + (lane & 15);
           A[(r0 + row) * mp + k0 + col] = acc[i][j][v];
         }
-    if (w == 0) {
+    if (w == 0 && look) {
       __syncthreads();   // the product's operand reads are done
       // sA[k][i] = L[i][k] serves as both operands: the product is L L^T
 #pragma unroll
@@ -374,28 +392,32 @@ __global__ __launch_bounds__(256) void chol_panel_kernel(double *__restrict__ A,
   }
 }
 
-// One 64 x 64 tile of the trailing update of panel p:
-//   A tile (rows r0, cols c0):  A_ij -= L_ip L_jp^T
-//   Z tile (rows r0, cols c0):  Z_ib,cb -= L_ip Z_p,cb
-// Both operands and the tile itself are loaded into registers first, so all
-// of the loads are in flight together, then the operands pass through LDS.
-__device__ __forceinline__ void trail_tile(double *__restrict__ A, double *__restrict__ Z, int64_t mp, int64_t k0,
-                                           int64_t r0, int64_t c0, bool zt) {
-  __shared__ double sA[NBK * SP];
-  __shared__ double sB[NBK * SP];
+// One 64 x 64 tile of a trailing update by the panels plo .. phi:
+//   A tile (rows r0, cols c0):  A_ij -= sum_p L_ip L_jp^T
+//   Z tile (rows r0, cols c0):  Z_ib,cb -= sum_p L_ip Z_p,cb
+// The sum over the panels stays in the MFMA accumulators, so the tile itself
+// is read and written once.  Each panel's two operand tiles are loaded into
+// registers while the previous panel's product runs, then pass through LDS
+// (sA, sB: NBK * SP doubles each).
+__device__ __forceinline__ void trail_tile(double *__restrict__ A, double *__restrict__ Z, int64_t mp, int64_t r0,
+                                           int64_t c0, bool zt, int plo, int phi, double *sA, double *sB) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
   double *C = zt ? Z : A;
   // ra[e] = A[r0+hi][k0+lo] -> sA[lo][hi]; rb[e] = Z[k0+hi][c0+lo] -> sB[hi][lo] (Z tile)
   // or A[c0+hi][k0+lo] -> sB[lo][hi] (A tile)
   double ra[16], rb[16], cv[2][2][4];
+  auto load_ops = [&](int p) __attribute__((always_inline)) {
+    const int64_t k0 = (int64_t)p * NBK;
 #pragma unroll
-  for (int e = 0; e < 16; ++e) {
-    const int idx = tid + e * 256;
-    const int hi = idx >> 6, lo = idx & 63;
-    ra[e] = A[(r0 + hi) * mp + k0 + lo];
-    rb[e] = zt ? Z[(k0 + hi) * mp + c0 + lo] : A[(c0 + hi) * mp + k0 + lo];
-  }
+    for (int e = 0; e < 16; ++e) {
+      const int idx = tid + e * 256;
+      const int hi = idx >> 6, lo = idx & 63;
+      ra[e] = A[(r0 + hi) * mp + k0 + lo];
+      rb[e] = zt ? Z[(k0 + hi) * mp + c0 + lo] : A[(c0 + hi) * mp + k0 + lo];
+    }
+  };
+  load_ops(plo);
 #pragma unroll
   for (int i = 0; i < 2; ++i)
 #pragma unroll
@@ -406,15 +428,19 @@ __device__ __forceinline__ void trail_tile(double *__restrict__ A, double *__res
         const int col = wn * 32 + j * 16 + (lane & 15);
         cv[i][j][v] = C[(r0 + row) * mp + c0 + col];
       }
-  stash_T(sA, ra, tid);
-  if (zt)
-    stash_N(sB, rb, tid);
-  else
-    stash_T(sB, rb, tid);
-  __syncthreads();
   f64x4_t acc[2][2];
   zero_acc(acc);
-  gemm64(sA, sB, acc, lane, wm, wn);
+  for (int p = plo; p <= phi; ++p) {
+    if (p > plo) __syncthreads();   // the previous product's operand reads are done
+    stash_T(sA, ra, tid);
+    if (zt)
+      stash_N(sB, rb, tid);
+    else
+      stash_T(sB, rb, tid);
+    __syncthreads();
+    if (p < phi) load_ops(p + 1);
+    gemm64(sA, sB, acc, lane, wm, wn);
+  }
 #pragma unroll
   for (int i = 0; i < 2; ++i)
 #pragma unroll
@@ -427,64 +453,99 @@ __device__ __forceinline__ void trail_tile(double *__restrict__ A, double *__res
       }
 }
 
-// Trailing update of panel p (NB panels in all), one launch with the next
-// diagonal block factored beside it (lookahead).  Workgroup b:
-//   b = 0          factors and inverts diagonal block p+1, which the panel
-//                  solve's workgroup for row block p+1 has already updated
-//                  (no other workgroup reads or writes it, nor TinvT);
-//   1 <= b < NB    the rest of block column p+1 of A (row blocks p+2 .. NB-1)
-//                  and row block p+1 of Z (column blocks 0 .. p);
-//   b >= NB        A tiles with row >= column >= p+2, and Z row blocks
-//                  p+2 .. NB-1 (column blocks 0 .. p).
-// The next panel solve needs all of block column p+1, the factored block and
-// row block p+1 of Z, so it follows this launch on the same stream with no
-// cross-stream wait.
-__device__ __forceinline__ void trail_coords(int64_t b, int p, int NB, int &ii, int &jj, bool &zt) {
-  if (b < NB) {
-    const int nA = NB - p - 1;   // block column p+1, the diagonal tile (b = 0) included
-    if (b < nA) {
-      ii = p + 1 + (int)b;
-      jj = p + 1;
-      zt = false;
-    } else {
-      ii = p + 1;
-      jj = (int)(b - nA);
-      zt = true;
-    }
-  } else {
-    const int64_t w = b - NB;
-    const int n2 = NB - p - 2;
-    const int64_t nA = (int64_t)n2 * (n2 + 1) / 2;
-    if (w < nA) {
-      const int id = (int)w;
-      int a = (int)((sqrt(8.0 * id + 1.0) - 1.0) * 0.5);
-      while ((a + 1) * (a + 2) / 2 <= id) ++a;
-      while (a * (a + 1) / 2 > id) --a;
-      ii = p + 2 + a;
-      jj = p + 2 + (id - a * (a + 1) / 2);
-      zt = false;
-    } else {
-      const int64_t id = w - nA;
-      ii = p + 2 + (int)(id / (p + 1));
-      jj = (int)(id % (p + 1));
-      zt = true;
-    }
-  }
+// XCD-aware work index: workgroup id w runs on XCD w % 8, so XCD x takes
+// the contiguous run of work items [x * per, x * per + per), per =
+// ceil(total / 8), in order: neighbouring tiles of a row share an operand
+// panel, which then stays in that XCD's L2.  Returns -1 for padding ids.
+__device__ __forceinline__ int64_t xcd_item(int64_t w, int64_t total) {
+  const int64_t per = (total + 7) / 8;
+  const int64_t t = (w & 7) * per + (w >> 3);
+  return t < total ? t : -1;
+}
+static unsigned xcd_grid(int64_t total) { return (unsigned)(8 * ((total + 7) / 8)); }
+
+// Row index a of a packed lower triangle (entries (a, b), b <= a, numbered
+// row by row) from the entry number id.
+__device__ __forceinline__ int tri_row(int64_t id) {
+  int a = (int)((sqrt(8.0 * (double)id + 1.0) - 1.0) * 0.5);
+  while ((int64_t)(a + 1) * (a + 2) / 2 <= id) ++a;
+  while ((int64_t)a * (a + 1) / 2 > id) --a;
+  return a;
 }
 
-__global__ __launch_bounds__(256) void chol_trail_diag_kernel(double *__restrict__ A, double *__restrict__ Z,
-                                                              double *__restrict__ TinvT,
-                                                              int32_t *__restrict__ info, int64_t mp, int p,
-                                                              int NB) {
-  if (blockIdx.x == 0) {
-    // tile (p+1, p+1) was updated by the panel solve
-    chol_diag_body<256>(A, mp, p + 1, TinvT, info);
+// Panels are taken in groups [p0, p1] of up to CHOL_GROUP.  Inside a group,
+// panel p's update reaches only the group's later block columns q in
+// (p, p1] (A tiles (i, q), i >= q) and Z's row blocks q (column blocks
+// <= p); everything right of the group is updated once per group, by all
+// of its panels in one product per tile (chol_group_update).
+//
+// Inner update of panel p (p < p1).  Work item b (xcd_item of the id):
+//   b = 0    factors and inverts diagonal block p+1, which the panel solve's
+//            workgroup for row block p+1 has already updated with panel p
+//            (its earlier panels of the group came with the previous inner
+//            updates, those before the group with the group updates);
+//   b >= 1   A tiles (i, q), q in (p, p1], i >= q, except (p+1, p+1), then Z
+//            tiles (q, cb), q in (p, p1], cb <= p; one panel, K = 64.
+__global__ __launch_bounds__(256, 2) void chol_inner_kernel(double *__restrict__ A, double *__restrict__ Z,
+                                                         double *__restrict__ TinvT, int32_t *__restrict__ info,
+                                                         int64_t mp, int p, int p1, int NB, int64_t total) {
+  __shared__ __attribute__((aligned(16))) double smem[2 * NBK * SP];
+  static_assert(DIAG_LDS <= 2 * NBK * SP, "the diagonal step fits the tile buffers");
+  const int64_t item = xcd_item(blockIdx.x, total);
+  if (item < 0) return;
+  if (item == 0) {
+    chol_diag_body<256>(A, mp, p + 1, TinvT, info, smem);
     return;
   }
-  int ii, jj;
-  bool zt;
-  trail_coords((int64_t)blockIdx.x, p, NB, ii, jj, zt);
-  trail_tile(A, Z, mp, (int64_t)p * NBK, (int64_t)ii * NBK, (int64_t)jj * NBK, zt);
+  int64_t b = item - 1;
+  for (int q = p + 1; q <= p1; ++q) {
+    const int first = q == p + 1 ? q + 1 : q;
+    const int64_t cnt = NB - first;
+    if (b < cnt) {
+      trail_tile(A, Z, mp, (int64_t)(first + b) * NBK, (int64_t)q * NBK, false, p, p, smem, smem + NBK * SP);
+      return;
+    }
+    b -= cnt;
+  }
+  const int q = p + 1 + (int)(b / (p + 1));
+  const int cb = (int)(b % (p + 1));
+  trail_tile(A, Z, mp, (int64_t)q * NBK, (int64_t)cb * NBK, true, p, p, smem, smem + NBK * SP);
+}
+
+// Group update after the group [p0, p1] (p1 < NB - 1).  Work item b:
+//   b = 0    tile (p1+1, p1+1) by the whole group, then factors and inverts
+//            that diagonal block (the next group's first panel);
+//   b >= 1   A tiles (i, j), p1 < j <= i, except (p1+1, p1+1), by panels
+//            p0 .. p1; then Z tiles (i, cb), i > p1, cb <= p1, by the panels
+//            max(p0, cb) .. p1 (Z_p,cb is zero for cb > p).
+__global__ __launch_bounds__(256, 2) void chol_group_update_kernel(double *__restrict__ A, double *__restrict__ Z,
+                                                                double *__restrict__ TinvT,
+                                                                int32_t *__restrict__ info, int64_t mp, int p0,
+                                                                int p1, int NB, int64_t total) {
+  __shared__ __attribute__((aligned(16))) double smem[2 * NBK * SP];
+  const int j0 = p1 + 1;
+  const int64_t item = xcd_item(blockIdx.x, total);
+  if (item < 0) return;
+  if (item == 0) {
+    trail_tile(A, Z, mp, (int64_t)j0 * NBK, (int64_t)j0 * NBK, false, p0, p1, smem, smem + NBK * SP);
+    __syncthreads();   // the updated tile is visible to the whole workgroup
+    chol_diag_body<256>(A, mp, j0, TinvT, info, smem);
+    return;
+  }
+  const int n2 = NB - j0;
+  const int64_t nA = (int64_t)n2 * (n2 + 1) / 2 - 1;
+  const int64_t b = item - 1;
+  if (b < nA) {
+    const int64_t id = b + 1;   // entry 0 is (j0, j0)
+    const int a = tri_row(id);
+    const int i = j0 + a, j = j0 + (int)(id - (int64_t)a * (a + 1) / 2);
+    trail_tile(A, Z, mp, (int64_t)i * NBK, (int64_t)j * NBK, false, p0, p1, smem, smem + NBK * SP);
+    return;
+  }
+  const int64_t id = b - nA;
+  const int i = j0 + (int)(id / (p1 + 1));
+  const int cb = (int)(id % (p1 + 1));
+  trail_tile(A, Z, mp, (int64_t)i * NBK, (int64_t)cb * NBK, true, cb > p0 ? cb : p0, p1, smem, smem + NBK * SP);
 }
 
 // hinv[j] = d_j; after the reversed sweep d holds the diagonal in reverse order.
@@ -554,6 +615,9 @@ __global__ __launch_bounds__(256) void sal_group_final_kernel(const double *__re
 
 static int64_t pad64(int64_t m) { return (m + NBK - 1) / NBK * NBK; }
 
+// Panels per group of the sweep (see launch_chol_inverse).
+constexpr int CHOL_GROUP = 8;
+
 size_t salience_ws_bytes(int64_t n, int64_t m, int group) {
   const int64_t mp = pad64(m);
   const int64_t nrb = (n + 63) / 64;
@@ -577,18 +641,31 @@ hipError_t launch_chol_inverse(const float *H, int64_t m, double damp, bool reve
     if (blocks > 65536) blocks = 65536;
     sal_init_kernel<<<(unsigned)blocks, 256, 0, st>>>(H, m, mp, alpha, A, Z, d, info, reverse ? 1 : 0);
   }
-  // Per panel: the panel solve, then the trailing update with the next
-  // diagonal block factored beside it in the same launch.
+  // Panels in groups of CHOL_GROUP: per panel the panel solve and, inside the
+  // group, the inner update (with the next diagonal block factored beside it);
+  // after the group the update of everything right of it by all of the
+  // group's panels at once (again with the next diagonal block).  A and Z are
+  // then read and written once per group rather than once per panel.
   const int NB = (int)(mp / NBK);
   chol_diag_kernel<<<1, 512, 0, st>>>(A, mp, 0, TinvT, info);
-  for (int p = 0; p < NB; ++p) {
-    const int nrow = NB - p - 1;
-    chol_panel_kernel<<<nrow + p + 1, 256, 0, st>>>(A, Z, TinvT, d, mp, p, nrow);
-    if (nrow > 0) {
-      const int64_t n2 = nrow - 1;
-      const int64_t rest = n2 * (n2 + 1) / 2 + n2 * (p + 1);
+  for (int p0 = 0; p0 < NB; p0 += CHOL_GROUP) {
+    const int p1 = std::min(p0 + CHOL_GROUP, NB) - 1;
+    for (int p = p0; p <= p1; ++p) {
+      const int nrow = NB - p - 1;
+      chol_panel_kernel<<<nrow + p + 1, 256, 0, st>>>(A, Z, TinvT, d, mp, p, nrow, p < p1 ? 1 : 0);
+      if (p < p1) {
+        int64_t tiles = (int64_t)(p1 - p) * (p + 1);
+        for (int q = p + 1; q <= p1; ++q) tiles += NB - (q == p + 1 ? q + 1 : q);
+        timer_begin(K_CHOL_UPDATE, st);
+        chol_inner_kernel<<<xcd_grid(1 + tiles), 256, 0, st>>>(A, Z, TinvT, info, mp, p, p1, NB, 1 + tiles);
+        timer_end(K_CHOL_UPDATE, st);
+      }
+    }
+    if (p1 < NB - 1) {
+      const int64_t n2 = NB - p1 - 1;
+      const int64_t tiles = n2 * (n2 + 1) / 2 + n2 * (p1 + 1);   // the diagonal one by workgroup 0
       timer_begin(K_CHOL_UPDATE, st);
-      chol_trail_diag_kernel<<<(unsigned)(NB + rest), 256, 0, st>>>(A, Z, TinvT, info, mp, p, NB);
+      chol_group_update_kernel<<<xcd_grid(tiles), 256, 0, st>>>(A, Z, TinvT, info, mp, p0, p1, NB, tiles);
       timer_end(K_CHOL_UPDATE, st);
     }
   }
