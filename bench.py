@@ -496,6 +496,16 @@ def main():
             "frac": round(n * m * SQC_LANE_OPS_PER_PARAM / (q_step * 1e-3) / PEAK_VALU_LANE_OPS, 4),
             "hbm_gbps": round(n * m * (2 + 1 + 0.125) / (q_step * 1e-3) / 1e9, 1),
             "hbm_frac": round(n * m * (2 + 1 + 0.125) / (q_step * 1e-3) / PEAK_HBM_BPS, 4)}
+    # salience: the float64 Cholesky sweep factors H_d (m^3/3 flops) and
+    # inverts the factor alongside (another m^3/3), on the f64 matrix cores;
+    # timed as the whole stage (its kernels run per panel)
+    sal_ms = stages["salience"]
+    if sal_ms > 0:
+        f = 2.0 * m ** 3 / 3.0
+        ro["salience"] = {"bound": "mfma", "dtype": "f64", "flops": f, "ms": round(sal_ms, 3),
+                          "achieved_tflops": round(f / (sal_ms * 1e-3) / 1e12, 2), "peak": 78.6,
+                          "frac": round(f / (sal_ms * 1e-3) / 78.6e12, 4),
+                          "factor_only_frac": round(f / 2.0 / (sal_ms * 1e-3) / 78.6e12, 4)}
     if pl:
         ro["pack_planes"] = {"bound": "hbm", "bytes": n * m * (1 + N / 8),
                              "achieved_gbps": round(n * m * (1 + N / 8) / (pms / pl * 1e-3) / 1e9, 1),
