@@ -12,8 +12,8 @@
 // substitution L Z = I: when panel p is factored, its rows of Z = L^-1 become
 // final (Z_p = L_pp^-1 R_p) and every later row block is updated
 // R_i -= L_ip Z_p.  Since H_d^-1 = Z^T Z, d_j is the squared norm of column j of
-// Z, accumulated panel by panel in a fixed order.  Panels come in groups of
-// four; per panel:
+// Z, accumulated panel by panel in a fixed order.  Panels come in groups (of
+// one to eight, by the width); per panel:
 //   chol_panel       L_ip = A_ip L_pp^-T for the rows below; Z_p = L_pp^-1 R_p and d += col-norms^2;
 //                    inside a group, diagonal tile p+1 updated with its L tile
 //   chol_inner       (not after a group's last panel) A_iq -= L_ip L_qp^T and
@@ -473,7 +473,7 @@ __device__ __forceinline__ int tri_row(int64_t id) {
   return a;
 }
 
-// Panels are taken in groups [p0, p1] of up to CHOL_GROUP.  Inside a group,
+// Panels are taken in groups [p0, p1] (chol_group).  Inside a group,
 // panel p's update reaches only the group's later block columns q in
 // (p, p1] (A tiles (i, q), i >= q) and Z's row blocks q (column blocks
 // <= p); everything right of the group is updated once per group, by all
@@ -615,8 +615,13 @@ __global__ __launch_bounds__(256) void sal_group_final_kernel(const double *__re
 
 static int64_t pad64(int64_t m) { return (m + NBK - 1) / NBK * NBK; }
 
-// Panels per group of the sweep (see launch_chol_inverse).
-constexpr int CHOL_GROUP = 8;
+// Panels per group of the sweep (see launch_chol_inverse), by the number of
+// 64-wide panels NB: with few panels each panel's serial chain (panel solve,
+// then the diagonal step) sets the time and one panel per update is best;
+// with many, the trailing traffic does and eight are (same-box sweep of 1, 2,
+// 4, 8, 16: m = 4096 3.01 / 3.10 / 3.22 / 3.31 ms; m = 8192 14.6 / 12.9 /
+// 12.9 / 12.6; m = 11008 33.2 / 26.7 / 25.7 / 24.6 / 24.3).
+static int chol_group(int NB) { return NB <= 64 ? 1 : (NB < 128 ? 4 : 8); }
 
 size_t salience_ws_bytes(int64_t n, int64_t m, int group) {
   const int64_t mp = pad64(m);
@@ -641,15 +646,16 @@ hipError_t launch_chol_inverse(const float *H, int64_t m, double damp, bool reve
     if (blocks > 65536) blocks = 65536;
     sal_init_kernel<<<(unsigned)blocks, 256, 0, st>>>(H, m, mp, alpha, A, Z, d, info, reverse ? 1 : 0);
   }
-  // Panels in groups of CHOL_GROUP: per panel the panel solve and, inside the
+  // Panels in groups of chol_group(NB): per panel the panel solve and, inside the
   // group, the inner update (with the next diagonal block factored beside it);
   // after the group the update of everything right of it by all of the
   // group's panels at once (again with the next diagonal block).  A and Z are
   // then read and written once per group rather than once per panel.
   const int NB = (int)(mp / NBK);
+  const int G = chol_group(NB);
   chol_diag_kernel<<<1, 512, 0, st>>>(A, mp, 0, TinvT, info);
-  for (int p0 = 0; p0 < NB; p0 += CHOL_GROUP) {
-    const int p1 = std::min(p0 + CHOL_GROUP, NB) - 1;
+  for (int p0 = 0; p0 < NB; p0 += G) {
+    const int p1 = std::min(p0 + G, NB) - 1;
     for (int p = p0; p <= p1; ++p) {
       const int nrow = NB - p - 1;
       chol_panel_kernel<<<nrow + p + 1, 256, 0, st>>>(A, Z, TinvT, d, mp, p, nrow, p < p1 ? 1 : 0);
