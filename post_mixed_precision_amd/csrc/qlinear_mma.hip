@@ -20,8 +20,10 @@
 // D[4 (l / 16) .. +3][l % 16].  With A = X (rows = tokens, K = columns) and
 // B = codes (K = columns, columns = output rows), lane l owns output row
 // l % 16 of its wave's 16 and the bits 8 (l / 16) .. +7 of each plane word:
-// a plane word covers one 32-column K slice.  Xs comes from the same MFMA
-// with B = 1.  float32 X enters as three bfloat16 terms whose sum is exact.
+// a plane word covers one 32-column K slice.  Xs, the group sums of X, is
+// formed once per workgroup from the staged X (up to 8 tokens) or by the same
+// MFMA with B = 1 (9 to 16).  float32 X enters as three bfloat16 terms whose
+// sum is exact.
 //
 // Expanding codes: for four columns, the nibble of plane p is spread to one
 // bit per byte by (nib * 0x00204081) & 0x01010101 (the four shifted copies of
@@ -130,9 +132,9 @@ __device__ __forceinline__ void qm_x(const void *__restrict__ Xv, int64_t idx, b
 // One group of NP planes.  wc[p]: the plane words this lane loaded (word
 // (lane / 16) % KS of its row, so each wave's load is 256 contiguous bytes);
 // the words of K slice s move to the four lanes that use them with a lane
-// shuffle.  X comes from LDS (zero rows past the batch).  acc += X q,
-// acc1 += X 1.
-template <int NP, int KS, int NT>
+// shuffle.  X comes from LDS (zero rows past the batch).  acc += X q, and
+// without XSPRE acc1 += X 1 (the group sums of X by the same MFMA).
+template <int NP, int KS, int NT, bool XSPRE>
 __device__ __forceinline__ void qm_group(const uint32_t (&wc)[8], const uint4 *__restrict__ xl, int xstride,
                                          int xrows, int qbase, bool tok, int col, int sh, f32x4_t &acc,
                                          f32x4_t &acc1) {
@@ -147,12 +149,16 @@ __device__ __forceinline__ void qm_group(const uint32_t (&wc)[8], const uint4 *_
     for (int e = 0; e < NT; ++e) {
       const uint4 xa = tok ? xl[e * xrows * xstride + qbase + 4 * s] : make_uint4(0u, 0u, 0u, 0u);
       acc = mfma16x32(xa, bq, acc);
-      acc1 = mfma16x32(xa, ones, acc1);
+      if constexpr (!XSPRE) acc1 = mfma16x32(xa, ones, acc1);
     }
   }
 }
 
-template <bool XBF16, int G>
+// XSPRE: the group sums of X (the zero-point term) are formed once per
+// workgroup before the groups (batches of up to 8 tokens: measured faster);
+// otherwise by a second MFMA per K slice against ones (9 to 16 tokens, where
+// the up-front pass over twice the rows costs more than the MFMAs it saves).
+template <bool XBF16, int G, bool XSPRE>
 __global__ __launch_bounds__(256) void qlinear_mma_kernel(const void *__restrict__ Xv, int t, int xrows, int64_t m,
                                                           const uint32_t *__restrict__ packed,
                                                           const int8_t *__restrict__ bits, int N,
@@ -199,6 +205,37 @@ __global__ __launch_bounds__(256) void qlinear_mma_kernel(const void *__restrict
   }
   const bool ok = !badw && tot == k * N;
   __syncthreads();
+  // Xs[a, j] of the run's groups, once per workgroup from the staged terms
+  // (their sum, high term first, is the float32 value exactly): the
+  // zero-point term needs it once per token and group, not once per output
+  // row.  One lane per 8-column chunk (neighbouring lanes read neighbouring
+  // chunks), then a butterfly over the group's G/8 lanes, in a fixed order.
+  __shared__ float4 qm_xs[8][QM_TOK / 4];   // [group of the run][token / 4]
+  if constexpr (XSPRE) {
+    constexpr int CH = G / 8;                // chunks (lanes) per token and group
+    const int gw = j1 - j0;
+    for (int e = tid; e < t * gw * CH; e += 256) {   // a multiple of CH: a chunk group is all in or all out
+      const int q = e % CH, pr = e / CH, a = pr / gw, jj = pr % gw;
+      uint4 v[NT];
+#pragma unroll
+      for (int u = 0; u < NT; ++u) v[u] = qm_x_lds[(u * xrows + a) * xstride + jj * CH + q];
+      float sum = 0.0f;
+#pragma unroll
+      for (int h = 0; h < 8; ++h) {
+        float x = 0.0f;
+#pragma unroll
+        for (int u = 0; u < NT; ++u) {
+          const uint32_t w = h < 2 ? v[u].x : (h < 4 ? v[u].y : (h < 6 ? v[u].z : v[u].w));
+          x += __uint_as_float((h & 1) ? (w & 0xffff0000u) : (w << 16));
+        }
+        sum += x;
+      }
+#pragma unroll
+      for (int d = 1; d < CH; d <<= 1) sum += __shfl_xor(sum, d, 64);
+      if (q == 0) ((float *)qm_xs)[jj * QM_TOK + a] = sum;
+    }
+  }
+  if constexpr (XSPRE) __syncthreads();
   f32x4_t y = {0.0f, 0.0f, 0.0f, 0.0f};
   if (ok) {
     const int64_t pstride = n * KS;                                // words between planes
@@ -220,19 +257,27 @@ __global__ __launch_bounds__(256) void qlinear_mma_kernel(const void *__restrict
       const int qbase = (tok ? col : 0) * xstride + (j - j0) * (G / 8) + quad;   // rows past the batch read as zero
       f32x4_t acc = {0.0f, 0.0f, 0.0f, 0.0f}, acc1 = {0.0f, 0.0f, 0.0f, 0.0f};
       switch (b) {
-        case 1: qm_group<1, KS, NT>(wc, qm_x_lds, xstride, xrows, qbase, tok, col, sh, acc, acc1); break;
-        case 2: qm_group<2, KS, NT>(wc, qm_x_lds, xstride, xrows, qbase, tok, col, sh, acc, acc1); break;
-        case 3: qm_group<3, KS, NT>(wc, qm_x_lds, xstride, xrows, qbase, tok, col, sh, acc, acc1); break;
-        case 4: qm_group<4, KS, NT>(wc, qm_x_lds, xstride, xrows, qbase, tok, col, sh, acc, acc1); break;
-        case 5: qm_group<5, KS, NT>(wc, qm_x_lds, xstride, xrows, qbase, tok, col, sh, acc, acc1); break;
-        case 6: qm_group<6, KS, NT>(wc, qm_x_lds, xstride, xrows, qbase, tok, col, sh, acc, acc1); break;
-        case 7: qm_group<7, KS, NT>(wc, qm_x_lds, xstride, xrows, qbase, tok, col, sh, acc, acc1); break;
-        default: qm_group<8, KS, NT>(wc, qm_x_lds, xstride, xrows, qbase, tok, col, sh, acc, acc1); break;
+        case 1: qm_group<1, KS, NT, XSPRE>(wc, qm_x_lds, xstride, xrows, qbase, tok, col, sh, acc, acc1); break;
+        case 2: qm_group<2, KS, NT, XSPRE>(wc, qm_x_lds, xstride, xrows, qbase, tok, col, sh, acc, acc1); break;
+        case 3: qm_group<3, KS, NT, XSPRE>(wc, qm_x_lds, xstride, xrows, qbase, tok, col, sh, acc, acc1); break;
+        case 4: qm_group<4, KS, NT, XSPRE>(wc, qm_x_lds, xstride, xrows, qbase, tok, col, sh, acc, acc1); break;
+        case 5: qm_group<5, KS, NT, XSPRE>(wc, qm_x_lds, xstride, xrows, qbase, tok, col, sh, acc, acc1); break;
+        case 6: qm_group<6, KS, NT, XSPRE>(wc, qm_x_lds, xstride, xrows, qbase, tok, col, sh, acc, acc1); break;
+        case 7: qm_group<7, KS, NT, XSPRE>(wc, qm_x_lds, xstride, xrows, qbase, tok, col, sh, acc, acc1); break;
+        default: qm_group<8, KS, NT, XSPRE>(wc, qm_x_lds, xstride, xrows, qbase, tok, col, sh, acc, acc1); break;
       }
       const float sc = live ? scale[i * k + j] : 0.0f;
       const float zp = live ? zero[i * k + j] : 0.0f;
+      float xsv[4];
+      if constexpr (XSPRE) {
+        const float4 xs = qm_xs[j - j0][quad];   // tokens 4 quad .. 4 quad + 3
+        xsv[0] = xs.x; xsv[1] = xs.y; xsv[2] = xs.z; xsv[3] = xs.w;
+      } else {
 #pragma unroll
-      for (int e = 0; e < 4; ++e) y[e] = __builtin_fmaf(sc, __builtin_fmaf(-zp, acc1[e], acc[e]), y[e]);
+        for (int e = 0; e < 4; ++e) xsv[e] = acc1[e];
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) y[e] = __builtin_fmaf(sc, __builtin_fmaf(-zp, xsv[e], acc[e]), y[e]);
     };
     auto width = [&](int j) __attribute__((always_inline)) {
       return j < j1 ? __builtin_amdgcn_readfirstlane((int)bits[j]) : 0;
@@ -513,8 +558,13 @@ void launch_qlinear_mma(const void *X, bool bf16, int t, int64_t m, const uint32
   const dim3 grid((unsigned)((n + 63) / 64), (unsigned)nrun);
   const int xrows = t <= 8 ? 8 : QM_TOK;   // token rows staged: no more LDS than the batch needs
   const size_t lds = (size_t)(bf16 ? 1 : 3) * xrows * gpr * group * 2;   // X terms of a run, bfloat16
-#define SLIM_QM(BF, G) \
-  qlinear_mma_kernel<BF, G><<<grid, 256, lds, st>>>(X, t, xrows, m, packed, bits, N, scale, zero, n, k, gpr, out)
+#define SLIM_QM(BF, G)                                                                                         \
+  if (xrows == 8)                                                                                              \
+    qlinear_mma_kernel<BF, G, true><<<grid, 256, lds, st>>>(X, t, xrows, m, packed, bits, N, scale, zero, n, k, gpr, \
+                                                            out);                                              \
+  else                                                                                                         \
+    qlinear_mma_kernel<BF, G, false><<<grid, 256, lds, st>>>(X, t, xrows, m, packed, bits, N, scale, zero, n, k,     \
+                                                             gpr, out)
   switch (group) {
     case 32: if (bf16) SLIM_QM(true, 32); else SLIM_QM(false, 32); break;
     case 64: if (bf16) SLIM_QM(true, 64); else SLIM_QM(false, 64); break;
