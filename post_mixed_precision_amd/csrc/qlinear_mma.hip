@@ -375,7 +375,7 @@ __global__ __launch_bounds__(QgShape<XBF16>::NTH, 1) void qlinear_gemm_kernel(
   // [term][token][slot] and [output row][slot], slot s of row r stored at s ^ (r & SWZ)
   __shared__ uint4 xt[NT][TOK][SLOTS];
   __shared__ uint4 qt[QG_OUT][SLOTS];
-  __shared__ float xs_s[TOK];
+  __shared__ __attribute__((aligned(16))) float xs_s[TOK];
   __shared__ int s_bad;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane((int)(tid >> 6));
@@ -401,11 +401,21 @@ __global__ __launch_bounds__(QgShape<XBF16>::NTH, 1) void qlinear_gemm_kernel(
   __syncthreads();
   const bool ok = !s_bad;
 
-  // registers holding one group's operands until they go to LDS
+  // registers holding one group's operands until they go to LDS, and the
+  // scale and zero of this lane's two output rows (one per 32-row block),
+  // fetched a group ahead so that their latency hides behind a group's products
   uint4 xr[XPT][NT];
   uint32_t wr[QIT][8];
   float xsr = 0.0f;
+  float scn[2], zpn[2];
+  const int fr = lane & 31;
   auto fetch = [&](int j, int b, int64_t off) __attribute__((always_inline)) {
+#pragma unroll
+    for (int ob = 0; ob < 2; ++ob) {
+      const int64_t i = i0 + wo * 64 + ob * 32 + fr;
+      scn[ob] = i < n ? scale[i * k + j] : 0.0f;
+      zpn[ob] = i < n ? zero[i * k + j] : 0.0f;
+    }
 #pragma unroll
     for (int q = 0; q < XPT; ++q) {
       const int e = tid + q * NTH;
@@ -467,10 +477,10 @@ __global__ __launch_bounds__(QgShape<XBF16>::NTH, 1) void qlinear_gemm_kernel(
   int64_t off = 0;                            // first word of group j
   int b = ok ? __builtin_amdgcn_readfirstlane((int)bits[0]) : 0;
   if (ok) fetch(0, b, off);
-  const int fr = lane & 31;
   for (int j = 0; j < k && ok; ++j) {
     if (j) __syncthreads();                   // the previous group's tiles are consumed
     stash(b);
+    const float sc_j[2] = {scn[0], scn[1]}, zp_j[2] = {zpn[0], zpn[1]};
     __syncthreads();
     // the next group's operands go out now and land during this group's products
     const int64_t off_n = off + (int64_t)b * pstride;
@@ -503,19 +513,22 @@ __global__ __launch_bounds__(QgShape<XBF16>::NTH, 1) void qlinear_gemm_kernel(
           for (int ob = 0; ob < 2; ++ob) acc[tb][ob] = mfma_bf16(xa, bq[ob], acc[tb][ob]);
         }
     }
-    // y += s (P - z Xs) for the lane's output column of each block
+    // y += s (P - z Xs) for the lane's output column of each block; the
+    // token sums of the lane's accumulator rows come four at a time
+    // (rows 8 g + 4 (lane / 32) + 0..3 for element group g)
 #pragma unroll
-    for (int ob = 0; ob < 2; ++ob) {
-      const int64_t i = i0 + wo * 64 + ob * 32 + fr;
-      const float sc = i < n ? scale[i * k + j] : 0.0f;
-      const float zp = i < n ? zero[i * k + j] : 0.0f;
+    for (int tb = 0; tb < 2; ++tb) {
+      float xsv[16];
 #pragma unroll
-      for (int tb = 0; tb < 2; ++tb)
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const float4 q = *(const float4 *)&xs_s[wt * 64 + tb * 32 + 8 * g4 + 4 * (lane >> 5)];
+        xsv[4 * g4] = q.x; xsv[4 * g4 + 1] = q.y; xsv[4 * g4 + 2] = q.z; xsv[4 * g4 + 3] = q.w;
+      }
 #pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const float xsv = xs_s[wt * 64 + tb * 32 + acc32_row(v, lane)];
-          y[tb][ob][v] = __builtin_fmaf(sc, __builtin_fmaf(-zp, xsv, acc[tb][ob][v]), y[tb][ob][v]);
-        }
+      for (int ob = 0; ob < 2; ++ob)
+#pragma unroll
+        for (int v = 0; v < 16; ++v)
+          y[tb][ob][v] = __builtin_fmaf(sc_j[ob], __builtin_fmaf(-zp_j[ob], xsv[v], acc[tb][ob][v]), y[tb][ob][v]);
     }
     off = off_n;
     b = bn;
