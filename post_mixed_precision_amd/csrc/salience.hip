@@ -227,6 +227,7 @@ __device__ __forceinline__ void chol_diag_body(double *__restrict__ A, int64_t m
 #pragma unroll
       for (int s2 = 0; s2 < EB; ++s2) bv[s2] = (inblk && s2 == tt) ? d[s2] : u[s2];
     }
+#undef L
     // A column is either past the block (A's trailing part) or not (R's
     // columns up to the block): one chain of EB fused multiply-adds on the
     // matching buffer (both are stored [t][pm(c)]).
