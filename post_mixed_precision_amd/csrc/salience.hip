@@ -26,9 +26,11 @@
 //   chol_group_update  A_ij -= sum_p L_ip L_jp^T and R_ij -= sum_p L_ip Z_pj
 //                    over everything right of / below the group, the sum over
 //                    the group's panels kept in the accumulators, so each tile
-//                    of A and Z is read and written once per group (the sweep
-//                    is bound by that traffic: A and Z are 2 m^2 doubles);
-//                    workgroup 0 updates and factors the next diagonal block.
+//                    of A and Z is read and written once per group (A and Z
+//                    are 2 m^2 doubles); the operands go straight to LDS half
+//                    a panel at a time, the next half's loads beside this
+//                    half's products (group_tile); workgroup 0 updates and
+//                    factors the next diagonal block.
 // The GEMM-shaped work uses v_mfma_f64_16x16x4_f64 on 64x64 tiles.
 
 #include <algorithm>
@@ -393,13 +395,15 @@ __global__ __launch_bounds__(256) void chol_panel_kernel(double *__restrict__ A,
   }
 }
 
-// One 64 x 64 tile of a trailing update by the panels plo .. phi:
+// One 64 x 64 tile of a trailing update by the panels plo .. phi (the inner
+// update uses it with a single panel):
 //   A tile (rows r0, cols c0):  A_ij -= sum_p L_ip L_jp^T
 //   Z tile (rows r0, cols c0):  Z_ib,cb -= sum_p L_ip Z_p,cb
 // The sum over the panels stays in the MFMA accumulators, so the tile itself
 // is read and written once.  Each panel's two operand tiles are loaded into
 // registers while the previous panel's product runs, then pass through LDS
-// (sA, sB: NBK * SP doubles each).
+// (sA, sB: NBK * SP doubles each).  (Loaded straight to LDS instead, as in
+// group_tile, a single-panel tile gained nothing.)
 __device__ __forceinline__ void trail_tile(double *__restrict__ A, double *__restrict__ Z, int64_t mp, int64_t r0,
                                            int64_t c0, bool zt, int plo, int phi, double *sA, double *sB) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -441,6 +445,125 @@ __device__ __forceinline__ void trail_tile(double *__restrict__ A, double *__res
     __syncthreads();
     if (p < phi) load_ops(p + 1);
     gemm64(sA, sB, acc, lane, wm, wn);
+  }
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int row = wm * 32 + i * 16 + 4 * v + (lane >> 4);
+        const int col = wn * 32 + j * 16 + (lane & 15);
+        C[(r0 + row) * mp + c0 + col] = cv[i][j][v] - acc[i][j][v];
+      }
+}
+
+// Group-update tiles take their operands straight from memory into LDS
+// (buffer loads to LDS), half a panel (K = 32) at a time into one of two
+// buffers, so a half panel's loads run during the previous half's products,
+// with one barrier per half panel; no operand passes through registers.  An
+// operand half tile is 16 KB: 64 rows of 32 doubles (rows are the product's m
+// or n index) or 32 rows of 64 doubles (rows are K, for the Z operand).  Its
+// 16-byte slots are swizzled so that the product's reads are conflict-free:
+// logical slot ls of row r sits in physical slot ls ^ (r & 15) when the
+// product reads one K across 16 rows, ls ^ 8 (r & 1) when it reads along a row.
+constexpr int HP_BYTES = 64 * 256;   // one operand half tile
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+// DMA of one operand half tile whose element (0, 0) is at `base` (row stride
+// mp doubles).  KIND 0: 64 rows x 32 doubles, four rows per wave instruction;
+// KIND 1: 32 rows x 64 doubles, two rows per instruction.  Each lane loads the
+// logical slot that belongs in the physical slot it writes.
+template <int KIND>
+__device__ __forceinline__ void load_half(const double *base, int64_t mp, unsigned char *dst) {
+  const __amdgpu_buffer_rsrc_t rs =
+      __builtin_amdgcn_make_buffer_rsrc((void *)base, (short)0, (int)((63 * mp + 64) * 8), 0x00020000);
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int r0 = KIND == 0 ? 16 * wave + 4 * q : 8 * wave + 2 * q;   // first row of this instruction
+    const int row = KIND == 0 ? r0 + (lane >> 4) : r0 + (lane >> 5);
+    const int ps = KIND == 0 ? (lane & 15) : (lane & 31);
+    const int ls = KIND == 0 ? ps ^ (row & 15) : ps ^ (8 * (row & 1));
+    const uint32_t off = (uint32_t)row * (uint32_t)(mp * 8) + (uint32_t)(ls * 16);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_t *)(dst + r0 * (KIND == 0 ? 256 : 512)), 16, (int)off, 0,
+                                             0, 0);
+  }
+}
+
+// acc += (A half tile LA) x (B half tile LB) over K = 32 on the 16x16x4 f64
+// MFMA, in the lane layout of gemm64.  LA holds rows m; LB holds rows n (A
+// tiles: B(k, n) = A[c0 + n][k0 + k]) or, for Z tiles, rows k (B(k, n) =
+// Z[k0 + k][c0 + n]).
+template <bool ZT>
+__device__ __forceinline__ void gemm_half(const unsigned char *LA, const unsigned char *LB, f64x4_t acc[2][2],
+                                          int lane, int wm, int wn) {
+  const int l15 = lane & 15;
+#pragma unroll
+  for (int ks = 0; ks < 8; ++ks) {
+    const int k = ks * 4 + (lane >> 4);
+    double a[2], b[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+      a[i] = *(const double *)(LA + (wm * 32 + i * 16 + l15) * 256 + (((k >> 1) ^ l15) * 16) + (k & 1) * 8);
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int n = wn * 32 + j * 16 + l15;
+      b[j] = ZT ? *(const double *)(LB + k * 512 + (((n >> 1) ^ (8 * (k & 1))) * 16) + (n & 1) * 8)
+                : *(const double *)(LB + n * 256 + (((k >> 1) ^ l15) * 16) + (k & 1) * 8);
+    }
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j) acc[i][j] = mfma_f64(a[i], b[j], acc[i][j]);
+  }
+}
+
+// One 64 x 64 tile of the group update by panels plo .. phi (A tile when !ZT:
+// A_ij -= sum_p L_ip L_jp^T; Z tile when ZT: Z_i,cb -= sum_p L_ip Z_p,cb),
+// the sum kept in the accumulators.  l0 and l1 are distinct LDS objects of
+// 2 HP_BYTES each, named statically in each half of the loop, so the compiler
+// can tell the loads into one from the product's reads of the other.
+template <bool ZT>
+__device__ __forceinline__ void group_tile(double *__restrict__ A, double *__restrict__ Z, int64_t mp, int64_t r0,
+                                           int64_t c0, int plo, int phi, unsigned char *l0, unsigned char *l1) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  double *C = ZT ? Z : A;
+  // half panel h: columns 64 plo + 32 h of L (rows r0.., and rows c0.. or Z's rows)
+  auto issue = [&](int h, unsigned char *buf) __attribute__((always_inline)) {
+    const int64_t k0 = (int64_t)plo * NBK + 32 * (int64_t)h;
+    load_half<0>(A + r0 * mp + k0, mp, buf);
+    if (ZT)
+      load_half<1>(Z + k0 * mp + c0, mp, buf + HP_BYTES);
+    else
+      load_half<0>(A + c0 * mp + k0, mp, buf + HP_BYTES);
+  };
+  double cv[2][2][4];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int row = wm * 32 + i * 16 + 4 * v + (lane >> 4);
+        const int col = wn * 32 + j * 16 + (lane & 15);
+        cv[i][j][v] = C[(r0 + row) * mp + c0 + col];
+      }
+  f64x4_t acc[2][2];
+  zero_acc(acc);
+  const int nh = 2 * (phi - plo + 1);   // even
+  issue(0, l0);
+  for (int h = 0; h < nh; h += 2) {
+    __builtin_amdgcn_s_waitcnt(0);   // this thread's loads of half h have landed
+    __syncthreads();                 // everyone's; and l1's previous products are done
+    issue(h + 1, l1);
+    gemm_half<ZT>(l0, l0 + HP_BYTES, acc, lane, wm, wn);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (h + 2 < nh) issue(h + 2, l0);
+    gemm_half<ZT>(l1, l1 + HP_BYTES, acc, lane, wm, wn);
   }
 #pragma unroll
   for (int i = 0; i < 2; ++i)
@@ -523,14 +646,16 @@ __global__ __launch_bounds__(256, 2) void chol_group_update_kernel(double *__res
                                                                 double *__restrict__ TinvT,
                                                                 int32_t *__restrict__ info, int64_t mp, int p0,
                                                                 int p1, int NB, int64_t total) {
-  __shared__ __attribute__((aligned(16))) double smem[2 * NBK * SP];
+  __shared__ __attribute__((aligned(16))) unsigned char l0[2 * HP_BYTES];
+  __shared__ __attribute__((aligned(16))) unsigned char l1[2 * HP_BYTES];
+  static_assert(DIAG_LDS * 8 <= 2 * HP_BYTES, "the diagonal step fits one tile buffer");
   const int j0 = p1 + 1;
   const int64_t item = xcd_item(blockIdx.x, total);
   if (item < 0) return;
   if (item == 0) {
-    trail_tile(A, Z, mp, (int64_t)j0 * NBK, (int64_t)j0 * NBK, false, p0, p1, smem, smem + NBK * SP);
+    group_tile<false>(A, Z, mp, (int64_t)j0 * NBK, (int64_t)j0 * NBK, p0, p1, l0, l1);
     __syncthreads();   // the updated tile is visible to the whole workgroup
-    chol_diag_body<256>(A, mp, j0, TinvT, info, smem);
+    chol_diag_body<256>(A, mp, j0, TinvT, info, (double *)l0);
     return;
   }
   const int n2 = NB - j0;
@@ -540,13 +665,13 @@ __global__ __launch_bounds__(256, 2) void chol_group_update_kernel(double *__res
     const int64_t id = b + 1;   // entry 0 is (j0, j0)
     const int a = tri_row(id);
     const int i = j0 + a, j = j0 + (int)(id - (int64_t)a * (a + 1) / 2);
-    trail_tile(A, Z, mp, (int64_t)i * NBK, (int64_t)j * NBK, false, p0, p1, smem, smem + NBK * SP);
+    group_tile<false>(A, Z, mp, (int64_t)i * NBK, (int64_t)j * NBK, p0, p1, l0, l1);
     return;
   }
   const int64_t id = b - nA;
   const int i = j0 + (int)(id / (p1 + 1));
   const int cb = (int)(id % (p1 + 1));
-  trail_tile(A, Z, mp, (int64_t)i * NBK, (int64_t)cb * NBK, true, cb > p0 ? cb : p0, p1, smem, smem + NBK * SP);
+  group_tile<true>(A, Z, mp, (int64_t)i * NBK, (int64_t)cb * NBK, cb > p0 ? cb : p0, p1, l0, l1);
 }
 
 // hinv[j] = d_j; after the reversed sweep d holds the diagonal in reverse order.
@@ -619,9 +744,10 @@ static int64_t pad64(int64_t m) { return (m + NBK - 1) / NBK * NBK; }
 // Panels per group of the sweep (see launch_chol_inverse), by the number of
 // 64-wide panels NB: with few panels each panel's serial chain (panel solve,
 // then the diagonal step) sets the time and one panel per update is best;
-// with many, the trailing traffic does and eight are (same-box sweep of 1, 2,
-// 4, 8, 16: m = 4096 3.01 / 3.10 / 3.22 / 3.31 ms; m = 8192 14.6 / 12.9 /
-// 12.9 / 12.6; m = 11008 33.2 / 26.7 / 25.7 / 24.6 / 24.3).
+// with many, the trailing products do and eight are (same-box sweep of 1, 2,
+// 4, 8, 16 with the group update's operands loaded straight to LDS: m = 4096
+// 3.01 / 3.00 / 3.04 / 3.16 / 3.20 ms; m = 8192 14.0 / 12.0 / 11.39 / 11.37 /
+// 11.48; m = 11008 32.5 / 25.2 / 22.5 / 21.4 / 22.0).
 static int chol_group(int NB) { return NB <= 64 ? 1 : (NB < 128 ? 4 : 8); }
 
 size_t salience_ws_bytes(int64_t n, int64_t m, int group) {
