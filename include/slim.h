@@ -164,9 +164,11 @@ int slim_salience_u(const float *H, int64_t m, double damp_frac, const void *W, 
  * below that the call returns SLIM_E_WORKSPACE.
  *
  * With bf16 operands, the KL objective, g = 64 or 128 and an even number of
- * 64-column stages over m, the scan reduces a step's softmax statistics
- * during the next step's matrix products; the results are bit-identical to
- * the plain scan, which the environment variable SLIM_SBA_NO_OVERLAP (any
+ * 64-column stages over m, the scan reduces half of a step's softmax
+ * statistics (one token block of each tile) during the next step's matrix
+ * products, the other half right after the step's own; the results are
+ * bit-identical to the plain scan, which the environment variable
+ * SLIM_SBA_NO_OVERLAP (any
  * value, read at each call) selects instead.
  * ---------------------------------------------------------------------- */
 size_t slim_sba_workspace(int64_t t, int64_t n, int64_t m, int group, int dtype);

@@ -658,24 +658,23 @@ __global__ __launch_bounds__(512, 1) void sba_klgemm_kernel(
     // lockstep between them; the arithmetic is the epilogue's, element for
     // element, so the results are the plain scan's bit for bit.
     //   token block 1: its accumulators are copied (the snapshot) after the
-    //     step's last products and reduced from the copy during the next step;
-    //   token block 0 (OVS = 4): the step's first and last stages run the two
-    //     token blocks' products one after the other, so block 0's max and
-    //     first half are taken while block 1's last products run and its
-    //     second half while block 1's first products of the next step run;
-    //     (OVS = 2: block 0 is reduced right after the step's last products);
+    //     step's last products and reduced from the copy during the next
+    //     step's first stages;
+    //   token block 0: reduced right after the step's last products (a second
+    //     snapshot does not fit the 256 registers);
     //   the halves of both blocks are merged at the start of a later stage.
     // A row written before a stage's closing barrier is read after it, and
     // rewritten only after another barrier past that read.
-    //   OVS = 4: S0 = [block 1 products | block 0 second half, row],
-    //                 [block 0 products];
-    //            S1 = products | block 1 max and first half;
-    //            S2 = products | block 1 second half, row;
-    //            S3 = merges of both blocks, [block 0 products], [block 1
-    //                 products | block 0 max and first half], snapshot of block 1.
+    //   OVS = 4: S0 = block-0 merge, products | block 1 max and first half;
+    //            S1 = products | block 1 second half, row;
+    //            S2 = block-1 merge, products;
+    //            S3 = products, block 0 in full, row, snapshot of block 1.
     //   OVS = 2: S0 = block-0 merge, products | block 1 in full, row;
     //            S1 = block-1 merge, products, block 0 in full, snapshot.
-    // (Merges and snapshots sit where the register budget allows: 256.)
+    // (An earlier OVS = 4 schedule split the first and last stages into one
+    // pass per token block so that block 0 could be reduced among block 1's
+    // products: 5-6% slower, from the passes' extra fragment reads and the
+    // fence between them.)
     f32x16_t snapA, snapB;   // token block 1 (outputs 0..31, 32..63 of the half) of the deferred step
     auto snap1 = [&]() __attribute__((always_inline)) {
       snapA = accQ[1];
@@ -688,18 +687,6 @@ __global__ __launch_bounds__(512, 1) void sba_klgemm_kernel(
       yh_sums(0, 0, accQ[0], mq2, zq, se);
       yh_sums(0, 1, accQ[2], mq2, zq, se);
       yh_publish(0, mq, zq, se);
-    };
-    float d0mq = 0.0f, d0mq2 = 0.0f, d0zq = 0.0f, d0se = 0.0f;   // token block 0, in progress
-    auto b0_first = [&]() __attribute__((always_inline)) {
-      d0mq = yh_max(0, accQ[0], accQ[2]);
-      d0mq2 = d0mq * 1.44269504088896341f;
-      d0zq = 0.0f;
-      d0se = 0.0f;
-      yh_sums(0, 0, accQ[0], d0mq2, d0zq, d0se);
-    };
-    auto b0_second = [&]() __attribute__((always_inline)) {
-      yh_sums(0, 1, accQ[2], d0mq2, d0zq, d0se);
-      yh_publish(0, d0mq, d0zq, d0se);
     };
     float dmq = 0.0f, dmq2 = 0.0f, dzq = 0.0f, dse = 0.0f;   // token block 1, in progress
     auto b1_first = [&]() __attribute__((always_inline)) {
@@ -752,67 +739,6 @@ __global__ __launch_bounds__(512, 1) void sba_klgemm_kernel(
       cr = nr;
       csub = nsub;
     };
-    // The products of one token block tb over a stage (both output blocks,
-    // K steps in order): a block's own accumulation order is the plain
-    // stage's, whichever block goes first.  The fragment offset passes through
-    // an empty asm statement (no instruction), so the two passes of a split
-    // stage read their weight fragments each for themselves instead of the
-    // second keeping the first's 64 registers alive.
-    auto update_pass = [&](const unsigned char *L, int tb) __attribute__((always_inline)) {
-      const unsigned char *Bt = L + (2 * SBO + wt * 64 + tb * 32 + (lane & 31)) * SBP;
-      const unsigned char *A0 = L + (wo * 64 + (lane & 31)) * SBP;
-      const unsigned char *A1 = L + (SBO + wo * 64 + (lane & 31)) * SBP;
-#pragma unroll
-      for (int kk = 0; kk < 4; ++kk) {
-        int off = ((2 * kk + (lane >> 5)) ^ sw) * 16;
-        asm volatile("" : "+v"(off));
-        const uint4 b = *(const uint4 *)(Bt + off);
-        uint4 a0[2], a1[2];
-#pragma unroll
-        for (int i = 0; i < 2; ++i) {
-          a0[i] = *(const uint4 *)(A0 + i * 32 * SBP + off);
-          a1[i] = *(const uint4 *)(A1 + i * 32 * SBP + off);
-          a1[i].x ^= 0x80008000u; a1[i].y ^= 0x80008000u; a1[i].z ^= 0x80008000u; a1[i].w ^= 0x80008000u;
-        }
-#pragma unroll
-        for (int ob = 0; ob < 2; ++ob) {
-          accQ[ob * 2 + tb] = mfma_bf16(a0[ob], b, accQ[ob * 2 + tb]);
-          accQ[ob * 2 + tb] = mfma_bf16(a1[ob], b, accQ[ob * 2 + tb]);
-        }
-      }
-    };
-    // Split stage: token block `first` over all K steps, then the other one;
-    // workA among the first pass, workB among the second; the next stage's DMA
-    // goes out among the first four products.
-    auto ov_split_stage = [&](const unsigned char *cur, unsigned char *nxt, int first, auto &&workA,
-                              auto &&workB) __attribute__((always_inline)) {
-      int nr, nsub;
-      advance(nr, nsub);
-      issue_next(nxt, nr, nsub);
-      update_pass(cur, first);
-      workA();
-      __builtin_amdgcn_sched_group_barrier(0x100, 5, 0);
-      for (int j = 0; j < 4; ++j) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x020, 2, 0);
-      }
-      for (int j = 0; j < 3; ++j) {
-        __builtin_amdgcn_sched_group_barrier(0x100, 5, 0);
-        __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
-      }
-      __builtin_amdgcn_sched_barrier(0);   // the first block's products all come first
-      update_pass(cur, 1 - first);
-      workB();
-      for (int j = 0; j < 4; ++j) {
-        __builtin_amdgcn_sched_group_barrier(0x100, 5, 0);
-        __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
-      }
-      __builtin_amdgcn_s_waitcnt(0);
-      __syncthreads();
-      cr = nr;
-      csub = nsub;
-    };
-
     // step 0: y statistics of both token blocks, then what is due of yhat's
     float2 pz01;
     pz01.x = y_stats(0);
@@ -821,31 +747,27 @@ __global__ __launch_bounds__(512, 1) void sba_klgemm_kernel(
       xp[wo][wt * 64 + lane] = make_float2(m_own[0], pz01.x);
       xp[wo][wt * 64 + 32 + lane] = make_float2(m_own[1], pz01.y);
     }
-    if constexpr (OVS == 4)
-      b0_first();
-    else
-      block0();
+    block0();
     snap1();
     __syncthreads();
     cr = 1;
     csub = 0;
     if constexpr (OVS == 4) {
       for (int r = 1; r < R; ++r) {
-        ov_split_stage(lds0, lds1, 1, b0_second, nothing);
-        ov_stage(lds1, lds0, b1_first);
-        ov_stage(lds0, lds1, b1_second);
         if (wo == 0 && lane < 32) merge_tok(0, r - 1);
+        ov_stage(lds0, lds1, b1_first);
+        ov_stage(lds1, lds0, b1_second);
         if (wo == 1 && lane < 32) merge_tok(1, r - 1);
-        ov_split_stage(lds1, lds0, 0, nothing, [&]() __attribute__((always_inline)) {
-          b0_first();
+        ov_stage(lds0, lds1, nothing);
+        ov_stage(lds1, lds0, [&]() __attribute__((always_inline)) {
+          block0();
           snap1();
         });
       }
-      b0_second();
+      if (wo == 0 && lane < 32) merge_tok(0, R - 1);
       b1_first();
       b1_second();
       __syncthreads();
-      if (wo == 0 && lane < 32) merge_tok(0, R - 1);
       if (wo == 1 && lane < 32) merge_tok(1, R - 1);
     } else {
       for (int r = 1; r < R; ++r) {
