@@ -74,7 +74,11 @@ __device__ __forceinline__ float pair_max32(float v) {
 }
 
 // ---------------------------------------------------------------------------
-// Trial weights at tau = 1 for the three widths N-1, N, N+1: Wv[v][n][m].
+// Trial weights at tau = 1 for the three widths N-1, N, N+1: Wv[v][n][m],
+// v = 0, 1, 2, and width N once more negated as Wv[3]: the update subtracts
+// X_g What^N_g^T and reads that copy without a sign flip per fragment, while
+// the main phase forms Yhat_0 from the positive copy with the same MFMA
+// sequence as Y.
 // LPS lanes per row segment, 8 weights per lane.
 template <bool BF16, int LPS>
 __global__ __launch_bounds__(256) void sba_trial_kernel(const void *__restrict__ W, int64_t n, int64_t m, int g,
@@ -137,10 +141,18 @@ __global__ __launch_bounds__(256) void sba_trial_kernel(const void *__restrict__
 #pragma unroll
       for (int e = 0; e < 4; ++e) o[e] = f32_to_bf16_bits(wh[2 * e]) | (f32_to_bf16_bits(wh[2 * e + 1]) << 16);
       *(uint4 *)((uint16_t *)Wv + (int64_t)v * n * m + base) = make_uint4(o[0], o[1], o[2], o[3]);
+      if (v == 1)
+        *(uint4 *)((uint16_t *)Wv + 3 * n * m + base) =
+            make_uint4(o[0] ^ 0x80008000u, o[1] ^ 0x80008000u, o[2] ^ 0x80008000u, o[3] ^ 0x80008000u);
     } else {
       float *dst = (float *)Wv + (int64_t)v * n * m + base;
       *(float4 *)dst = make_float4(wh[0], wh[1], wh[2], wh[3]);
       *(float4 *)(dst + 4) = make_float4(wh[4], wh[5], wh[6], wh[7]);
+      if (v == 1) {
+        float *neg = (float *)Wv + 3 * n * m + base;
+        *(float4 *)neg = make_float4(-wh[0], -wh[1], -wh[2], -wh[3]);
+        *(float4 *)(neg + 4) = make_float4(-wh[4], -wh[5], -wh[6], -wh[7]);
+      }
     }
   }
 }
@@ -233,6 +245,10 @@ __global__ __launch_bounds__(512, 1) void sba_klgemm_kernel(
       (void *)((const unsigned char *)W + out0 * rowb), (short)0, (int)(a_rows_ok * rowb), RSRC_FLAGS);
   const __amdgpu_buffer_rsrc_t rV = __builtin_amdgcn_make_buffer_rsrc(
       (void *)((const unsigned char *)Wv + out0 * rowb), (short)0, (int)(2 * vstride + a_rows_ok * rowb), RSRC_FLAGS);
+  // the negated width-N copy (Wv[3]), read by the update's second A operand
+  const __amdgpu_buffer_rsrc_t rVn = __builtin_amdgcn_make_buffer_rsrc(
+      (void *)((const unsigned char *)Wv + 3 * (int64_t)vstride + out0 * rowb), (short)0, (int)(a_rows_ok * rowb),
+      RSRC_FLAGS);
   const __amdgpu_buffer_rsrc_t rX = __builtin_amdgcn_make_buffer_rsrc(
       (void *)((const unsigned char *)X + (tok_base + tok0) * (int64_t)rowb), (short)0, (int)(x_rows_ok * rowb),
       RSRC_FLAGS);
@@ -257,7 +273,7 @@ __global__ __launch_bounds__(512, 1) void sba_klgemm_kernel(
     voff[q] = row < rows_ok ? (uint32_t)row * rowb + (uint32_t)(sl * 16) : OOB;
   }
   const __amdgpu_buffer_rsrc_t rMain = kind == 2 ? rX : (kind == 0 ? rW : rV);
-  const __amdgpu_buffer_rsrc_t rUpd = kind == 2 ? rX : rV;
+  const __amdgpu_buffer_rsrc_t rUpd = kind == 2 ? rX : (kind == 0 ? rV : rVn);
   const uint32_t mainBase = kind == 1 ? vstride : 0u;           // A1 of the main phase: variant N
 
   auto issue = [&](int st, unsigned char *buf) __attribute__((always_inline)) {
@@ -285,8 +301,8 @@ __global__ __launch_bounds__(512, 1) void sba_klgemm_kernel(
     const int c0 = ((st - KM) % SPR) * KT;
     const int gu = s_order[r - 1], gd = s_order[k - r];
     // variant of the changing group's new width: N+1 (index 2) going up, N-1 (0) going down
-    const uint32_t vup = kind == 0 ? 2u * vstride : (kind == 1 ? vstride : 0u);
-    const uint32_t vdn = kind == 1 ? vstride : 0u;
+    const uint32_t vup = kind == 0 ? 2u * vstride : 0u;   // A0: N+1 (variant 2); A1: -What^N (rVn); X
+    const uint32_t vdn = 0u;                                // A0: N-1 (variant 0); A1: -What^N; X
     if (g >= KT) {                 // the stage lies inside one of the two groups
       const bool up = c0 < g;
       const uint32_t so = __builtin_amdgcn_readfirstlane(up ? vup + (uint32_t)((gu * g + c0) * ESZ)
@@ -380,8 +396,7 @@ __global__ __launch_bounds__(512, 1) void sba_klgemm_kernel(
         for (int i = 0; i < 2; ++i) {
           b[i] = *(const uint4 *)(Bt + i * 32 * SBP + off);
           a0[i] = *(const uint4 *)(A0 + i * 32 * SBP + off);
-          a1[i] = *(const uint4 *)(A1 + i * 32 * SBP + off);
-          a1[i].x ^= 0x80008000u; a1[i].y ^= 0x80008000u; a1[i].z ^= 0x80008000u; a1[i].w ^= 0x80008000u;
+          a1[i] = *(const uint4 *)(A1 + i * 32 * SBP + off);   // -What^N, stored negated
         }
 #pragma unroll
         for (int ob = 0; ob < 2; ++ob)
@@ -401,7 +416,7 @@ __global__ __launch_bounds__(512, 1) void sba_klgemm_kernel(
         for (int i = 0; i < 2; ++i) {
           b[i] = *(const float *)(Bt + i * 32 * SBP + off);
           a0[i] = *(const float *)(A0 + i * 32 * SBP + off);
-          a1[i] = -*(const float *)(A1 + i * 32 * SBP + off);
+          a1[i] = *(const float *)(A1 + i * 32 * SBP + off);   // -What^N, stored negated
         }
 #pragma unroll
         for (int ob = 0; ob < 2; ++ob)
@@ -616,8 +631,8 @@ __global__ __launch_bounds__(512, 1) void sba_klgemm_kernel(
       unsigned char *dst = nxt + lds_row0 * SBP;
       const int c0 = nsub * KT;
       const int gu = s_order[nr - 1], gd = s_order[k - nr];
-      const uint32_t vup = kind == 0 ? 2u * vstride : (kind == 1 ? vstride : 0u);
-      const uint32_t vdn = kind == 1 ? vstride : 0u;
+      const uint32_t vup = kind == 0 ? 2u * vstride : 0u;
+      const uint32_t vdn = 0u;
       const uint32_t so = __builtin_amdgcn_readfirstlane(c0 < g ? vup + (uint32_t)((gu * g + c0) * ESZ)
                                                                 : vdn + (uint32_t)((gd * g + c0 - g) * ESZ));
 #pragma unroll
@@ -708,8 +723,8 @@ __global__ __launch_bounds__(512, 1) void sba_klgemm_kernel(
       unsigned char *dst = nxt + lds_row0 * SBP;
       const int c0 = nsub * KT;
       const int gu = s_order[nr - 1], gd = s_order[k - nr];
-      const uint32_t vup = kind == 0 ? 2u * vstride : (kind == 1 ? vstride : 0u);
-      const uint32_t vdn = kind == 1 ? vstride : 0u;
+      const uint32_t vup = kind == 0 ? 2u * vstride : 0u;
+      const uint32_t vdn = 0u;
       const uint32_t so = __builtin_amdgcn_readfirstlane(c0 < g ? vup + (uint32_t)((gu * g + c0) * ESZ)
                                                                 : vdn + (uint32_t)((gd * g + c0 - g) * ESZ));
 #pragma unroll
@@ -933,7 +948,7 @@ SbaPlan sba_plan(int64_t t, int64_t n, int64_t m, int group, bool bf16, size_t w
   // Parts that do not depend on the batch size: the trial weights, the order
   // and the per-block partial sums (at most one partly filled block per
   // batch, and at most one batch per token tile, so 2 ceil(t/256) blocks).
-  const size_t fixed = align_up((size_t)3 * n * m * esz, 256) + align_up((size_t)p.k * 4, 256) +
+  const size_t fixed = align_up((size_t)4 * n * m * esz, 256) + align_up((size_t)p.k * 4, 256) +
                        align_up((size_t)2 * ((t + 255) / 256) * p.R * 8, 256);
   // Chunk statistics per token: LSE(y) once, (D, E) per step.  A batch
   // holds at most 4 GB of them (HBM is 288 GB), or what the caller's
@@ -960,7 +975,7 @@ SbaPlan sba_plan(int64_t t, int64_t n, int64_t m, int group, bool bf16, size_t w
   }
   size_t off = 0;
   p.off_wv = off;
-  off += align_up((size_t)3 * n * m * esz, 256);
+  off += align_up((size_t)4 * n * m * esz, 256);   // N-1, N, N+1 and -N
   p.off_order = off;
   off += align_up((size_t)p.k * 4, 256);
   p.off_sp = off;
