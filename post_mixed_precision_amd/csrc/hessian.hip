@@ -293,19 +293,31 @@ __global__ __launch_bounds__(512, 1) void hessian_gram_tr_kernel(const uint16_t 
   };
   // Steady state: the next stage's eight DMA loads go out one after each MFMA
   // of the first K step rather than back to back ahead of it, so the matrix
-  // pipe stays fed while the texture path accepts them.
+  // pipe stays fed while the texture path accepts them; and the twelve
+  // fragment reads of K step k + 1 are spread over the eight MFMAs of K step k
+  // (two after each of the first four, one after each of the rest), so a
+  // wave's next operands are in flight while its own products run instead of
+  // being read between them.
+  auto pin_reads = [&](bool dma) __attribute__((always_inline)) {
+    for (int j = 0; j < 4; ++j) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
+      if (dma) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);   // one DMA load of the next stage
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);   // two fragment reads of the next K step
+    }
+    for (int j = 0; j < 4; ++j) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      if (dma) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+  };
   auto stage_pinned = [&](int64_t t0, const unsigned char *cur, unsigned char *nxt) __attribute__((always_inline)) {
     issue(t0 + HK2, nxt);
     compute(cur);
     __builtin_amdgcn_sched_group_barrier(0x100, 12, 0);     // fragment reads of K step 0
-    for (int j = 0; j < 8; ++j) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
-      __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);   // one DMA load of the next stage
-    }
-    for (int j = 0; j < 3; ++j) {
-      __builtin_amdgcn_sched_group_barrier(0x100, 12, 0);
-      __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
-    }
+    pin_reads(true);
+    pin_reads(false);
+    pin_reads(false);
+    __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);      // K step 3
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
   };
