@@ -1,7 +1,7 @@
 """Parity of the HIP path (through the C ABI) with the CPU oracle.
 
 Each GPU stage is fed the oracle's upstream outputs (never the reverse), so a
-stage is judged on its own; an end-to-end case then runs the whole path on
+stage is checked on its own; an end-to-end case then runs the whole path on
 both sides.  Sizes span several tiles plus ragged tails; the full-size layer
 (4096 x 4096, 262144 tokens, as the benchmark runs it) is checked on sampled
 entries and on properties that hold at any size.
