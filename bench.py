@@ -256,8 +256,10 @@ def decoder_layer_bench(slim, torch, synth, args):
     """The whole 7B-shaped decoder layer: q/k/v/o 4096x4096, gate/up
     11008x4096, down 4096x11008, bf16; one calibration X per input width
     (262144 tokens each), so H is formed once per width and shared by the
-    linears that read it.  A step is both Hessians plus salience, SBA, SQC and
-    packing of all seven linears.  value = total params / 1e6 / seconds."""
+    linears that read it, and so is diag(H_d^-1): the first linear of a width
+    factors H, the others form their group means from its d.  A step is both
+    Hessians and both factorisations plus salience, SBA, SQC and packing of
+    all seven linears.  value = total params / 1e6 / seconds."""
     wl = synth.WORKLOADS["llama7b-decoder-layer"]
     group = args.group or 128
     N = wl.avg_bits
@@ -274,9 +276,15 @@ def decoder_layer_bench(slim, torch, synth, args):
         if ev is not None:
             ev[1].record()
         infos = []
+        hinv_w = {}
         for lin, W in zip(wl.linears, Wd):
             X = Xd[lin.m]
-            hinv, gsal, info, _ = slim.salience(H[lin.m], W, group, 0.01)
+            if lin.m in hinv_w:
+                hinv = hinv_w[lin.m]
+                gsal, info, _ = slim.group_salience(hinv, W, group)
+            else:
+                hinv, gsal, info, _ = slim.salience(H[lin.m], W, group, 0.01)
+                hinv_w[lin.m] = hinv
             bits, kl, rs = slim.sba_search(X, W, gsal, group, N)
             sq = slim.sqc_calibrate(W, bits, hinv, group, 0.1, 50, want_tau=False)
             packed, pinfo = slim.pack(sq["codes"], bits, group, N)
@@ -305,7 +313,8 @@ def decoder_layer_bench(slim, torch, synth, args):
            "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
            "data": "synthetic (seeded; stands in for 128x2048 WikiText2 tokens and LLaMA weights)",
            "config": {"workload": "llama7b-decoder-layer", "linears": [f"{l.name} {l.n}x{l.m}" for l in wl.linears],
-                      "tokens": wl.tokens, "group": group, "avg_bits": N, "hessians": len(Xd)},
+                      "tokens": wl.tokens, "group": group, "avg_bits": N, "hessians": len(Xd),
+                      "factorisations": len(Xd)},
            "hessians_ms": round(h_ms, 3)}
     print(json.dumps(out), flush=True)
 

@@ -10,6 +10,7 @@
  *   slim_hessian        H = 2 X^T X                         (component one, Hessian from calibration)
  *   slim_salience       d = diag((H + a I)^-1), delta = w^2 / d^2, group means   (component one)
  *   slim_salience_u     the same, also writing the upper Cholesky factor of (H + a I)^-1
+ *   slim_group_salience the group means from a d already formed (linears sharing H)
  *   slim_sba_search     balanced bit allocation scored by output KL           (component one)
  *   slim_sba_search_ex  the same with an output-MSE objective or a given group order (ablations)
  *   slim_sqc_calibrate  3-sigma mask + tau-grid search of scale and zero       (component two)
@@ -135,6 +136,24 @@ int slim_salience(const float *H, int64_t m, double damp_frac, const void *W, in
 int slim_salience_u(const float *H, int64_t m, double damp_frac, const void *W, int wdt, int64_t n,
                     int group, float *hinv_diag, double *group_sal, float *elem_sal, double *U,
                     int32_t *info, void *ws, size_t ws_bytes, void *stream);
+
+/* The group-salience half of slim_salience, from a hinv_diag already formed:
+ * delta and group_sal exactly as slim_salience forms them from its own
+ * hinv_diag, so for the same hinv_diag and W the results are bit-identical.
+ * H comes from a layer's input activations (component one), so the linears
+ * that read the same input share H and d: one slim_salience per input width
+ * gives hinv_diag, and the other linears of that width call this instead of
+ * factoring H again.
+ * hinv_diag: float32 [m] (slim_salience's, or any positive d).  W: [n, m] in
+ * dtype wdt.  group_sal: float64 [m/group].  elem_sal: optional float32
+ * [n, m] (NULL = skip).  info: device int32, written 0, or -1 if W holds a
+ * non-finite value (then group_sal is unspecified).
+ * Requires n >= 1, m >= 1, m % group == 0.
+ */
+size_t slim_group_salience_workspace(int64_t n, int64_t m, int group);
+int slim_group_salience(const float *hinv_diag, int64_t m, const void *W, int wdt, int64_t n, int group,
+                        double *group_sal, float *elem_sal, int32_t *info, void *ws, size_t ws_bytes,
+                        void *stream);
 
 /* ------------------------------------------------------------------------
  * SBA search (component one: bit-widths minimise the KL divergence of the

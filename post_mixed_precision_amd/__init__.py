@@ -17,11 +17,11 @@ hand-written HIP kernels:
 ``quantize_layer`` chains them on the current stream.  PyTorch only provides
 device memory and the stream.
 """
-from ._lib import (SlimError, load_library, hessian, salience, sba_search, sba_search_ex, sqc_calibrate, gptq_quantize,
+from ._lib import (SlimError, load_library, hessian, salience, group_salience, sba_search, sba_search_ex, sqc_calibrate, gptq_quantize,
                    lwc_calibrate, pack, qlinear, qlinear_noalloc, tau_table,
                    timing_enable, timing_select, timing_reset, timing_read, SLIM_F32, SLIM_BF16)
 from .layer import quantize_layer
 
-__all__ = ["SlimError", "load_library", "hessian", "salience", "sba_search", "sba_search_ex", "sqc_calibrate",
+__all__ = ["SlimError", "load_library", "hessian", "salience", "group_salience", "sba_search", "sba_search_ex", "sqc_calibrate",
            "gptq_quantize", "lwc_calibrate", "pack", "qlinear", "qlinear_noalloc", "tau_table", "timing_enable", "timing_select", "timing_reset", "timing_read", "quantize_layer", "SLIM_F32",
            "SLIM_BF16"]

@@ -32,6 +32,9 @@ _SIGS = {
                                _c_vp, _c_vp, _c_sz, _c_vp]),
     "slim_salience_u": (_c_int, [_c_vp, _c_i64, _c_dbl, _c_vp, _c_int, _c_i64, _c_int, _c_vp, _c_vp, _c_vp,
                                  _c_vp, _c_vp, _c_vp, _c_sz, _c_vp]),
+    "slim_group_salience_workspace": (_c_sz, [_c_i64, _c_i64, _c_int]),
+    "slim_group_salience": (_c_int, [_c_vp, _c_i64, _c_vp, _c_int, _c_i64, _c_int, _c_vp, _c_vp, _c_vp, _c_vp,
+                                     _c_sz, _c_vp]),
     "slim_sba_workspace": (_c_sz, [_c_i64, _c_i64, _c_i64, _c_int, _c_int]),
     "slim_sba_search": (_c_int, [_c_vp, _c_int, _c_i64, _c_vp, _c_int, _c_i64, _c_i64, _c_int, _c_vp, _c_int,
                                  _c_vp, _c_vp, _c_vp, _c_vp, _c_sz, _c_vp]),
@@ -238,6 +241,26 @@ def salience(H, W, group: int, damp_frac: float = 0.01, elem: bool = False, want
     check(lib.slim_salience(_ptr(H), m, float(damp_frac), _ptr(W), _dtype_code(W), n, group, _ptr(hinv), _ptr(gsal),
                             _ptr(esal), _ptr(info), _ptr(ws), ws.numel(), _stream(W.device)), "slim_salience")
     return hinv, gsal, info, esal
+
+
+def group_salience(hinv, W, group: int, elem: bool = False):
+    """-> (group_sal f64 [k], info i32 [1], elem_sal f32 [n, m] or None) from a
+    hinv_diag f32 [m] already formed (slim_group_salience): for the linears that
+    share an input width, and so H, with the one that called salience()."""
+    torch = _torch()
+    lib = load_library()
+    W = _arg(W, "W", (None, None), _float_types())
+    n, m = W.shape
+    k = _group_count(m, group)
+    hinv = _arg(hinv, "hinv", (m,), (torch.float32,))
+    _on_gpu(hinv, W)
+    gsal = torch.empty(k, dtype=torch.float64, device=W.device)
+    info = torch.zeros(1, dtype=torch.int32, device=W.device)
+    esal = torch.empty((n, m), dtype=torch.float32, device=W.device) if elem else None
+    ws = _ws(lib.slim_group_salience_workspace(n, m, group), W.device)
+    check(lib.slim_group_salience(_ptr(hinv), m, _ptr(W), _dtype_code(W), n, group, _ptr(gsal), _ptr(esal),
+                                  _ptr(info), _ptr(ws), ws.numel(), _stream(W.device)), "slim_group_salience")
+    return gsal, info, esal
 
 
 def sba_search(X, W, group_sal, group: int, avg_bits: int, ws_bytes: int | None = None):

@@ -163,6 +163,27 @@ int slim_salience_u(const float *H, int64_t m, double damp_frac, const void *W, 
   return e == hipSuccess ? SLIM_OK : hip_fail(e);
 }
 
+size_t slim_group_salience_workspace(int64_t n, int64_t m, int group) {
+  if (n < 1 || m < 1 || m > SLIM_MAX_WIDTH || !valid_group(group) || m % group) return 0;
+  return slim::group_salience_ws_bytes(n, m, group);
+}
+
+int slim_group_salience(const float *hinv_diag, int64_t m, const void *W, int wdt, int64_t n, int group,
+                        double *group_sal, float *elem_sal, int32_t *info, void *ws, size_t ws_bytes,
+                        void *stream) {
+  if (!hinv_diag || !W || !group_sal || !info) return SLIM_E_NULL;
+  if (!valid_dtype(wdt)) return SLIM_E_DTYPE;
+  if (n < 1 || m < 1 || m > SLIM_MAX_WIDTH) return SLIM_E_SHAPE;
+  if (!valid_group(group) || m % group) return SLIM_E_SHAPE;
+  if (!aligned16(W) || !aligned16(hinv_diag)) return SLIM_E_ALIGN;
+  const size_t need = slim::group_salience_ws_bytes(n, m, group);
+  if (!ws || ws_bytes < need) return SLIM_E_WORKSPACE;
+  if (!aligned16(ws)) return SLIM_E_ALIGN;
+  hipError_t e = slim::launch_group_salience(hinv_diag, m, W, wdt == SLIM_BF16, n, group, group_sal, elem_sal, info,
+                                             ws, (hipStream_t)stream);
+  return e == hipSuccess ? SLIM_OK : hip_fail(e);
+}
+
 // ---------------------------------------------------------------- SBA
 size_t slim_sba_workspace(int64_t t, int64_t n, int64_t m, int group, int dtype) {
   if (t < 1 || n < 1 || m < 1 || m > SLIM_MAX_WIDTH || !valid_group(group) || m % group || !valid_dtype(dtype))

@@ -40,6 +40,9 @@ hipError_t launch_chol_inverse(const float *H, int64_t m, double damp, bool reve
 hipError_t launch_salience(const float *H, int64_t m, double damp, const void *W, bool bf16,
                            int64_t n, int group, float *hinv, double *gsal, float *esal,
                            double *U, int32_t *info, void *ws, hipStream_t st);
+size_t group_salience_ws_bytes(int64_t n, int64_t m, int group);
+hipError_t launch_group_salience(const float *hinv, int64_t m, const void *W, bool bf16, int64_t n, int group,
+                                 double *gsal, float *esal, int32_t *info, void *ws, hipStream_t st);
 
 // ---- SBA ----
 struct SbaPlan {

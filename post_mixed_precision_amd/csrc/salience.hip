@@ -739,6 +739,8 @@ __global__ __launch_bounds__(256) void sal_group_final_kernel(const double *__re
   gsal[j] = s / denom;
 }
 
+__global__ void sal_info_zero_kernel(int32_t *__restrict__ info) { *info = 0; }
+
 static int64_t pad64(int64_t m) { return (m + NBK - 1) / NBK * NBK; }
 
 // Panels per group of the sweep (see launch_chol_inverse), by the number of
@@ -805,12 +807,24 @@ hipError_t launch_chol_inverse(const float *H, int64_t m, double damp, bool reve
   return hipGetLastError();
 }
 
+// delta per element, float64 partial sums per (64-row block, group), then the
+// group means over the blocks in block order
+static void launch_group_means(const float *hinv, int64_t m, const void *W, bool bf16, int64_t n, int group,
+                               double *gsal, float *esal, int32_t *info, double *part, hipStream_t st) {
+  const int64_t nrb = (n + 63) / 64;
+  const int k = (int)(m / group);
+  dim3 grid(k, (unsigned)nrb);
+  if (bf16)
+    sal_group_partial_kernel<true><<<grid, 256, 0, st>>>(W, n, m, group, hinv, esal, part, info);
+  else
+    sal_group_partial_kernel<false><<<grid, 256, 0, st>>>(W, n, m, group, hinv, esal, part, info);
+  sal_group_final_kernel<<<(k + 255) / 256, 256, 0, st>>>(part, (int)nrb, k, (double)n * group, gsal);
+}
+
 hipError_t launch_salience(const float *H, int64_t m, double damp, const void *W, bool bf16, int64_t n, int group,
                            float *hinv, double *gsal, float *esal, double *U, int32_t *info, void *ws,
                            hipStream_t st) {
   const int64_t mp = pad64(m);
-  const int64_t nrb = (n + 63) / 64;
-  const int k = (int)(m / group);
   char *base = (char *)ws;
   size_t off = 0;
   double *A = (double *)(base + off);
@@ -838,12 +852,19 @@ hipError_t launch_salience(const float *H, int64_t m, double damp, const void *W
     sal_u_out_kernel<<<(unsigned)blocks, 256, 0, st>>>(Z, mp, m, U);
   }
   sal_hinv_out_kernel<<<(unsigned)((m + 255) / 256), 256, 0, st>>>(d, m, hinv, rev ? 1 : 0);
-  dim3 grid(k, (unsigned)nrb);
-  if (bf16)
-    sal_group_partial_kernel<true><<<grid, 256, 0, st>>>(W, n, m, group, hinv, esal, part, info);
-  else
-    sal_group_partial_kernel<false><<<grid, 256, 0, st>>>(W, n, m, group, hinv, esal, part, info);
-  sal_group_final_kernel<<<(k + 255) / 256, 256, 0, st>>>(part, (int)nrb, k, (double)n * group, gsal);
+  launch_group_means(hinv, m, W, bf16, n, group, gsal, esal, info, part, st);
+  return hipGetLastError();
+}
+
+size_t group_salience_ws_bytes(int64_t n, int64_t m, int group) {
+  return align_up((size_t)((n + 63) / 64) * (size_t)(m / group) * 8, 256);
+}
+
+hipError_t launch_group_salience(const float *hinv, int64_t m, const void *W, bool bf16, int64_t n, int group,
+                                 double *gsal, float *esal, int32_t *info, void *ws, hipStream_t st) {
+  // a kernel rather than a memset, so that the call can sit in a captured graph
+  sal_info_zero_kernel<<<1, 1, 0, st>>>(info);
+  launch_group_means(hinv, m, W, bf16, n, group, gsal, esal, info, (double *)ws, st);
   return hipGetLastError();
 }
 

@@ -97,6 +97,22 @@ def test_salience_u_validation(lib):
     assert call(U=ctypes.c_void_p(4100)) == -7
 
 
+def test_group_salience_validation(lib):
+    def call(**kw):
+        return lib.slim_group_salience(kw.get("hinv", FAKE), kw.get("m", 256), kw.get("W", FAKE), kw.get("wdt", 1),
+                                       kw.get("n", 64), kw.get("g", 128), kw.get("gsal", FAKE), None,
+                                       kw.get("info", FAKE), FAKE, kw.get("ws", 1 << 40), None)
+    assert call(hinv=None) == -1 and call(W=None) == -1 and call(gsal=None) == -1 and call(info=None) == -1
+    assert call(wdt=3) == -3
+    assert call(m=200) == -2 and call(g=96) == -2 and call(n=0) == -2 and call(m=0) == -2
+    assert call(ws=16) == -5
+    assert call(hinv=ctypes.c_void_p(4100)) == -7
+    # one float64 partial per (64-row block, group), rounded up to 256 bytes
+    assert lib.slim_group_salience_workspace(130, 256, 128) == 256
+    assert lib.slim_group_salience_workspace(64 * 40, 4096, 32) == 40 * 128 * 8
+    assert lib.slim_group_salience_workspace(64, 250, 128) == 0
+
+
 def test_sba_validation(lib):
     def call(**kw):
         return lib.slim_sba_search(FAKE, kw.get("xdt", 1), kw.get("t", 100), FAKE, kw.get("wdt", 1),

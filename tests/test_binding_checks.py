@@ -55,6 +55,13 @@ def test_salience_checks(L):
     raises(L, lambda: L.salience(f32(128, 128), bf(8, 256), 128), "H", "shape")
 
 
+def test_group_salience_checks(L):
+    raises(L, lambda: L.group_salience(f32(255), bf(8, 256), 128), "hinv", "shape")
+    raises(L, lambda: L.group_salience(torch.zeros(256, dtype=torch.float64), bf(8, 256), 128), "hinv", "dtype")
+    raises(L, lambda: L.group_salience(f32(256), bf(8, 256), 96), "group")
+    raises(L, lambda: L.group_salience(f32(256), bf(8, 256), 128), "GPU")
+
+
 def test_sba_checks(L):
     X, W, S = bf(32, 256), bf(8, 256), torch.zeros(2, dtype=torch.float64)
     raises(L, lambda: L.sba_search(X, bf(8, 384), S, 128, 2), "W", "shape")

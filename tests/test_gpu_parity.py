@@ -126,6 +126,52 @@ def test_salience_failure_codes(slim):
     assert int(info2.item()) == -1
 
 
+@pytest.mark.parametrize("n1,n2,m,g,dtype", [
+    (512, 130, 512, 128, "bf16"),    # the second linear with ragged row blocks
+    (64, 200, 384, 64, "f32"),
+    (70, 1, 160, 32, "bf16"),        # one row; width not a multiple of 64
+])
+def test_group_salience_shared_h(slim, n1, n2, m, g, dtype):
+    # two linears reading one input share H and d: the group means from the
+    # first linear's d equal what a full salience call gives for the second
+    print(f"group salience from a shared d: n1={n1} n2={n2} m={m} g={g} {dtype}", flush=True)
+    wl, X, W1 = _case_inputs(1200, n1, m, dtype, wid=58)
+    W2 = synth.make_w(synth.custom(tokens=8, dtype=dtype, n=n2, m=m, dist="t5", wid=59), 0)
+    Ho = oracle.hessian(X).astype(np.float32)
+    Hd = dev(Ho, torch, False)
+    W1d, W2d = dev(W1, torch, dtype == "bf16"), dev(W2, torch, dtype == "bf16")
+    hinv, gsal1, info1, esal1 = slim.salience(Hd, W1d, g, 0.01, elem=True)
+    _, gsal2, info2, esal2 = slim.salience(Hd, W2d, g, 0.01, elem=True)
+    gsal1s, infos1, esal1s = slim.group_salience(hinv, W1d, g, elem=True)
+    gsal2s, infos2, esal2s = slim.group_salience(hinv, W2d, g, elem=True)
+    _sync()
+    assert int(info1.item()) == int(info2.item()) == int(infos1.item()) == int(infos2.item()) == 0
+    # bit-identical to the full call: the same d, the same kernels
+    assert np.array_equal(host(gsal1s), host(gsal1)) and np.array_equal(host(esal1s), host(esal1))
+    assert np.array_equal(host(gsal2s), host(gsal2)) and np.array_equal(host(esal2s), host(esal2))
+    # and the oracle's group means from that d
+    d32 = host(hinv)
+    S_o = oracle.group_salience(oracle.element_salience(W2, d32), g)
+    assert rel_err(host(gsal2s), S_o) <= 1e-6
+    np.testing.assert_array_equal(host(esal2s), oracle.element_salience(W2, d32))
+
+
+def test_group_salience_info(slim):
+    # a non-finite weight sets info to -1; the next clean call writes 0 again
+    m, n, g = 256, 16, 64
+    rng = np.random.default_rng(3)
+    d32 = (rng.random(m) + 0.5).astype(np.float32)
+    W = rng.standard_normal((n, m)).astype(np.float32)
+    W_bad = W.copy()
+    W_bad[5, 77] = np.inf
+    hd = torch.from_numpy(d32).to("cuda:0")
+    _, info_bad, _ = slim.group_salience(hd, torch.from_numpy(W_bad).to("cuda:0"), g)
+    gsal, info, _ = slim.group_salience(hd, torch.from_numpy(W).to("cuda:0"), g)
+    _sync()
+    assert int(info_bad.item()) == -1 and int(info.item()) == 0
+    assert rel_err(host(gsal), oracle.group_salience(oracle.element_salience(W, d32), g)) <= 1e-6
+
+
 # ----------------------------------------------------------------- SBA
 def _sba_check(slim, X, W, S, g, N, storage, kl_rtol=1e-3):
     bits, kl, rs = slim.sba_search(dev(X, torch, storage == "bf16"), dev(W, torch, storage == "bf16"),
@@ -302,6 +348,24 @@ def test_end_to_end_tiny_layer(slim):
         compare_sqc(g_out, ref["sqc"], 128)
         if (g_out["codes"] == ref["sqc"]["codes"]).all():
             np.testing.assert_array_equal(host(res["packed"]).view(np.uint32), ref["packed"])
+
+
+def test_end_to_end_shared_factor(slim):
+    # a second linear of the same input width through quantize_layer with the
+    # first one's H and d: the same outputs as with the factorisation redone
+    wl = synth.WORKLOADS["tiny-512"]
+    X, W = synth.make_x(wl, 512), synth.make_w(wl, 0)
+    W2 = synth.make_w(synth.custom(tokens=8, dtype="f32", n=384, m=512, dist="t5", wid=60), 0)
+    Xd = dev(X, torch, False)
+    first = slim.quantize_layer(Xd, dev(W, torch, False), 128, 2)
+    shared = slim.quantize_layer(Xd, dev(W2, torch, False), 128, 2, H=first["H"], hinv=first["hinv"])
+    own = slim.quantize_layer(Xd, dev(W2, torch, False), 128, 2, H=first["H"])
+    _sync()
+    assert int(shared["info"].item()) == 0 and int(own["info"].item()) == 0
+    for key in ("hinv", "group_sal", "bits", "kl", "scale", "zero", "codes", "mask", "packed"):
+        assert np.array_equal(host(shared[key]), host(own[key])), key
+    with pytest.raises(slim.SlimError):
+        slim.quantize_layer(Xd, dev(W2, torch, False), 128, 2, hinv=first["hinv"])
 
 
 def test_end_to_end_tiny_layer_gptq_backbone(slim):
