@@ -398,13 +398,17 @@ __global__ __launch_bounds__(512, 1) void sba_klgemm_kernel(
           a0[i] = *(const uint4 *)(A0 + i * 32 * SBP + off);
           a1[i] = *(const uint4 *)(A1 + i * 32 * SBP + off);   // -What^N, stored negated
         }
+        // all four blocks' W_new products, then their -W_N products: a block's
+        // two products sit four MFMAs apart instead of back to back, where the
+        // second waited for the first's result
 #pragma unroll
         for (int ob = 0; ob < 2; ++ob)
 #pragma unroll
-          for (int tb = 0; tb < 2; ++tb) {
-            accQ[ob * 2 + tb] = mfma_bf16(a0[ob], b[tb], accQ[ob * 2 + tb]);
-            accQ[ob * 2 + tb] = mfma_bf16(a1[ob], b[tb], accQ[ob * 2 + tb]);
-          }
+          for (int tb = 0; tb < 2; ++tb) accQ[ob * 2 + tb] = mfma_bf16(a0[ob], b[tb], accQ[ob * 2 + tb]);
+#pragma unroll
+        for (int ob = 0; ob < 2; ++ob)
+#pragma unroll
+          for (int tb = 0; tb < 2; ++tb) accQ[ob * 2 + tb] = mfma_bf16(a1[ob], b[tb], accQ[ob * 2 + tb]);
       }
     } else {
 #pragma unroll 4
@@ -418,13 +422,17 @@ __global__ __launch_bounds__(512, 1) void sba_klgemm_kernel(
           a0[i] = *(const float *)(A0 + i * 32 * SBP + off);
           a1[i] = *(const float *)(A1 + i * 32 * SBP + off);   // -What^N, stored negated
         }
+        // all four blocks' W_new products, then their -W_N products: a block's
+        // two products sit four MFMAs apart instead of back to back, where the
+        // second waited for the first's result
 #pragma unroll
         for (int ob = 0; ob < 2; ++ob)
 #pragma unroll
-          for (int tb = 0; tb < 2; ++tb) {
-            accQ[ob * 2 + tb] = mfma_f32(a0[ob], b[tb], accQ[ob * 2 + tb]);
-            accQ[ob * 2 + tb] = mfma_f32(a1[ob], b[tb], accQ[ob * 2 + tb]);
-          }
+          for (int tb = 0; tb < 2; ++tb) accQ[ob * 2 + tb] = mfma_f32(a0[ob], b[tb], accQ[ob * 2 + tb]);
+#pragma unroll
+        for (int ob = 0; ob < 2; ++ob)
+#pragma unroll
+          for (int tb = 0; tb < 2; ++tb) accQ[ob * 2 + tb] = mfma_f32(a1[ob], b[tb], accQ[ob * 2 + tb]);
       }
     }
   };
