@@ -200,22 +200,73 @@ constexpr int HROW2 = HT2 * 2;             // bytes per LDS token row of one ope
 constexpr int HOP2 = HK2 * HROW2;          // bytes of one operand per stage (32 KB)
 constexpr uint32_t HOOB = 0x7ffffff0u;     // buffer offset that reads as zero
 
+// Work item of workgroup L of the 1-D grid.  Workgroups go to the eight XCDs
+// round-robin (L % 8), and each XCD has its own L2.  The lower tiles are put
+// in stripe order (stripes of HXS block columns; within a stripe, rows top to
+// bottom and columns left to right) and cut into eight clusters of
+// consecutive tiles; the work items are listed cluster by cluster, each
+// cluster split by split.  XCD x takes the x-th eighth of that list, so the
+// workgroups running together on it read one token range and a compact set of
+// column blocks (14-22 (split, block) pairs for its first 32 items at m = 4096
+// to 11008, against 23-31 with tiles dealt out round-robin), and no XCD has
+// more than one item more than another.  Returns false for the grid's padding.
+constexpr int HXS = 8;
+__device__ __forceinline__ bool hess_item(int L, int nb, int ntiles, int nsplit, int &bi, int &bj, int &split) {
+  const int x = L & 7, s = L >> 3;
+  const int W = ntiles * nsplit;
+  if (s >= (W >> 3) + (x < (W & 7) ? 1 : 0)) return false;
+  const int g = x * (W >> 3) + min(x, W & 7) + s;   // position in the item list
+  const int base = ntiles >> 3, rem = ntiles & 7;
+  int c = 0, first = 0, tx = base + (rem > 0 ? 1 : 0);
+  while (g >= first + tx * nsplit) {               // the cluster holding item g
+    first += tx * nsplit;
+    ++c;
+    tx = base + (c < rem ? 1 : 0);
+  }
+  const int u = g - first;
+  split = u / tx;
+  int p = c * base + min(c, rem) + u % tx;         // position in stripe order
+  for (int J0 = 0; J0 < nb; J0 += HXS) {
+    const int w = min(HXS, nb - J0);               // stripe width
+    const int tri = w * (w + 1) / 2;               // tiles in the stripe's first w rows
+    const int cnt = tri + (nb - J0 - w) * w;
+    if (p < cnt) {
+      if (p < tri) {
+        int r = 0;
+        while ((r + 1) * (r + 2) / 2 <= p) ++r;
+        bi = J0 + r;
+        bj = J0 + p - r * (r + 1) / 2;
+      } else {
+        const int q = p - tri;
+        bi = J0 + w + q / w;
+        bj = J0 + q % w;
+      }
+      return true;
+    }
+    p -= cnt;
+  }
+  return false;
+}
+
 typedef short v4i16_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) v4i16_t lds_v4i16_t;
 typedef __attribute__((address_space(3))) void lds_void2_t;
 
 __global__ __launch_bounds__(512, 1) void hessian_gram_tr_kernel(const uint16_t *__restrict__ X, int64_t T,
                                                                  int64_t m, int64_t tok_per_split, int ntiles,
-                                                                 float *__restrict__ part) {
+                                                                 float *__restrict__ part, int nsplit) {
   __shared__ __attribute__((aligned(16))) unsigned char lds0[2 * HOP2];
   __shared__ __attribute__((aligned(16))) unsigned char lds1[2 * HOP2];
-  // workgroup (x, y) = (lower tile, token split), tiles varying fastest.  Both
-  // come from the grid rather than from a division of one id: a quotient made
-  // on the vector unit stays in a vector register, and a buffer descriptor
-  // built from it (the token range below) would need a waterfall loop per load.
-  const int tile = (int)blockIdx.x, split = (int)blockIdx.y;
-  int bi, bj;
-  tri_decode(tile, bi, bj);
+  // (tile, token split) from the XCD-aware walk.  The divisions in it may run
+  // on the vector unit; the results are read back as scalars, since a buffer
+  // descriptor built from a vector register (the token range below) would need
+  // a waterfall loop per load.
+  int bi, bj, split;
+  if (!hess_item((int)blockIdx.x, (int)((m + HT2 - 1) / HT2), ntiles, nsplit, bi, bj, split)) return;
+  bi = __builtin_amdgcn_readfirstlane(bi);
+  bj = __builtin_amdgcn_readfirstlane(bj);
+  split = __builtin_amdgcn_readfirstlane(split);
+  const int tile = bi * (bi + 1) / 2 + bj;
   const int64_t tbeg = (int64_t)split * tok_per_split;
   const int64_t tend = min(T, tbeg + tok_per_split);
   const int tid = threadIdx.x, lane = tid & 63;
@@ -442,8 +493,8 @@ hipError_t launch_hessian(const void *X, bool bf16, int64_t t, int64_t m, float 
   const unsigned grid = (unsigned)(p.ntiles * p.nsplit);
   timer_begin(K_HESSIAN, st);
   if (p.tr) {
-    hessian_gram_tr_kernel<<<dim3(p.ntiles, p.nsplit), 512, 0, st>>>((const uint16_t *)X, t, m, p.tok_per_split,
-                                                                   p.ntiles, part);
+    hessian_gram_tr_kernel<<<dim3(8 * ((p.ntiles * p.nsplit + 7) / 8)), 512, 0, st>>>(
+        (const uint16_t *)X, t, m, p.tok_per_split, p.ntiles, part, p.nsplit);
   } else {
     const bool aligned = bf16 ? (m % 8 == 0) : (m % 4 == 0);
     if (bf16)
