@@ -49,6 +49,7 @@ def _case_inputs(T, n, m, dtype, dist="normal", wid=50, avg_bits=2):
     (1, 33, "f32"),          # single token
     (20000, 768, "bf16"),    # 256-wide tiles, several token splits
     (4100, 520, "bf16"),     # ragged 256-tile and ragged last split
+    (30000, 2312, "bf16"),   # 10 block columns (the last one 8 wide): 55 tiles over two stripes, several splits
 ])
 def test_hessian_parity(slim, T, m, dtype):
     print(f"hessian T={T} m={m} {dtype}", flush=True)
