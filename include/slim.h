@@ -304,14 +304,16 @@ int slim_gptq_quantize_u(const double *U, int64_t m, const void *W, int wdt, int
  * 0.999, eps 1e-8, learning rate lr) on the layer's output MSE over the
  * t_tokens calibration tokens, L = tr((W - W_hat) H (W - W_hat)^T) / (2 t),
  * through a straight-through rounding (no gradient where the clamp holds).
- * H is the slim_hessian output for those tokens (float32 [m, m]).  Then the
+ * H is the slim_hessian output for those tokens (float32 [m, m], symmetric;
+ * only the lower triangle is read).  Then the
  * clipped range is rounded once to float32 and SQC's float32 min-max
  * quantizer at tau = 1 gives scale, zero (float32 [n, k]) and codes (uint8
  * [n, m]), which slim_pack and slim_qlinear take as they take SQC's.
  * loss: float64 [iters + 1], L before each step and after the last;
  * logits: float64 [2, n, k] (gamma, then beta) or NULL.  W: [n, m] in dtype
  * wdt.  Requires 0 <= iters <= SLIM_LWC_MAX_ITERS, lr > 0.  Workspace:
- * slim_lwc_workspace(n, m, g, iters) bytes (two float64 [n, m] matrices and
+ * slim_lwc_workspace(n, m, g, iters) bytes (float64 copies of W - W_hat and
+ * of H, padded to multiples of 64, the float64 product [n, m], and
  * per-segment state).
  * ---------------------------------------------------------------------- */
 #define SLIM_LWC_MAX_ITERS 10000

@@ -83,7 +83,7 @@ hipError_t launch_gptq(const float *H, const double *Ugiven, int64_t m, double d
 // ---- Learnable weight clipping (SliM-LLM+) ----
 struct LwcPlan {
   int64_t nblk;              // per-segment kernel blocks (16 segments each)
-  size_t off_D, off_P, off_st, off_part, ws_bytes;
+  size_t off_D, off_Hd, off_P, off_st, off_part, ws_bytes;
 };
 LwcPlan lwc_plan(int64_t n, int64_t m, int group, int iters);
 hipError_t launch_lwc(const void *W, bool bf16, int64_t n, int64_t m, int group, const int8_t *bits, const float *H,

@@ -116,9 +116,10 @@ __global__ __launch_bounds__(256) void lwc_init_kernel(const void *__restrict__ 
   st[9 * nseg + seg] = p.z;
 }
 
-// D = W - W_hat (float64 [n, m]) for the current segment parameters.
+// D = W - W_hat for the current segment parameters, float64 with row stride
+// md (the width padded to 64; the padding stays zero).
 __global__ __launch_bounds__(256) void lwc_forward_kernel(const void *__restrict__ W, bool bf16, int64_t n, int64_t m,
-                                                          int g, const int8_t *__restrict__ bits,
+                                                          int64_t md, int g, const int8_t *__restrict__ bits,
                                                           const double *__restrict__ st, double *__restrict__ D) {
   const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (e >= n * m) return;
@@ -133,42 +134,61 @@ __global__ __launch_bounds__(256) void lwc_forward_kernel(const void *__restrict
   u = u + z;
   const double q = fmin(fmax(rint(u), 0.0), maxq);
   const double wh = (q - z) * s;
-  D[e] = w - wh;
+  D[i * md + col] = w - wh;
 }
 
-// P = D H: D float64 [n, m], H float32 [m, m] (symmetric; widened exactly),
-// 64 x 64 output tiles on the float64 matrix cores, K = m in chunks of 64 with
-// the next chunk's operands loaded into registers during the current product.
-__global__ __launch_bounds__(256) void lwc_dh_kernel(const double *__restrict__ D, const float *__restrict__ H,
-                                                     int64_t n, int64_t m, double *__restrict__ P) {
-  __shared__ double sA[NBK * SP];
-  __shared__ double sB[NBK * SP];
+// Hd = H widened to float64 (exact) from its lower triangle, so that Hd is
+// symmetric, padded with zeros to [md, md]; and D's padding zeroed (the
+// forward writes only its n x m part).
+__global__ __launch_bounds__(256) void lwc_prep_kernel(const float *__restrict__ H, int64_t m, int64_t n, int64_t md,
+                                                       int64_t nd, double *__restrict__ Hd, double *__restrict__ D) {
+  const int64_t stride = (int64_t)gridDim.x * 256;
+  for (int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x; e < md * md; e += stride) {
+    const int64_t r = e / md, c = e % md;
+    Hd[e] = (r < m && c < m) ? (double)H[max(r, c) * m + min(r, c)] : 0.0;
+  }
+  for (int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x; e < nd * md; e += stride) {
+    const int64_t r = e / md, c = e % md;
+    if (r >= n || c >= m) D[e] = 0.0;
+  }
+}
+
+// P = D H (float64 [n, m]).  H is symmetric, so P[r][c] is row r of D
+// against row c of Hd, K contiguous in both: 64 x 64 output tiles on the
+// float64 matrix cores, both operands DMA'd straight to LDS half a 64-wide
+// panel (K = 32) at a time into one of two buffers, the next half's loads
+// beside the current half's products; two workgroups per CU; tiles in
+// row-major order, a contiguous run per XCD, so an XCD's tiles share D's row
+// block in its L2.  Each accumulator takes the products in K order, four k per
+// MFMA, as the register-staged version did, so P is the same bit for bit.
+__global__ __launch_bounds__(256, 2) void lwc_dh_kernel(const double *__restrict__ D, const double *__restrict__ Hd,
+                                                        int64_t n, int64_t m, int64_t md, int64_t ncb, int64_t total,
+                                                        double *__restrict__ P) {
+  __shared__ __attribute__((aligned(16))) unsigned char l0[2 * HP_BYTES];
+  __shared__ __attribute__((aligned(16))) unsigned char l1[2 * HP_BYTES];
+  const int64_t item = xcd_item(blockIdx.x, total);
+  if (item < 0) return;
+  const int64_t r0 = (item / ncb) * NBK, c0 = (item % ncb) * NBK;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
-  const int64_t r0 = (int64_t)blockIdx.x * NBK;
-  const int64_t col0 = (int64_t)blockIdx.y * NBK;
-  const int64_t nk = (m + NBK - 1) / NBK;
-  double ra[16], rb[16];
-  auto load = [&](int64_t kc) __attribute__((always_inline)) {
-#pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      const int idx = tid + e * 256;
-      const int hi = idx >> 6, lo = idx & 63;
-      const int64_t kk = kc * NBK + lo, kr = kc * NBK + hi;
-      ra[e] = (r0 + hi < n && kk < m) ? D[(r0 + hi) * m + kk] : 0.0;
-      rb[e] = (kr < m && col0 + lo < m) ? (double)H[kr * m + col0 + lo] : 0.0;
-    }
+  auto issue = [&](int h, unsigned char *buf) __attribute__((always_inline)) {
+    const int64_t k0 = 32 * (int64_t)h;
+    load_half<0>(D + r0 * md + k0, md, buf);
+    load_half<0>(Hd + c0 * md + k0, md, buf + HP_BYTES);
   };
   f64x4_t acc[2][2];
   zero_acc(acc);
-  load(0);
-  for (int64_t kc = 0; kc < nk; ++kc) {
-    if (kc) __syncthreads();
-    stash_T(sA, ra, tid);     // sA[k][row] = D[row][k]
-    stash_N(sB, rb, tid);     // sB[k][col] = H[k][col]
+  const int nh = (int)(md / 32);   // even
+  issue(0, l0);
+  for (int h = 0; h < nh; h += 2) {
+    __builtin_amdgcn_s_waitcnt(0);   // this thread's loads of half h have landed
+    __syncthreads();                 // everyone's; and l1's previous products are done
+    issue(h + 1, l1);
+    gemm_half<false>(l0, l0 + HP_BYTES, acc, lane, wm, wn);
+    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    if (kc + 1 < nk) load(kc + 1);
-    gemm64(sA, sB, acc, lane, wm, wn);
+    if (h + 2 < nh) issue(h + 2, l0);
+    gemm_half<false>(l1, l1 + HP_BYTES, acc, lane, wm, wn);
   }
 #pragma unroll
   for (int a = 0; a < 2; ++a)
@@ -177,7 +197,7 @@ __global__ __launch_bounds__(256) void lwc_dh_kernel(const double *__restrict__ 
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
         const int64_t row = r0 + wm * 32 + a * 16 + 4 * v + (lane >> 4);
-        const int64_t col = col0 + wn * 32 + b * 16 + (lane & 15);
+        const int64_t col = c0 + wn * 32 + b * 16 + (lane & 15);
         if (row < n && col < m) P[row * m + col] = acc[a][b][v];
       }
 }
@@ -186,7 +206,7 @@ __global__ __launch_bounds__(256) void lwc_dh_kernel(const double *__restrict__ 
 // 0) one Adam step, then the parameters for the next forward.  Each block
 // writes the sum of its segments' loss partials to part[blockIdx.x].
 __global__ __launch_bounds__(256) void lwc_step_kernel(const void *__restrict__ W, bool bf16, int64_t n, int64_t m,
-                                                       int g, const int8_t *__restrict__ bits,
+                                                       int64_t md, int g, const int8_t *__restrict__ bits,
                                                        const double *__restrict__ D, const double *__restrict__ P,
                                                        double T, int step, double lr, double *__restrict__ st,
                                                        double *__restrict__ part) {
@@ -212,7 +232,7 @@ __global__ __launch_bounds__(256) void lwc_step_kernel(const void *__restrict__ 
       const bool inside = qr >= 0.0 && qr <= maxq;
       const double q = fmin(fmax(qr, 0.0), maxq);
       const double p = P[e];
-      loss += D[e] * p;
+      loss += D[i * md + j * g + c] * p;
       const double G = -p / T;
       const double dws = inside ? -w / s + (q - z) : q - z;
       const double dwz = inside ? 0.0 : -s;
@@ -325,9 +345,12 @@ LwcPlan lwc_plan(int64_t n, int64_t m, int group, int iters) {
   LwcPlan p;
   const int64_t nseg = n * (m / group);
   p.nblk = (nseg + LWC_SEG_PER_BLOCK - 1) / LWC_SEG_PER_BLOCK;
+  const int64_t md = (m + NBK - 1) / NBK * NBK, nd = (n + NBK - 1) / NBK * NBK;
   size_t off = 0;
   p.off_D = off;
-  off += align_up((size_t)n * m * 8, 256);
+  off += align_up((size_t)nd * md * 8, 256);   // D, padded to 64 multiples
+  p.off_Hd = off;
+  off += align_up((size_t)md * md * 8, 256);   // H in float64, padded
   p.off_P = off;
   off += align_up((size_t)n * m * 8, 256);
   p.off_st = off;
@@ -343,20 +366,27 @@ hipError_t launch_lwc(const void *W, bool bf16, int64_t n, int64_t m, int group,
                       double *logits, double *loss, void *ws, const LwcPlan &p, hipStream_t st) {
   char *base = (char *)ws;
   double *D = (double *)(base + p.off_D);
+  double *Hd = (double *)(base + p.off_Hd);
   double *P = (double *)(base + p.off_P);
   double *state = (double *)(base + p.off_st);
   double *part = (double *)(base + p.off_part);
   const unsigned sblocks = (unsigned)p.nblk;
   const unsigned eblocks = (unsigned)((n * m + 255) / 256);
-  const dim3 pgrid((unsigned)((n + NBK - 1) / NBK), (unsigned)((m + NBK - 1) / NBK));
+  const int64_t md = (m + NBK - 1) / NBK * NBK, nd = (n + NBK - 1) / NBK * NBK;
+  const int64_t ncb = md / NBK, ptiles = (nd / NBK) * ncb;
+  {
+    int64_t blocks = (md * md + 255) / 256;
+    if (blocks > 65536) blocks = 65536;
+    lwc_prep_kernel<<<(unsigned)blocks, 256, 0, st>>>(H, m, n, md, nd, Hd, D);
+  }
   lwc_init_kernel<<<sblocks, 256, 0, st>>>(W, bf16, n, m, group, bits, init, state);
   for (int it = 0; it <= iters; ++it) {
-    lwc_forward_kernel<<<eblocks, 256, 0, st>>>(W, bf16, n, m, group, bits, state, D);
+    lwc_forward_kernel<<<eblocks, 256, 0, st>>>(W, bf16, n, m, md, group, bits, state, D);
     timer_begin(K_LWC_DH, st);
-    lwc_dh_kernel<<<pgrid, 256, 0, st>>>(D, H, n, m, P);
+    lwc_dh_kernel<<<xcd_grid(ptiles), 256, 0, st>>>(D, Hd, n, m, md, ncb, ptiles, P);
     timer_end(K_LWC_DH, st);
     // step it + 1 updates the logits; the pass after the last step only adds its loss
-    lwc_step_kernel<<<sblocks, 256, 0, st>>>(W, bf16, n, m, group, bits, D, P, T, it < iters ? it + 1 : 0, lr,
+    lwc_step_kernel<<<sblocks, 256, 0, st>>>(W, bf16, n, m, md, group, bits, D, P, T, it < iters ? it + 1 : 0, lr,
                                              state, part + (int64_t)it * p.nblk);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;

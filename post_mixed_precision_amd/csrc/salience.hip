@@ -457,69 +457,6 @@ __device__ __forceinline__ void trail_tile(double *__restrict__ A, double *__res
         C[(r0 + row) * mp + c0 + col] = cv[i][j][v] - acc[i][j][v];
       }
 }
-
-// Group-update tiles take their operands straight from memory into LDS
-// (buffer loads to LDS), half a panel (K = 32) at a time into one of two
-// buffers, so a half panel's loads run during the previous half's products,
-// with one barrier per half panel; no operand passes through registers.  An
-// operand half tile is 16 KB: 64 rows of 32 doubles (rows are the product's m
-// or n index) or 32 rows of 64 doubles (rows are K, for the Z operand).  Its
-// 16-byte slots are swizzled so that the product's reads are conflict-free:
-// logical slot ls of row r sits in physical slot ls ^ (r & 15) when the
-// product reads one K across 16 rows, ls ^ 8 (r & 1) when it reads along a row.
-constexpr int HP_BYTES = 64 * 256;   // one operand half tile
-typedef __attribute__((address_space(3))) void lds_void_t;
-
-// DMA of one operand half tile whose element (0, 0) is at `base` (row stride
-// mp doubles).  KIND 0: 64 rows x 32 doubles, four rows per wave instruction;
-// KIND 1: 32 rows x 64 doubles, two rows per instruction.  Each lane loads the
-// logical slot that belongs in the physical slot it writes.
-template <int KIND>
-__device__ __forceinline__ void load_half(const double *base, int64_t mp, unsigned char *dst) {
-  const __amdgpu_buffer_rsrc_t rs =
-      __builtin_amdgcn_make_buffer_rsrc((void *)base, (short)0, (int)((63 * mp + 64) * 8), 0x00020000);
-  const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const int r0 = KIND == 0 ? 16 * wave + 4 * q : 8 * wave + 2 * q;   // first row of this instruction
-    const int row = KIND == 0 ? r0 + (lane >> 4) : r0 + (lane >> 5);
-    const int ps = KIND == 0 ? (lane & 15) : (lane & 31);
-    const int ls = KIND == 0 ? ps ^ (row & 15) : ps ^ (8 * (row & 1));
-    const uint32_t off = (uint32_t)row * (uint32_t)(mp * 8) + (uint32_t)(ls * 16);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_t *)(dst + r0 * (KIND == 0 ? 256 : 512)), 16, (int)off, 0,
-                                             0, 0);
-  }
-}
-
-// acc += (A half tile LA) x (B half tile LB) over K = 32 on the 16x16x4 f64
-// MFMA, in the lane layout of gemm64.  LA holds rows m; LB holds rows n (A
-// tiles: B(k, n) = A[c0 + n][k0 + k]) or, for Z tiles, rows k (B(k, n) =
-// Z[k0 + k][c0 + n]).
-template <bool ZT>
-__device__ __forceinline__ void gemm_half(const unsigned char *LA, const unsigned char *LB, f64x4_t acc[2][2],
-                                          int lane, int wm, int wn) {
-  const int l15 = lane & 15;
-#pragma unroll
-  for (int ks = 0; ks < 8; ++ks) {
-    const int k = ks * 4 + (lane >> 4);
-    double a[2], b[2];
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-      a[i] = *(const double *)(LA + (wm * 32 + i * 16 + l15) * 256 + (((k >> 1) ^ l15) * 16) + (k & 1) * 8);
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int n = wn * 32 + j * 16 + l15;
-      b[j] = ZT ? *(const double *)(LB + k * 512 + (((n >> 1) ^ (8 * (k & 1))) * 16) + (n & 1) * 8)
-                : *(const double *)(LB + n * 256 + (((k >> 1) ^ l15) * 16) + (k & 1) * 8);
-    }
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-#pragma unroll
-      for (int j = 0; j < 2; ++j) acc[i][j] = mfma_f64(a[i], b[j], acc[i][j]);
-  }
-}
-
 // One 64 x 64 tile of the group update by panels plo .. phi (A tile when !ZT:
 // A_ij -= sum_p L_ip L_jp^T; Z tile when ZT: Z_i,cb -= sum_p L_ip Z_p,cb),
 // the sum kept in the accumulators.  l0 and l1 are distinct LDS objects of
@@ -576,17 +513,6 @@ __device__ __forceinline__ void group_tile(double *__restrict__ A, double *__res
         C[(r0 + row) * mp + c0 + col] = cv[i][j][v] - acc[i][j][v];
       }
 }
-
-// XCD-aware work index: workgroup id w runs on XCD w % 8, so XCD x takes
-// the contiguous run of work items [x * per, x * per + per), per =
-// ceil(total / 8), in order: neighbouring tiles of a row share an operand
-// panel, which then stays in that XCD's L2.  Returns -1 for padding ids.
-__device__ __forceinline__ int64_t xcd_item(int64_t w, int64_t total) {
-  const int64_t per = (total + 7) / 8;
-  const int64_t t = (w & 7) * per + (w >> 3);
-  return t < total ? t : -1;
-}
-static unsigned xcd_grid(int64_t total) { return (unsigned)(8 * ((total + 7) / 8)); }
 
 // Row index a of a packed lower triangle (entries (a, b), b <= a, numbered
 // row by row) from the entry number id.
