@@ -98,11 +98,19 @@ __global__ __launch_bounds__(64) void gptq_sweep_kernel(const double *__restrict
   const int64_t il = live ? i : n - 1;
   const int64_t k = m / G;
   const int64_t c0 = (int64_t)j * G;
-  // 16-byte pieces: U is 16-byte aligned and m, c0 are even
-#pragma unroll 8
-  for (int idx = lane; idx < G * G / 2; idx += 64) {
-    const int r = idx / (G / 2), c = 2 * (idx % (G / 2));
-    *(double2 *)&ublk[r * G + c] = *(const double2 *)(U + (c0 + r) * m + c0 + c);
+  // Straight to LDS, one load per row of G doubles (G / 2 lanes of 16 bytes;
+  // U is 16-byte aligned and m, c0 are even), every row's load in flight at
+  // once.  Through registers, eight at a time, the block's 128 KB had cost
+  // most of the sweep.
+  // For G < 128 only the first G / 2 lanes load: a lane's LDS destination is
+  // fixed by its index, so another lane would write into the next row.
+  if (lane < G / 2) {
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+        (void *)(U + c0 * m + c0), (short)0, (int)(((int64_t)(G - 1) * m + G) * 8), 0x00020000);
+#pragma unroll 16
+    for (int r = 0; r < G; ++r)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_t *)&ublk[r * G], 16, lane * 16,
+                                               (int)((uint32_t)r * (uint32_t)(m * 8)), 0, 0);
   }
   for (int sb = 0; sb < NSB; ++sb) {
     const double2 *src = (const double2 *)(W64 + il * m + c0 + sb * GQ_SB + 4 * q);
@@ -115,6 +123,7 @@ __global__ __launch_bounds__(64) void gptq_sweep_kernel(const double *__restrict
   const float s = scale[il * k + j], z = zero[il * k + j];
   const float maxq = (float)((1 << bits[j]) - 1);
   const float r = 1.0f / s;
+  __builtin_amdgcn_s_waitcnt(0);   // the block of U has landed in LDS
   __syncthreads();
   for (int sb = 0; sb < NSB; ++sb) {
     const int64_t cb = c0 + sb * GQ_SB;   // first column of the sub-block
