@@ -186,35 +186,37 @@ __global__ __launch_bounds__(64) void gptq_sweep_kernel(const double *__restrict
 }
 
 // W64[:, c1:] -= Err (n x G) . U[c1-G .. c1-1][c1:], 64 x 64 output tiles;
-// columns of the next group also go to the float32 copy.  Every operand of
-// the tile (all K chunks and the W64 tile itself) is loaded into registers
-// first, so the loads are in flight together; the chunks then pass through
-// LDS one at a time.
+// columns of the next group also go to the float32 copy.  Both operands go
+// straight to LDS half a 64-wide panel (K = 32) at a time into one of two
+// buffers, the next half's loads beside the current half's products (the
+// Cholesky group update's Z-tile form: Err's rows are the tile's rows, U's
+// rows its K); two workgroups per CU; tiles in row-major order, a contiguous
+// run per XCD, so an XCD's tiles share Err's row block in its L2.  Err is
+// padded to whole 64-row blocks (rows past n feed only rows that are not
+// written); U's rows are read 64 columns wide, past the end of a row for the
+// last column tile, which stays inside U (its row is at most m - 2) and feeds
+// only columns that are not written.  Each accumulator takes its products in
+// K order, four k per MFMA, as the register-staged version did.
 template <int G>
-__global__ __launch_bounds__(256) void gptq_trail_kernel(double *__restrict__ W64, float *__restrict__ W32,
-                                                         int64_t n, int64_t m, int64_t c1,
-                                                         const double *__restrict__ Err,
-                                                         const double *__restrict__ U) {
-  constexpr int NKC = (G + NBK - 1) / NBK;   // K chunks of up to 64
-  constexpr int KC = G < NBK ? G : NBK;      // K columns per chunk
-  __shared__ double sA[NBK * SP];
-  __shared__ double sB[NBK * SP];
+__global__ __launch_bounds__(256, 2) void gptq_trail_kernel(double *__restrict__ W64, float *__restrict__ W32,
+                                                            int64_t n, int64_t m, int64_t c1,
+                                                            const double *__restrict__ Err,
+                                                            const double *__restrict__ U, int64_t ncb,
+                                                            int64_t total) {
+  constexpr int NH = G / 32;   // half panels
+  __shared__ __attribute__((aligned(16))) unsigned char l0[2 * HP_BYTES];
+  __shared__ __attribute__((aligned(16))) unsigned char l1[2 * HP_BYTES];
+  const int64_t item = xcd_item(blockIdx.x, total);
+  if (item < 0) return;
+  const int64_t r0 = (item / ncb) * NBK;
+  const int64_t col0 = c1 + (item % ncb) * NBK;
+  const int64_t u0 = c1 - G;   // first U row of the group
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
-  const int64_t r0 = (int64_t)blockIdx.x * NBK;
-  const int64_t col0 = c1 + (int64_t)blockIdx.y * NBK;
-  const int64_t u0 = c1 - G;   // first U row of the group
-  // ra: Err[r0+ii][kc+kk] for sA[kk][ii]; rb: U[u0+kc+k2][col0+cc] for sB[k2][cc]; zero outside
-  double ra[NKC][16], rb[NKC][16];
-#pragma unroll
-  for (int c = 0; c < NKC; ++c)
-#pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      const int idx = tid + e * 256;
-      const int hi = idx >> 6, lo = idx & 63;
-      ra[c][e] = (r0 + hi < n && lo < KC) ? Err[(r0 + hi) * G + c * NBK + lo] : 0.0;
-      rb[c][e] = (hi < KC && col0 + lo < m) ? U[(u0 + c * NBK + hi) * m + col0 + lo] : 0.0;
-    }
+  auto issue = [&](int h, unsigned char *buf) __attribute__((always_inline)) {
+    load_half<0>(Err + r0 * G + 32 * h, G, buf);
+    load_half<1>(U + (u0 + 32 * h) * m + col0, m, buf + HP_BYTES);
+  };
   double wv[2][2][4];
 #pragma unroll
   for (int a = 0; a < 2; ++a)
@@ -228,18 +230,19 @@ __global__ __launch_bounds__(256) void gptq_trail_kernel(double *__restrict__ W6
       }
   f64x4_t acc[2][2];
   zero_acc(acc);
+  issue(0, l0);
 #pragma unroll
-  for (int c = 0; c < NKC; ++c) {
-    if (c) __syncthreads();
-#pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      const int idx = tid + e * 256;
-      const int hi = idx >> 6, lo = idx & 63;
-      sA[lo * SP + hi] = ra[c][e];
-      sB[hi * SP + lo] = rb[c][e];
+  for (int h = 0; h < NH; h += 2) {
+    __builtin_amdgcn_s_waitcnt(0);   // this thread's loads of half h have landed
+    __syncthreads();                 // everyone's; and l1's previous products are done
+    if (h + 1 < NH) issue(h + 1, l1);
+    gemm_half<true>(l0, l0 + HP_BYTES, acc, lane, wm, wn);
+    if (h + 1 < NH) {
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+      if (h + 2 < NH) issue(h + 2, l0);
+      gemm_half<true>(l1, l1 + HP_BYTES, acc, lane, wm, wn);
     }
-    __syncthreads();
-    gemm64(sA, sB, acc, lane, wm, wn);
   }
 #pragma unroll
   for (int a = 0; a < 2; ++a)
@@ -269,7 +272,7 @@ size_t gptq_ws_bytes(int64_t n, int64_t m, int group) {
   off += 256;                                     // alpha
   off += align_up((size_t)n * m * 8, 256);        // W64
   off += align_up((size_t)n * m * 4, 256);        // W32
-  off += align_up((size_t)n * group * 8, 256);    // Err
+  off += align_up((size_t)gq_pad64(n) * group * 8, 256);   // Err, whole 64-row blocks
   return off;
 }
 
@@ -283,9 +286,9 @@ static void gq_group(double *W64, float *W32, int64_t n, int64_t m, int j, const
   timer_end(K_GPTQ_SWEEP, st);
   const int64_t c1 = (int64_t)(j + 1) * G;
   if (c1 < m) {
-    dim3 grid(nrb, (unsigned)((m - c1 + NBK - 1) / NBK));
+    const int64_t ncb = (m - c1 + NBK - 1) / NBK, total = (int64_t)nrb * ncb;
     timer_begin(K_GPTQ_TRAIL, st);
-    gptq_trail_kernel<G><<<grid, 256, 0, st>>>(W64, W32, n, m, c1, Err, U);
+    gptq_trail_kernel<G><<<xcd_grid(total), 256, 0, st>>>(W64, W32, n, m, c1, Err, U, ncb, total);
     timer_end(K_GPTQ_TRAIL, st);
   }
 }
